@@ -1,0 +1,116 @@
+// Device helpers shared by the libcsa kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define CSA_WAVE 64
+
+namespace csa {
+
+// ---- bf16 storage ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round to nearest even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+// ---- low-precision encoders (the rules stated in csa.h for csa_quantize_keys) ---------------
+// e4m3 (bias 7, largest finite 448): round to nearest even, saturate, keep the sign bit.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  float a = fabsf(x);
+  if (!(a < 448.0f)) return sign | 0x7eu;                  // saturate (also catches NaN input)
+  if (a < 0.015625f) {                                     // below 2^-6: multiples of 2^-9
+    uint32_t k = uint32_t(rintf(a * 512.0f));              // exact scaling, RNE
+    return sign | k;                                       // k == 8 is the code of 2^-6
+  }
+  uint32_t u = __float_as_uint(a);
+  uint32_t r = u + 0x7ffffu + ((u >> 20) & 1u);            // RNE to 3 mantissa bits
+  uint32_t e = (r >> 23) - 127u + 7u;
+  uint32_t code = (e << 3) | ((r >> 20) & 7u);
+  return sign | (code > 0x7eu ? 0x7eu : code);
+}
+
+// e2m1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}: nearest, ties to the even code, saturate at 6.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float x) {
+  uint32_t sign = (__float_as_uint(x) >> 28) & 0x8u;
+  float a = fabsf(x);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;            // tie at .25 -> 0 (even)
+  else if (a < 0.75f) c = 1;        // (.25,.75) -> .5
+  else if (a <= 1.25f) c = 2;       // tie .75 -> 1.0 (even), tie 1.25 -> 1.0
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;        // tie 1.75 -> 2 (even), tie 2.5 -> 2
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;        // tie 3.5 -> 4, tie 5 -> 4
+  else c = 7;                       // (5, inf) -> 6 (NaN input is not expected)
+  return sign | c;
+}
+
+// Smallest e with amax <= 448 * 2^e, clamped to [-126, 127]; 0 for amax == 0.
+__device__ __forceinline__ int e4m3_row_exp(float amax) {
+  if (amax == 0.0f) return 0;
+  int ex = int((__float_as_uint(amax) >> 23) & 0xff);
+  if (ex == 0) return -126;                      // every fitting e is <= -126 for amax < 2^-126
+  int e = ex - 127 - 8;                          // amax / 2^e lies in [256, 512)
+  if (amax > ldexpf(448.0f, e)) ++e;
+  return e < -126 ? -126 : (e > 127 ? 127 : e);
+}
+
+// e8m0 byte of the MX scale for a block maximum: clamp(floor(log2 amax) - 2 + 127, 0, 254).
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
+  uint32_t u = __float_as_uint(amax);
+  int ex = int((u >> 23) & 0xff);                 // floor(log2) + 127 for normals; 0 for 0/subnormal
+  int b = ex - 2;                                 // biased exponent of 2^(floor(log2 amax) - 2)
+  if (ex == 0) b = 0;
+  return uint32_t(b < 0 ? 0 : (b > 254 ? 254 : b));
+}
+
+// ---- order-preserving keys for selection ---------------------------------------------------
+// High word: float score mapped to an unsigned order; low word: ~index so equal scores prefer
+// the lower index.  Key 0 never occurs for a real entry (marks "no entry").
+__device__ __forceinline__ uint32_t score_order(float s) {
+  uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t make_key(float s, uint32_t idx) {
+  return (uint64_t(score_order(s)) << 32) | uint64_t(~idx);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t k) { return ~uint32_t(k); }
+
+// ---- wave / block reductions ---------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ---- rotary angles ---------------------------------------------------------------------------
+// cos/sin of pos * base^(-2u/r).  The angle is formed and reduced modulo 2*pi in double so that
+// positions near 2^20 keep full fp32 accuracy; the final sin/cos are fp32.
+__device__ __forceinline__ void rope_cos_sin(int64_t pos, int u, int r, double log2_base,
+                                             float *c, float *s) {
+  double inv = exp2(-(2.0 * double(u) / double(r)) * log2_base);
+  double phi = double(pos) * inv;
+  const double two_pi = 6.283185307179586476925286766559;
+  phi -= two_pi * rint(phi / two_pi);
+  float p = float(phi);
+  sincosf(p, s, c);
+}
+
+}  // namespace csa

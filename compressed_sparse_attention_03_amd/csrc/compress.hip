@@ -1,0 +1,188 @@
+// KV compressor: per-channel softmax pooling of each entry's tokens, RMSNorm, partial RoPE.
+//
+// "DeepSeek-V4: Million-Token Context" (codexsims explainer), CSA walk-through: every m tokens
+// become one entry through a learned softmax weighting; HCA walk-through: non-overlapping windows
+// of m' = 128 tokens.  "Follow the white rabbit" (sambatista.com), CSA paragraph: each entry also
+// draws on the previous group; HCA paragraph: weights differ per part of the representation.
+// paperlayer summary, section 2.3 "Other details": RMSNorm on compressed entries.
+//
+// Layout: one workgroup (4 waves) per entry.  A lane owns CPL = d/64 consecutive channels, so a
+// wave reads a 2*d-byte token row with one coalesced vector load per lane.  The waves split the
+// entry's tokens; each keeps an online softmax (running max, running sum, weighted sum) per
+// channel in registers, and the four states are merged through LDS.  Exponentials are exp2 of
+// log2(e)-scaled logits.
+#include "common.h"
+#include "internal.h"
+
+namespace csa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int CPL>
+__device__ __forceinline__ void load_row(const uint16_t *p, float (&v)[CPL]) {
+  if constexpr (CPL == 1) {
+    v[0] = bf16_to_f32(*p);
+  } else if constexpr (CPL == 2) {
+    uint32_t w = *reinterpret_cast<const uint32_t *>(p);
+    v[0] = bf16lo(w); v[1] = bf16hi(w);
+  } else if constexpr (CPL == 4) {
+    uint2 w = *reinterpret_cast<const uint2 *>(p);
+    v[0] = bf16lo(w.x); v[1] = bf16hi(w.x); v[2] = bf16lo(w.y); v[3] = bf16hi(w.y);
+  } else {
+#pragma unroll
+    for (int q = 0; q < CPL / 8; ++q) {
+      uint4 w = reinterpret_cast<const uint4 *>(p)[q];
+      v[8 * q + 0] = bf16lo(w.x); v[8 * q + 1] = bf16hi(w.x);
+      v[8 * q + 2] = bf16lo(w.y); v[8 * q + 3] = bf16hi(w.y);
+      v[8 * q + 4] = bf16lo(w.z); v[8 * q + 5] = bf16hi(w.z);
+      v[8 * q + 6] = bf16lo(w.w); v[8 * q + 7] = bf16hi(w.w);
+    }
+  }
+}
+
+template <int CPL>
+__device__ __forceinline__ void store_row(uint16_t *p, const float (&v)[CPL]) {
+  if constexpr (CPL == 1) {
+    *p = f32_to_bf16(v[0]);
+  } else if constexpr (CPL == 2) {
+    *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(v[0], v[1]);
+  } else if constexpr (CPL == 4) {
+    *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  } else {
+#pragma unroll
+    for (int q = 0; q < CPL / 8; ++q)
+      reinterpret_cast<uint4 *>(p)[q] =
+          make_uint4(pack_bf16x2(v[8 * q + 0], v[8 * q + 1]), pack_bf16x2(v[8 * q + 2], v[8 * q + 3]),
+                     pack_bf16x2(v[8 * q + 4], v[8 * q + 5]), pack_bf16x2(v[8 * q + 6], v[8 * q + 7]));
+  }
+}
+
+// RMSNorm (weight g, or ones) then rotation of the channels >= d - r at position pos.
+// Every lane of the wave must call this (it reduces across the wave).
+template <int CPL>
+__device__ __forceinline__ void norm_rope(float (&v)[CPL], const uint16_t *g, int d, int r,
+                                          int64_t pos, double log2_base, float eps, int lane) {
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) ss += v[j] * v[j];
+  ss = wave_sum(ss);
+  float inv = rsqrtf(ss / float(d) + eps);
+  const int c0 = lane * CPL;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) v[j] *= inv * (g ? bf16_to_f32(g[c0 + j]) : 1.0f);
+  const int rope0 = d - r;
+  if constexpr (CPL >= 2) {
+    if (c0 + CPL > rope0) {
+#pragma unroll
+      for (int j = 0; j < CPL; j += 2) {
+        int ch = c0 + j;
+        if (ch >= rope0) {
+          float cs, sn;
+          rope_cos_sin(pos, (ch - rope0) >> 1, r, log2_base, &cs, &sn);
+          float a = v[j], b = v[j + 1];
+          v[j] = a * cs - b * sn;
+          v[j + 1] = a * sn + b * cs;
+        }
+      }
+    }
+  } else {
+    float partner = __shfl_xor(v[0], 1, 64);
+    if (c0 >= rope0) {
+      float cs, sn;
+      rope_cos_sin(pos, (c0 - rope0) >> 1, r, log2_base, &cs, &sn);
+      v[0] = (c0 & 1) ? (partner * sn + v[0] * cs) : (v[0] * cs - partner * sn);
+    }
+  }
+}
+
+template <int CPL>
+__global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
+  const int d = a.d, m = a.m;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t i = blockIdx.x;                                // local entry index
+  const int b = blockIdx.y;
+  const int64_t gi = a.pos0 / m + i;                           // global entry index
+  const bool has_prev = a.overlap && gi > 0;
+  const int nt = has_prev ? 2 * m : m;
+  const int64_t row_first = a.halo + (has_prev ? (i - 1) * m : i * m);
+  const int slot_first = has_prev ? 0 : (a.overlap ? m : 0);
+  const int own_first = has_prev ? m : 0;                      // token index where the own group starts
+  const int64_t rows = a.halo + a.n_new;
+  const uint16_t *cb = a.c + (int64_t(b) * rows) * d + lane * CPL;
+  const uint16_t *zb = a.z + (int64_t(b) * rows) * d + lane * CPL;
+
+  float mx[CPL], sm[CPL], acc[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) { mx[j] = -INFINITY; sm[j] = 0.f; acc[j] = 0.f; }
+
+  const int per = (nt + 3) >> 2;
+  const int k0 = wave * per, k1 = min(nt, k0 + per);
+  for (int k = k0; k < k1; ++k) {
+    float cv[CPL], zv[CPL], bv[CPL];
+    const int64_t row = row_first + k;
+    load_row<CPL>(cb + row * d, cv);
+    load_row<CPL>(zb + row * d, zv);
+    load_row<CPL>(a.bias + int64_t(slot_first + k) * d + lane * CPL, bv);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      float l = (zv[j] + bv[j]) * kLog2e;
+      float nm = fmaxf(mx[j], l);
+      float sc = exp2f(mx[j] - nm);                           // 0 on the first token
+      float e = exp2f(l - nm);
+      sm[j] = sm[j] * sc + e;
+      acc[j] = acc[j] * sc + e * cv[j];
+      mx[j] = nm;
+    }
+    if (a.win_rows && k >= own_first) {                       // per-token window row
+      const int64_t tok = i * m + (k - own_first);           // index among the new tokens
+      norm_rope<CPL>(cv, a.norm_w, d, a.rope_dim, a.pos0 + tok, a.log2_base, a.eps, lane);
+      store_row<CPL>(a.win_rows + (int64_t(b) * a.n_new + tok) * d + lane * CPL, cv);
+    }
+  }
+
+  __shared__ float s_state[3][4][64 * CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    s_state[0][wave][lane * CPL + j] = mx[j];
+    s_state[1][wave][lane * CPL + j] = sm[j];
+    s_state[2][wave][lane * CPL + j] = acc[j];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float p[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int ch = lane * CPL + j;
+    float M = fmaxf(fmaxf(s_state[0][0][ch], s_state[0][1][ch]), fmaxf(s_state[0][2][ch], s_state[0][3][ch]));
+    float S = 0.f, A = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float mw = s_state[0][w][ch];
+      float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      S += s_state[1][w][ch] * f;
+      A += s_state[2][w][ch] * f;
+    }
+    p[j] = A / S;
+  }
+  norm_rope<CPL>(p, a.norm_w, d, a.rope_dim, gi * m, a.log2_base, a.eps, lane);
+  store_row<CPL>(a.entries + (int64_t(b) * (a.n_new / m) + i) * d + lane * CPL, p);
+}
+
+}  // namespace
+
+hipError_t launch_compress(const CompressArgs &a, hipStream_t stream) {
+  dim3 grid(unsigned(a.n_new / a.m), unsigned(a.B));
+  dim3 block(256);
+  switch (a.d / 64) {
+    case 1: hipLaunchKernelGGL(compress_kernel<1>, grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(compress_kernel<2>, grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(compress_kernel<4>, grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(compress_kernel<8>, grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(compress_kernel<16>, grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,88 @@
+// Internal launcher interface between the C-ABI front (api.cpp) and the kernel sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+struct CompressArgs {
+  const uint16_t *c, *z, *bias, *norm_w;
+  uint16_t *entries, *win_rows;
+  int B, d, m, overlap, rope_dim, halo;
+  int64_t n_new, pos0;
+  double log2_base;
+  float eps;
+};
+hipError_t launch_compress(const CompressArgs &a, hipStream_t stream);
+
+struct QuantizeArgs {
+  const uint16_t *x;
+  void *codes, *scales;
+  int64_t rows;
+  int dim, format;
+};
+hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t stream);
+
+// ---- lightning indexer + top-k -------------------------------------------------------------
+// The entry axis of every query is cut into tiles of `tile` entries.  The score kernel keeps, per
+// tile, the `cand` best (score, index) keys; the merge kernel selects the global top-k among all
+// tiles' candidates and re-scores any tile whose candidate list might have been too short.
+struct IndexPlan {
+  int tile;        // entries per tile (multiple of 64)
+  int cand;        // candidates kept per tile (power of two, <= tile)
+  int n_tiles;     // tiles per query
+};
+IndexPlan plan_index(int64_t n_queries, int64_t N_cap, int topk);
+size_t index_workspace_bytes(int64_t n_queries, int64_t N_cap, int topk);
+
+struct IndexArgs {
+  const void *q_idx;
+  const float *w_idx;
+  const void *k_codes, *k_scales;
+  const int64_t *n_entries, *q_pos0;
+  int32_t *topk_idx;
+  float *scores;
+  void *workspace;
+  int format, B, Sq, H_I, D_I, m, topk;
+  int64_t N_cap;
+  IndexPlan plan;
+};
+hipError_t launch_index_score(const IndexArgs &a, hipStream_t stream);
+hipError_t launch_index_merge(const IndexArgs &a, hipStream_t stream);
+
+// ---- core attention ------------------------------------------------------------------------
+struct AttendPlan {
+  int n_hb;         // head blocks of 16
+  int n_splits;     // row splits per (query, head block)
+  int rows_per_split;
+  int n_rows;       // row-list length per query: n_sel + window
+};
+AttendPlan plan_attend(int64_t n_queries, int H, int64_t n_sel, int window);
+size_t attend_workspace_bytes(int64_t n_queries, int H, int D, int64_t n_sel, int window);
+
+struct AttendArgs {
+  const uint16_t *q, *q_norm_w, *entries, *win_rows;
+  const int32_t *topk_idx;          // CSA selection, or NULL for HCA (dense prefix)
+  const int64_t *n_entries;         // HCA only
+  const int64_t *win_pos0, *q_pos0;
+  uint16_t *out;
+  float *lse;
+  void *workspace;
+  int64_t N_cap, W_cap;
+  int64_t n_sel;                    // CSA: topk; HCA: N_cap
+  int B, Sq, H, D, rope_dim, window, m;
+  float scale_log2;                 // softmax_scale * log2(e)
+  double log2_base;
+  float eps;
+  AttendPlan plan;
+};
+hipError_t launch_attend(const AttendArgs &a, hipStream_t stream);
+hipError_t launch_combine(const AttendArgs &a, hipStream_t stream);
+
+// Kernel timing hooks (api.cpp): bracket a launch with events when timing is on.
+void timing_begin(const char *name, hipStream_t stream);
+void timing_end(const char *name, hipStream_t stream);
+
+}  // namespace csa

@@ -147,27 +147,30 @@ WORKLOADS = {w.name: w for w in (TINY, CSA_DECODE_32K, CSA_PREFILL_128K, HCA_DEC
                                  CSA_DECODE_1M, CSA_DECODE_128K)}
 
 
-def decode_inputs(w: Workload, b_lo: int = 0, b_hi: int | None = None, n_rows: int | None = None):
+def decode_inputs(w: Workload, b_lo: int = 0, b_hi: int | None = None, n_rows: int | None = None,
+                  parts=("attend", "index")):
     """Host-side decode inputs for sequences [b_lo, b_hi).
 
     Returns a dict of numpy arrays: bf16 tensors as uint16 bit patterns, fp32 otherwise.
     ``n_rows`` limits the entries/keys to the first n rows (for sampled checks); the planted
-    entries are placed relative to the full N.
+    entries are placed relative to the full N.  ``parts`` selects the attention inputs (q,
+    entries, window rows) and/or the indexer inputs (q_idx, w_idx, k_idx).
     """
     b_hi = w.B if b_hi is None else b_hi
     nb = b_hi - b_lo
     N = w.N if n_rows is None else n_rows
     d, H = w.d, w.H
     out = {}
-    out["q"] = normal_bf16(w.cfg, T_Q, (w.B * w.Sq * H, d), row0=b_lo * w.Sq * H,
-                           nrows=nb * w.Sq * H).reshape(nb, w.Sq, H, d)
-    out["win_rows"] = normal_bf16(w.cfg, T_WIN, (w.B * w.window, d), row0=b_lo * w.window,
-                                  nrows=nb * w.window).reshape(nb, w.window, d)
-    ent = np.empty((nb, N, d), dtype=np.uint16)
-    for j, b in enumerate(range(b_lo, b_hi)):
-        ent[j] = normal_bf16(w.cfg, T_ENTRIES, (w.B * w.N, d), row0=b * w.N, nrows=N)
-    out["entries"] = ent
-    if w.kind == "csa_decode":
+    if "attend" in parts:
+        out["q"] = normal_bf16(w.cfg, T_Q, (w.B * w.Sq * H, d), row0=b_lo * w.Sq * H,
+                               nrows=nb * w.Sq * H).reshape(nb, w.Sq, H, d)
+        out["win_rows"] = normal_bf16(w.cfg, T_WIN, (w.B * w.window, d), row0=b_lo * w.window,
+                                      nrows=nb * w.window).reshape(nb, w.window, d)
+        ent = np.empty((nb, N, d), dtype=np.uint16)
+        for j, b in enumerate(range(b_lo, b_hi)):
+            ent[j] = normal_bf16(w.cfg, T_ENTRIES, (w.B * w.N, d), row0=b * w.N, nrows=N)
+        out["entries"] = ent
+    if w.kind == "csa_decode" and "index" in parts:
         out["q_idx"] = normal_bf16(w.cfg, T_QIDX, (w.B * w.Sq * w.H_I, w.D_I), row0=b_lo * w.Sq * w.H_I,
                                    nrows=nb * w.Sq * w.H_I).reshape(nb, w.Sq, w.H_I, w.D_I)
         wts = uniform_f32(w.cfg, T_W, (w.B * w.Sq, w.H_I))

@@ -1,0 +1,239 @@
+"""Python binding of libcsa: argument marshalling only.
+
+Each function takes torch tensors that already live on the GPU, checks dtype/shape/contiguity,
+allocates outputs and workspace with torch (device memory is plumbing), and calls the C-ABI
+function of the same name on the current torch stream.  Every step of the computation runs in the
+HIP library; there is no fallback: if ``libcsa.so`` is missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa.so")
+
+KEY_F32, KEY_FP8_E4M3, KEY_MXFP4 = 0, 1, 2
+KEY_FORMATS = {"f32": KEY_F32, "fp8": KEY_FP8_E4M3, "mxfp4": KEY_MXFP4}
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "HIP error"}
+
+_lib = None
+P = ctypes.c_void_p
+I32, I64, F32, SZ = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+_SIGS = {
+    "csa_compress": (I32, [P, P, P, P, I32, I64, I32, I32, I32, I32, I32, I64, F32, F32, P, P, P]),
+    "csa_quantize_keys": (I32, [P, I64, I32, I32, P, P, P]),
+    "csa_index_topk": (I32, [P, P, P, P, I32, I32, I32, I32, I32, I64, P, P, I32, I32, P, P, P, SZ, P]),
+    "csa_index_topk_workspace_bytes": (SZ, [I32, I32, I64, I32]),
+    "csa_attend": (I32, [P, P, P, I64, P, I32, P, I64, P, P, I32, I32, I32, I32, I32, I32, F32, F32,
+                         F32, P, P, P, SZ, P]),
+    "csa_attend_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
+    "hca_attend": (I32, [P, P, P, I64, P, I32, P, I64, P, P, I32, I32, I32, I32, I32, I32, F32, F32,
+                         F32, P, P, P, SZ, P]),
+    "hca_attend_workspace_bytes": (SZ, [I32, I32, I32, I32, I64, I32]),
+    "csa_status_string": (ctypes.c_char_p, [I32]),
+    "csa_last_error": (ctypes.c_char_p, []),
+    "csa_timing_enable": (None, [I32]),
+    "csa_timing_read": (I32, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
+}
+
+
+class CsaError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libcsa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise CsaError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m compressed_sparse_attention_03_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        detail = lib().csa_last_error().decode()
+        raise CsaError(f"{what}: {STATUS.get(status, status)}: {detail}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _i64(t, name, B):
+    t = _dev(t, name, torch.int64, 1)
+    if t.shape[0] != B:
+        raise ValueError(f"{name} must have shape [{B}]")
+    return t
+
+
+# ---------------------------------------------------------------------------------------------
+def csa_compress(c, z, bias, *, m, overlap, rope_dim, pos0=0, norm_w=None, rope_base=10000.0,
+                 eps=1e-6, win_rows=False, entries_out=None, win_rows_out=None):
+    """Compressed entries [B, n_new/m, d] (and prepared window rows [B, n_new, d] if asked)."""
+    _dev(c, "c", torch.bfloat16, 3)
+    _dev(z, "z", torch.bfloat16, 3)
+    _dev(bias, "bias", torch.bfloat16, 2)
+    B, rows, d = c.shape
+    if z.shape != c.shape:
+        raise ValueError("z must have the shape of c")
+    halo = m if (overlap and pos0 > 0) else 0
+    n_new = rows - halo
+    ent = entries_out if entries_out is not None else torch.empty((B, max(n_new, 0) // m, d), dtype=torch.bfloat16, device=c.device)
+    wr = None
+    if win_rows:
+        wr = win_rows_out if win_rows_out is not None else torch.empty((B, n_new, d), dtype=torch.bfloat16, device=c.device)
+    if norm_w is not None:
+        _dev(norm_w, "norm_w", torch.bfloat16, 1)
+    st = lib().csa_compress(_ptr(c), _ptr(z), _ptr(bias), _ptr(norm_w), B, n_new, halo, d, m, overlap,
+                            rope_dim, pos0, rope_base, eps, _ptr(ent), _ptr(wr), _stream())
+    _check(st, "csa_compress")
+    return ent, wr
+
+
+def csa_quantize_keys(x, fmt):
+    """Keys bf16 [..., dim] -> (codes, scales) in the storage format ``fmt`` ("fp8" | "mxfp4")."""
+    _dev(x, "x", torch.bfloat16)
+    dim = x.shape[-1]
+    rows = x.numel() // dim
+    f = KEY_FORMATS[fmt]
+    lead = tuple(x.shape[:-1])
+    if f == KEY_FP8_E4M3:
+        codes = torch.empty(lead + (dim,), dtype=torch.uint8, device=x.device)
+        scales = torch.empty(lead, dtype=torch.float32, device=x.device)
+    else:
+        codes = torch.empty(lead + (dim // 2,), dtype=torch.uint8, device=x.device)
+        scales = torch.empty(lead + (dim // 32,), dtype=torch.uint8, device=x.device)
+    st = lib().csa_quantize_keys(_ptr(x), rows, dim, f, _ptr(codes), _ptr(scales), _stream())
+    _check(st, "csa_quantize_keys")
+    return codes, scales
+
+
+def index_topk_workspace(B, Sq, N_cap, topk, device="cuda"):
+    n = lib().csa_index_topk_workspace_bytes(B, Sq, N_cap, topk)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def csa_index_topk(q_idx, w_idx, k_codes, k_scales, *, key_format, n_entries, q_pos0, m, topk,
+                   scores=False, workspace=None, topk_out=None):
+    """Top-k entry indices int32 [B, Sq, topk] (ascending, -1 padded) and optionally the scores."""
+    f = KEY_FORMATS[key_format] if isinstance(key_format, str) else int(key_format)
+    _dev(q_idx, "q_idx", torch.float32 if f == KEY_F32 else torch.bfloat16, 4)
+    B, Sq, H_I, D_I = q_idx.shape
+    _dev(w_idx, "w_idx", torch.float32, 3)
+    if tuple(w_idx.shape) != (B, Sq, H_I):
+        raise ValueError("w_idx must be [B, Sq, H_I]")
+    _dev(k_codes, "k_codes", torch.float32 if f == KEY_F32 else torch.uint8, 3)
+    N_cap = k_codes.shape[1]
+    if k_codes.shape[0] != B:
+        raise ValueError("k_codes must be [B, N_cap, ...]")
+    if f != KEY_F32:
+        _dev(k_scales, "k_scales")
+    _i64(n_entries, "n_entries", B)
+    _i64(q_pos0, "q_pos0", B)
+    out = topk_out if topk_out is not None else torch.empty((B, Sq, topk), dtype=torch.int32, device=q_idx.device)
+    sc = torch.empty((B, Sq, N_cap), dtype=torch.float32, device=q_idx.device) if scores else None
+    ws = workspace if workspace is not None else index_topk_workspace(B, Sq, N_cap, topk, q_idx.device)
+    st = lib().csa_index_topk(_ptr(q_idx), _ptr(w_idx), _ptr(k_codes), _ptr(k_scales), f, B, Sq, H_I, D_I,
+                              N_cap, _ptr(n_entries), _ptr(q_pos0), m, topk, _ptr(out), _ptr(sc),
+                              _ptr(ws), ws.numel(), _stream())
+    _check(st, "csa_index_topk")
+    return out, sc
+
+
+def attend_workspace(B, Sq, H, D, topk, window, device="cuda"):
+    n = lib().csa_attend_workspace_bytes(B, Sq, H, D, topk, window)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def hca_workspace(B, Sq, H, D, N_cap, window, device="cuda"):
+    n = lib().hca_attend_workspace_bytes(B, Sq, H, D, N_cap, window)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _attend_common(q, entries, win_rows, win_pos0, q_pos0, q_norm_w):
+    _dev(q, "q", torch.bfloat16, 4)
+    B, Sq, H, D = q.shape
+    _dev(entries, "entries", torch.bfloat16, 3)
+    _dev(win_rows, "win_rows", torch.bfloat16, 3)
+    if entries.shape[0] != B or entries.shape[2] != D or win_rows.shape[0] != B or win_rows.shape[2] != D:
+        raise ValueError("entries/win_rows must be [B, rows, D]")
+    _i64(win_pos0, "win_pos0", B)
+    _i64(q_pos0, "q_pos0", B)
+    if q_norm_w is not None:
+        _dev(q_norm_w, "q_norm_w", torch.bfloat16, 1)
+    return B, Sq, H, D
+
+
+def csa_attend(q, entries, topk_idx, win_rows, win_pos0, q_pos0, *, rope_dim, window, q_norm_w=None,
+               softmax_scale=None, rope_base=10000.0, eps=1e-6, lse=False, workspace=None, out=None):
+    """CSA core attention -> (out bf16 [B, Sq, H, D], lse fp32 [B, Sq, H] or None)."""
+    B, Sq, H, D = _attend_common(q, entries, win_rows, win_pos0, q_pos0, q_norm_w)
+    _dev(topk_idx, "topk_idx", torch.int32, 3)
+    topk = topk_idx.shape[2]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
+    o = out if out is not None else torch.empty_like(q)
+    ls = torch.empty((B, Sq, H), dtype=torch.float32, device=q.device) if lse else None
+    ws = workspace if workspace is not None else attend_workspace(B, Sq, H, D, topk, window, q.device)
+    st = lib().csa_attend(_ptr(q), _ptr(q_norm_w), _ptr(entries), entries.shape[1], _ptr(topk_idx), topk,
+                          _ptr(win_rows), win_rows.shape[1], _ptr(win_pos0), _ptr(q_pos0), B, Sq, H, D,
+                          rope_dim, window, scale, rope_base, eps, _ptr(o), _ptr(ls), _ptr(ws), ws.numel(),
+                          _stream())
+    _check(st, "csa_attend")
+    return o, ls
+
+
+def hca_attend(q, entries, n_entries, win_rows, win_pos0, q_pos0, *, m, rope_dim, window, q_norm_w=None,
+               softmax_scale=None, rope_base=10000.0, eps=1e-6, lse=False, workspace=None, out=None):
+    """HCA core attention (dense over visible entries + window) -> (out, lse or None)."""
+    B, Sq, H, D = _attend_common(q, entries, win_rows, win_pos0, q_pos0, q_norm_w)
+    _i64(n_entries, "n_entries", B)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
+    o = out if out is not None else torch.empty_like(q)
+    ls = torch.empty((B, Sq, H), dtype=torch.float32, device=q.device) if lse else None
+    N_cap = entries.shape[1]
+    ws = workspace if workspace is not None else hca_workspace(B, Sq, H, D, N_cap, window, q.device)
+    st = lib().hca_attend(_ptr(q), _ptr(q_norm_w), _ptr(entries), N_cap, _ptr(n_entries), m, _ptr(win_rows),
+                          win_rows.shape[1], _ptr(win_pos0), _ptr(q_pos0), B, Sq, H, D, rope_dim, window,
+                          scale, rope_base, eps, _ptr(o), _ptr(ls), _ptr(ws), ws.numel(), _stream())
+    _check(st, "hca_attend")
+    return o, ls
+
+
+def timing_enable(on: bool):
+    lib().csa_timing_enable(1 if on else 0)
+
+
+def timing_read(kernel: str):
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(lib().csa_timing_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)), "csa_timing_read")
+    return ms.value, n.value

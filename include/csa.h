@@ -1,0 +1,205 @@
+/*
+ * csa.h -- C ABI of libcsa, an MI355X (gfx950) implementation of the hybrid compressed attention
+ * forward pass: CSA (compressed sparse attention) and HCA (heavily compressed attention).
+ *
+ * The operations follow these pages (cited by title and section):
+ *   [EXPLAINER] "DeepSeek-V4: Million-Token Context" (codexsims.com explainer): the CSA
+ *               walk-through (compressor, lightning indexer, top-k selector, core attention plus
+ *               sliding window) and the HCA walk-through (128-token windows, dense attention).
+ *   [DEVTO]     "How DeepSeek-V4 Achieves Million-Token Contexts Without Quadratic Attention
+ *               Costs" (dev.to), section "Two Compression Strategies: CSA and HCA".
+ *   [SUMMARY]   "DeepSeek-V4: Towards Highly Efficient Million-Token Context Intelligence"
+ *               (paperlayer.ai summary), section 2.3 "Hybrid Attention with CSA and HCA".
+ *   [RABBIT]    "Follow the white rabbit: DeepSeek V4's architecture in 3D" (sambatista.com),
+ *               paragraphs on HCA, CSA, the sliding window and the lightning indexer.
+ *
+ * Conventions for every call:
+ *   - Pointers to tensors are DEVICE pointers owned by the caller.  The library never allocates,
+ *     frees or keeps a pointer after the call returns.  Scalars are passed by value; the few
+ *     per-sequence integers (positions, entry counts) are device arrays of int64.
+ *   - Tensors are row-major and contiguous.  bf16 tensors are passed as uint16_t bit patterns.
+ *     Every tensor base pointer must be 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  A call validates its
+ *     arguments on the host, enqueues its kernels on `stream` and returns without synchronising.
+ *   - Errors: a call returns a csa_status.  Argument errors (CSA_ERR_INVALID, CSA_ERR_UNSUPPORTED,
+ *     CSA_ERR_WORKSPACE) are detected before any HIP call, so nothing is enqueued.  CSA_ERR_HIP
+ *     reports a failed launch.  Faults inside a kernel surface at the caller's next
+ *     synchronisation.  csa_last_error() returns a thread-local message naming the argument.
+ *   - Values inside device arrays (positions, counts, indices) cannot be checked on the host
+ *     without a synchronisation; out-of-range values are undefined behaviour.
+ *   - Workspace is caller-provided device memory of at least the size the matching
+ *     *_workspace_bytes() function returns; two calls that run concurrently must not share it.
+ *   - Results are deterministic: fixed reduction orders, no floating-point atomics.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum csa_status {
+  CSA_OK = 0,
+  CSA_ERR_INVALID = 1,     /* an argument is out of its documented range; nothing enqueued */
+  CSA_ERR_UNSUPPORTED = 2, /* a valid shape or format this build has no kernel for; nothing enqueued */
+  CSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required; nothing enqueued */
+  CSA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} csa_status;
+
+/* Storage format of the lightning-indexer keys (and the rule used for the query). */
+typedef enum csa_key_format {
+  CSA_KEY_F32 = 0,      /* fp32 keys [rows, D_I]; the query is used as fp32 (no quantisation) */
+  CSA_KEY_FP8_E4M3 = 1, /* e4m3 codes [rows, D_I] (uint8) + one fp32 power-of-two scale per row */
+  CSA_KEY_MXFP4 = 2     /* OCP MXFP4: e2m1 codes packed two per byte [rows, D_I/2] (element 2j in
+                           the low nibble) + one e8m0 scale byte per 32 values [rows, D_I/32] */
+} csa_key_format;
+
+/*
+ * csa_compress -- the KV compressor.
+ * [EXPLAINER] CSA walk-through: every m tokens become one entry through a learned softmax
+ * weighting; [RABBIT] CSA paragraph: each entry also draws on the previous group; [EXPLAINER] HCA
+ * walk-through: non-overlapping windows of m' = 128 tokens; [SUMMARY] 2.3 "Other details": RMSNorm
+ * on the compressed entries; [DEVTO] partial RoPE.
+ *
+ * For entry i and channel j the weights are a softmax over the entry's tokens of
+ * z[t,j] + bias[slot(t), j]; the pooled value sum_t w[t,j] c[t,j] is RMS-normalised (weight
+ * norm_w, eps) and then rotated on its last rope_dim channels at position i*m (interleaved pairs,
+ * angle pos * rope_base^(-2u/rope_dim)).  With overlap the entry spans tokens (i-1)m .. (i+1)m-1;
+ * bias rows 0..m-1 act on the previous group and m..2m-1 on the own group; entry 0 (no previous
+ * group) takes the softmax over its own m tokens only.  Without overlap it spans i*m .. (i+1)m-1.
+ *
+ *   c, z     bf16 [B, halo + n_new, d]: token rows for positions pos0-halo .. pos0+n_new-1.
+ *   bias     bf16 [(1+overlap)*m, d].
+ *   norm_w   bf16 [d] RMSNorm weight, or NULL for ones.
+ *   halo     must be m when overlap && pos0 > 0, else 0.
+ *   pos0     position of the first new token; pos0 % m == 0; n_new % m == 0.
+ *   entries  out bf16 [B, n_new/m, d]: entries pos0/m .. (pos0+n_new)/m - 1.
+ *   win_rows out bf16 [B, n_new, d] or NULL: each new token's row RMS-normalised (norm_w) and
+ *            rotated at its own position -- the rows the sliding window attends to.
+ * Limits: d in {64, 128, 256, 512, 1024}; 1 <= m <= 1024; rope_dim % 4 == 0, rope_dim <= d; eps > 0.
+ */
+csa_status csa_compress(const uint16_t *c, const uint16_t *z, const uint16_t *bias,
+                        const uint16_t *norm_w, int B, int64_t n_new, int halo, int d, int m,
+                        int overlap, int rope_dim, int64_t pos0, float rope_base, float eps,
+                        uint16_t *entries, uint16_t *win_rows, void *stream);
+
+/*
+ * csa_quantize_keys -- quantise lightning-indexer keys to their storage format (quantise on write).
+ * [DEVTO] "Two Compression Strategies": the indexer runs in FP4; [RABBIT] indexer paragraph:
+ * smaller representations and lower-precision numbers.
+ *
+ *   x       bf16 [rows, dim] keys.
+ *   format  CSA_KEY_FP8_E4M3: codes uint8 [rows, dim]; scales fp32 [rows] = 2^e, e the smallest
+ *           integer with max|row| <= 448 * 2^e (clamped to [-126, 127]; 1.0 for a zero row);
+ *           codes = round-to-nearest-even(x / 2^e) in e4m3, saturating at +-448.
+ *           CSA_KEY_MXFP4: codes uint8 [rows, dim/2] (two e2m1 codes per byte); scales uint8
+ *           [rows, dim/32] e8m0 = clamp(floor(log2 amax) - 2 + 127, 0, 254) (0 for a zero block);
+ *           codes = round-to-nearest-even(x / 2^(scale-127)) in e2m1, saturating at +-6.
+ *           Zero magnitudes keep the sign bit of the input.
+ * Limits: dim % 32 == 0, dim <= 1024.  CSA_KEY_F32 is not a stored code format (CSA_ERR_INVALID).
+ */
+csa_status csa_quantize_keys(const uint16_t *x, int64_t rows, int dim, int format, void *codes,
+                             void *scales, void *stream);
+
+/*
+ * csa_index_topk -- lightning-indexer scores and per-query top-k selection.
+ * [EXPLAINER] CSA walk-through: a small attention head scores every compressed block against the
+ * current query and the top-k selector keeps the best; [RABBIT] indexer paragraph: the top 1,024
+ * of about 262,000 entries pass to attention.
+ *
+ * For query s of sequence b at position t = q_pos0[b] + s the visible entries are
+ * i < min(n_entries[b], (t+1)/m) (an entry is usable once its last token exists).  Its score is
+ *     score[i] = sum_h w_idx[b,s,h] * max(0, <q~[b,s,h,:], k~[b,i,:]>)
+ * where k~ are the decoded keys and q~ the query quantised by the keys' rule (per head row for
+ * fp8, per 32 values for MXFP4; unchanged for fp32).  The selection is the min(topk, visible)
+ * highest scores, ties to the lower index, written in ascending index order and padded with -1.
+ *
+ *   q_idx      [B, Sq, H_I, D_I]: fp32 when key_format == CSA_KEY_F32, else bf16.
+ *   w_idx      fp32 [B, Sq, H_I].
+ *   k_codes    keys [B, N_cap, ...] in key_format (see csa_key_format); k_scales its scales
+ *              (NULL for CSA_KEY_F32).
+ *   n_entries  device int64 [B]: valid entries per sequence (<= N_cap).
+ *   q_pos0     device int64 [B]: position of query 0 of each sequence.
+ *   topk_idx   out int32 [B, Sq, topk].
+ *   scores     out fp32 [B, Sq, N_cap] or NULL; when given, visible entries get their score and
+ *              the rest -inf (for inspection; it adds traffic).
+ * Limits: 1 <= topk <= 2048; fp8/MXFP4 need D_I == 128 and H_I in {16, 32, 48, 64}; fp32 needs
+ * H_I * D_I <= 2048 with D_I % 4 == 0; 1 <= N_cap <= 2^21; m >= 1.
+ */
+csa_status csa_index_topk(const void *q_idx, const float *w_idx, const void *k_codes,
+                          const void *k_scales, int key_format, int B, int Sq, int H_I, int D_I,
+                          int64_t N_cap, const int64_t *n_entries, const int64_t *q_pos0, int m,
+                          int topk, int32_t *topk_idx, float *scores, void *workspace,
+                          size_t workspace_bytes, void *stream);
+size_t csa_index_topk_workspace_bytes(int B, int Sq, int64_t N_cap, int topk);
+
+/*
+ * csa_attend -- CSA core attention: shared-KV multi-query attention over the selected compressed
+ * entries plus the sliding window, in one joint softmax.
+ * [EXPLAINER] CSA walk-through: each query head attends to the picked set plus a sliding window of
+ * the most recent tokens; [SUMMARY] 2.3: shared-KV multi-query attention, RMSNorm on the query
+ * heads before core attention; [DEVTO] partial RoPE; [RABBIT] sliding-window paragraph: the
+ * window holds the most recent 128 tokens.
+ *
+ * For query s of sequence b at t = q_pos0[b] + s, every head h uses
+ *     q^ = RoPE(RMSNorm(q[b,s,h,:]; q_norm_w, eps), t)
+ * and the rows X = { entries[b, i] : i in topk_idx[b,s,:], i >= 0 } followed by
+ * { win_rows[b, p - win_pos0[b]] : max(0, t-window+1) <= p <= t }.  K = V = the row.
+ *     out[b,s,h] = sum_x softmax_x(softmax_scale * <q^, x>) x,  lse[b,s,h] = log-sum-exp (natural).
+ *
+ *   q          bf16 [B, Sq, H, D] raw query heads; q_norm_w bf16 [D] or NULL (ones).
+ *   entries    bf16 [B, N_cap, D] compressed entries (as written by csa_compress).
+ *   topk_idx   int32 [B, Sq, topk]; -1 marks an empty slot.
+ *   win_rows   bf16 [B, W_cap, D] prepared rows; the caller guarantees the window's positions are
+ *              inside [win_pos0[b], win_pos0[b] + W_cap).
+ *   out        bf16 [B, Sq, H, D]; lse fp32 [B, Sq, H] or NULL.
+ * Limits: D in {64, 128, 256, 512}; H >= 1 (heads are processed in blocks of 16);
+ *         rope_dim % 4 == 0, rope_dim <= D; 1 <= window <= 4096; 1 <= topk <= 2048.
+ */
+csa_status csa_attend(const uint16_t *q, const uint16_t *q_norm_w, const uint16_t *entries,
+                      int64_t N_cap, const int32_t *topk_idx, int topk, const uint16_t *win_rows,
+                      int64_t W_cap, const int64_t *win_pos0, const int64_t *q_pos0, int B, int Sq,
+                      int H, int D, int rope_dim, int window, float softmax_scale, float rope_base,
+                      float eps, uint16_t *out, float *lse, void *workspace,
+                      size_t workspace_bytes, void *stream);
+size_t csa_attend_workspace_bytes(int B, int Sq, int H, int D, int topk, int window);
+
+/*
+ * hca_attend -- HCA core attention: dense over every visible compressed entry plus the window.
+ * [EXPLAINER] HCA walk-through: every query attends to all compressed entries -- the same
+ * multi-query attention math on a much shorter sequence -- plus a sliding window of recent
+ * uncompressed tokens.
+ *
+ * As csa_attend with the selection replaced by entries 0 .. min(n_entries[b], (t+1)/m) - 1.
+ * Limits as csa_attend; N_cap < 2^31.
+ */
+csa_status hca_attend(const uint16_t *q, const uint16_t *q_norm_w, const uint16_t *entries,
+                      int64_t N_cap, const int64_t *n_entries, int m, const uint16_t *win_rows,
+                      int64_t W_cap, const int64_t *win_pos0, const int64_t *q_pos0, int B, int Sq,
+                      int H, int D, int rope_dim, int window, float softmax_scale, float rope_base,
+                      float eps, uint16_t *out, float *lse, void *workspace,
+                      size_t workspace_bytes, void *stream);
+size_t hca_attend_workspace_bytes(int B, int Sq, int H, int D, int64_t N_cap, int window);
+
+/* Text for a status code (static storage). */
+const char *csa_status_string(csa_status s);
+/* Thread-local detail of the last failed call on this thread ("" if none). */
+const char *csa_last_error(void);
+
+/*
+ * Kernel timing for measurement tools.  csa_timing_enable(1) clears the counters and makes every
+ * later launch record a pair of HIP events on its stream; csa_timing_enable(0) stops recording.
+ * csa_timing_read() waits for the recorded events and returns the summed duration (ms) and the
+ * launch count for one kernel name: "compress", "quantize", "index_score", "index_merge",
+ * "attend_split", "attend_combine".  Not for use while a stream is being captured into a graph.
+ */
+void csa_timing_enable(int on);
+csa_status csa_timing_read(const char *kernel, double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H */

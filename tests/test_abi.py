@@ -1,0 +1,139 @@
+"""The C-ABI library loads, exports every function include/csa.h declares, and rejects bad
+arguments on the host (before any HIP call -- these tests need no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from compressed_sparse_attention_03_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ops.LIB_PATH), reason="libcsa.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*\b([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_the_four_operations():
+    names = declared_functions()
+    for n in ("csa_compress", "csa_index_topk", "csa_attend", "hca_attend", "csa_quantize_keys"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(ops.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+    assert set(ops._SIGS) <= set(declared_functions())
+
+
+def test_status_strings():
+    L = ops.lib()
+    assert L.csa_status_string(0) == b"ok"
+    assert b"invalid" in L.csa_status_string(1)
+    assert b"workspace" in L.csa_status_string(3)
+
+
+def _compress(**kw):
+    L = ops.lib()
+    a = dict(c=16, z=16, bias=16, norm_w=None, B=1, n_new=64, halo=0, d=64, m=4, overlap=1, rope_dim=16,
+             pos0=0, rope_base=10000.0, eps=1e-6, entries=16, win_rows=None, stream=None)
+    a.update(kw)
+    return L.csa_compress(*[ctypes.c_void_p(v) if k in ("c", "z", "bias", "norm_w", "entries", "win_rows", "stream")
+                            and v is not None else v for k, v in a.items()])
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(d=100), b"d must be"),
+    (dict(m=0), b"m must be"),
+    (dict(n_new=62), b"multiple of m"),
+    (dict(pos0=8, halo=0), b"halo"),
+    (dict(pos0=6), b"pos0"),
+    (dict(rope_dim=18), b"rope_dim"),
+    (dict(eps=0.0), b"eps"),
+    (dict(c=None), b"must not be NULL"),
+    (dict(entries=24), b"aligned"),
+])
+def test_compress_rejects_bad_arguments(kw, needle):
+    assert _compress(**kw) == 1
+    assert needle in ops.lib().csa_last_error()
+
+
+def test_zero_sized_calls_are_no_ops():
+    assert _compress(B=0, c=None) == 0
+    assert _compress(n_new=0, c=None) == 0
+
+
+def _index(**kw):
+    L = ops.lib()
+    a = dict(q_idx=16, w_idx=16, k_codes=16, k_scales=16, fmt=1, B=1, Sq=1, H_I=64, D_I=128, N_cap=1024,
+             n_entries=16, q_pos0=16, m=4, topk=64, topk_idx=16, scores=None, ws=16, ws_bytes=1 << 30,
+             stream=None)
+    a.update(kw)
+    ptrs = ("q_idx", "w_idx", "k_codes", "k_scales", "n_entries", "q_pos0", "topk_idx", "scores", "ws", "stream")
+    return L.csa_index_topk(*[ctypes.c_void_p(v) if k in ptrs and v is not None else v for k, v in a.items()])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fmt=7), 1),
+    (dict(topk=0), 1),
+    (dict(topk=4096), 1),
+    (dict(D_I=64), 2),
+    (dict(H_I=40), 2),
+    (dict(N_cap=1 << 22), 1),
+    (dict(k_scales=None), 1),
+    (dict(ws_bytes=16), 3),
+    (dict(ws=None), 3),
+    (dict(fmt=0, H_I=64, D_I=128), 1),     # fp32 keys: H_I * D_I too large
+])
+def test_index_rejects_bad_arguments(kw, status):
+    assert _index(**kw) == status
+
+
+def test_workspace_queries_are_host_only():
+    L = ops.lib()
+    # at least 4*k candidate keys (8 bytes) per query are kept
+    assert L.csa_index_topk_workspace_bytes(4, 1, 262144, 1024) >= 4 * (4 * 1024) * 8
+    assert L.csa_attend_workspace_bytes(4, 1, 64, 512, 1024, 128) > 0
+    assert L.hca_attend_workspace_bytes(8, 1, 64, 512, 8192, 128) > 0
+
+
+def _attend(fn="csa_attend", **kw):
+    L = ops.lib()
+    a = dict(q=16, q_norm_w=None, entries=16, N_cap=1024, sel=16, topk=64, win_rows=16, W_cap=128,
+             win_pos0=16, q_pos0=16, B=1, Sq=1, H=64, D=512, rope_dim=64, window=128, scale=0.04,
+             base=10000.0, eps=1e-6, out=16, lse=None, ws=16, ws_bytes=1 << 30, stream=None)
+    if fn == "hca_attend":
+        a["topk"] = 128  # m
+    a.update(kw)
+    ptrs = ("q", "q_norm_w", "entries", "sel", "win_rows", "win_pos0", "q_pos0", "out", "lse", "ws", "stream")
+    return getattr(L, fn)(*[ctypes.c_void_p(v) if k in ptrs and v is not None else v for k, v in a.items()])
+
+
+@pytest.mark.parametrize("fn", ["csa_attend", "hca_attend"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), 2),
+    (dict(H=0), 1),
+    (dict(rope_dim=66), 1),
+    (dict(window=0), 1),
+    (dict(scale=-1.0), 1),
+    (dict(q=None), 1),
+    (dict(ws=None, B=4), 3),
+])
+def test_attend_rejects_bad_arguments(fn, kw, status):
+    assert _attend(fn, **kw) == status
+
+
+def test_quantize_rejects_bad_arguments():
+    L = ops.lib()
+    v = ctypes.c_void_p(16)
+    assert L.csa_quantize_keys(v, 10, 128, 0, v, v, None) == 1      # fp32 is not a code format
+    assert L.csa_quantize_keys(v, 10, 100, 1, v, v, None) == 1
+    assert L.csa_quantize_keys(v, 0, 128, 1, None, None, None) == 0
