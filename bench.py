@@ -1,0 +1,315 @@
+"""Benchmark: CSA decode query-tokens/s at 1M and 128K context on one MI355X, with the roofline of
+the dominant kernel and the CPU oracle timed beside it.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs main,d128,c32k,hca] [--mode bench|copy]
+
+One step = one decode pass of the whole hot path over one batch: csa_index_topk (lightning-indexer
+scores + top-k) then csa_attend (shared-KV attention over the selected entries + window) for CSA;
+hca_attend for HCA.  Inputs are seeded synthetic tensors resident in HBM before timing.  Every
+step reads one of several copies of the caches, enough copies that the working set exceeds the
+256 MB Infinity Cache by 4x, so each step streams from HBM.  The steps are replayed from a HIP
+graph (launch overhead would otherwise exceed the ~15 us step).  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from compressed_sparse_attention_03_amd import inputs as gen  # noqa: E402
+from compressed_sparse_attention_03_amd import ops  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "CSA decode query-tokens/sec at 128K and 1M ctx; % of peak HBM GB/s"
+KEY_BYTES = {"fp8": 128 + 4, "mxfp4": 64 + 4}
+MALL_BYTES = 256e6
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev_bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+# ---- algorithmic bytes (each item the method must touch, once per step) ----------------------
+def csa_query_bytes(w):
+    keys = w.N * KEY_BYTES[w.key_format]
+    rows = (w.topk + w.window) * w.d * 2
+    q_out = 2 * w.H * w.d * 2
+    idx_q = w.H_I * w.D_I * 2 + w.H_I * 4
+    sel = w.topk * 4 * 2
+    return keys + rows + q_out + idx_q + sel
+
+
+def hca_query_bytes(w):
+    return (w.N + w.window) * w.d * 2 + 2 * w.H * w.d * 2
+
+
+def index_score_bytes(w):
+    return w.B * (w.N * KEY_BYTES[w.key_format] + w.H_I * w.D_I * 2 + w.H_I * 4)
+
+
+# ---- one workload leg --------------------------------------------------------------------------
+class Leg:
+    def __init__(self, w: gen.Workload):
+        self.w = w
+        self.step_bytes = w.B * (hca_query_bytes(w) if w.kind == "hca_decode" else csa_query_bytes(w))
+        self.ncopies = max(2, math.ceil(4 * MALL_BYTES / self.step_bytes))
+        log(f"[{w.name}] generating inputs; {self.ncopies} copies of {self.step_bytes / 1e6:.1f} MB/step")
+        t0 = time.time()
+        x = gen.decode_inputs(w)
+        self.t = dev(x["t"])
+        self.win_pos0 = dev(x["win_pos0"])
+        self.n_ent = dev(x["n_entries"])
+        q, ent, win = dev_bf16(x["q"]), dev_bf16(x["entries"]), dev_bf16(x["win_rows"])
+        self.q = [q] + [q.clone() for _ in range(self.ncopies - 1)]
+        self.ent = [ent] + [ent.clone() for _ in range(self.ncopies - 1)]
+        self.win = [win] + [win.clone() for _ in range(self.ncopies - 1)]
+        self.out = [torch.empty_like(q) for _ in range(self.ncopies)]
+        if w.kind == "csa_decode":
+            qi, wi = dev_bf16(x["q_idx"]), dev(x["w_idx"])
+            codes, scales = ops.csa_quantize_keys(dev_bf16(x["k_idx"]), w.key_format)
+            self.q_idx = [qi] + [qi.clone() for _ in range(self.ncopies - 1)]
+            self.w_idx = [wi] + [wi.clone() for _ in range(self.ncopies - 1)]
+            self.codes = [codes] + [codes.clone() for _ in range(self.ncopies - 1)]
+            self.scales = [scales] + [scales.clone() for _ in range(self.ncopies - 1)]
+            self.sel = [torch.empty((w.B, 1, w.topk), dtype=torch.int32, device="cuda") for _ in range(self.ncopies)]
+            self.ws_i = ops.index_topk_workspace(w.B, 1, w.N, w.topk)
+            self.ws_a = ops.attend_workspace(w.B, 1, w.H, w.d, w.topk, w.window)
+        else:
+            self.ws_a = ops.hca_workspace(w.B, 1, w.H, w.d, w.N, w.window)
+        del x
+        torch.cuda.synchronize()
+        log(f"[{w.name}] inputs ready in {time.time() - t0:.1f}s")
+
+    def step(self, i):
+        w, c = self.w, i % self.ncopies
+        if w.kind == "csa_decode":
+            ops.csa_index_topk(self.q_idx[c], self.w_idx[c], self.codes[c], self.scales[c], key_format=w.key_format,
+                               n_entries=self.n_ent, q_pos0=self.t, m=w.m, topk=w.topk, workspace=self.ws_i,
+                               topk_out=self.sel[c])
+            ops.csa_attend(self.q[c], self.ent[c], self.sel[c], self.win[c], self.win_pos0, self.t,
+                           rope_dim=w.rope_dim, window=w.window, workspace=self.ws_a, out=self.out[c])
+        else:
+            ops.hca_attend(self.q[c], self.ent[c], self.n_ent, self.win[c], self.win_pos0, self.t, m=w.m,
+                           rope_dim=w.rope_dim, window=w.window, workspace=self.ws_a, out=self.out[c])
+
+    def kernel_times(self, n=None):
+        """Average per-kernel durations (us) from HIP events recorded around each launch."""
+        n = self.ncopies * 2 if n is None else n
+        for i in range(self.ncopies):
+            self.step(i)
+        torch.cuda.synchronize()
+        ops.timing_enable(True)
+        for i in range(n):
+            self.step(i)
+        torch.cuda.synchronize()
+        res = {}
+        for k in ("index_score", "index_merge", "attend_split", "attend_combine"):
+            ms, cnt = ops.timing_read(k)
+            if cnt:
+                res[k] = 1000.0 * ms / cnt
+        ops.timing_enable(False)
+        return res
+
+    def run(self, steps, warmup, graph=True):
+        """Time exactly `steps` steps after `warmup` steps; returns seconds."""
+        G = self.ncopies
+        if graph:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for i in range(G):                      # prime the allocator-free path once
+                    self.step(i)
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            full = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(full):
+                for i in range(G):
+                    self.step(i)
+            singles = []
+            for i in range(G):
+                g1 = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g1):
+                    self.step(i)
+                singles.append(g1)
+
+            def run_n(n):
+                for _ in range(n // G):
+                    full.replay()
+                for i in range(n % G):
+                    singles[i].replay()
+        else:
+            def run_n(n):
+                for i in range(n):
+                    self.step(i)
+        run_n(warmup)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run_n(steps)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def free(self):
+        for k in list(self.__dict__):
+            if k != "w" and k != "step_bytes" and k != "ncopies":
+                delattr(self, k)
+        torch.cuda.empty_cache()
+
+
+def profile_traffic(kernel: str, workload: str):
+    """HBM bytes per dispatch from a committed rocprofv3 PMC summary, if it matches the source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "compressed_sparse_attention_03_amd", "csrc", vals.get("source", "indexer.hip"))
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != vals.get("source_sha256_16"):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---- CPU oracle baseline -------------------------------------------------------------------------
+def cpu_baseline(w: gen.Workload, budget_s: float = 12.0):
+    """The oracle as it stands, on the host cores: one decode query of sequence 0 (its full
+    indexer scan, top-k and attention), repeated until the time budget is spent."""
+    from oracle import attention as oa
+    from oracle import indexer as oi
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    x = gen.decode_inputs(w, 0, 1)
+    f = lambda a: gen.bf16_bits_to_f32(a).astype(np.float64)
+    kt = np.empty((w.N, w.D_I))
+    for i in range(0, w.N, 65536):                       # the stored (quantised) keys: not timed
+        codes, sc = oi.quantize_keys(f(x["k_idx"][0, i:i + 65536]), w.key_format)
+        kt[i:i + 65536] = oi.dequantize_keys(codes, sc, w.key_format)
+    ent = x["entries"][0]
+    win = f(x["win_rows"][0])
+    t = int(x["t"][0])
+    n, t0 = 0, time.perf_counter()
+    while True:
+        qt = oi.quantize_query(f(x["q_idx"][0, 0]), w.key_format)
+        s = oi.index_scores(qt, x["w_idx"][0, 0].astype(np.float64), kt, w.N)
+        sel = oi.topk_fast(s, w.topk, w.N)
+        oa.csa_attend(f(x["q"][0, 0]), f(ent[sel]), np.arange(w.topk), win, int(x["win_pos0"][0]), t, w.window,
+                      w.rope_dim)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 50:
+            break
+    return {"value": n / el, "unit": "query-tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} decode queries of sequence 0 of {w.name} (indexer over all {w.N} entries, "
+                      f"top-{w.topk}, attention over {w.topk}+{w.window} rows); keys pre-quantised"}
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--legs", default="main,d128,c32k,hca")
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU sharding of this "
+              "path is a design note, not a measured configuration.", file=sys.stderr)
+        sys.exit(2)
+    if args.mode == "copy":
+        copy_calibration()
+        return
+    legs = args.legs.split(",")
+    table = {"main": gen.CSA_DECODE_1M, "d128": gen.CSA_DECODE_128K, "c32k": gen.CSA_DECODE_32K,
+             "hca": gen.HCA_DECODE_1M}
+    results = {}
+    for name in legs:
+        w = table[name]
+        leg = Leg(w)
+        kt = leg.kernel_times()
+        sec = leg.run(args.steps, args.warmup, graph=True)
+        sec_eager = leg.run(min(args.steps, 200), min(args.warmup, 20), graph=False)
+        ms = 1000 * sec / args.steps
+        tok_s = w.B * args.steps / sec
+        r = {"workload": w.name, "value": tok_s, "unit": "query-tokens/s", "ms_per_step": ms,
+             "hbm_frac_step": leg.step_bytes * args.steps / sec / (PEAK_HBM_GBS * 1e9),
+             "bytes_per_step": leg.step_bytes, "copies": leg.ncopies,
+             "eager_ms_per_step": 1000 * sec_eager / min(args.steps, 200), "kernel_us": kt}
+        if w.kind == "csa_decode":
+            ab = index_score_bytes(w)
+            dur = kt["index_score"] * 1e-6
+            r["roofline"] = {"kernel": "index_score", "bound": "hbm", "achieved": ab / dur / 1e9,
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ab / dur / 1e9 / PEAK_HBM_GBS,
+                             "traffic": profile_traffic("index_score", w.name),
+                             "algorithmic_bytes": ab, "avg_us": kt["index_score"]}
+        else:
+            ab = leg.step_bytes
+            dur = (kt.get("attend_split", 0.0) + kt.get("attend_combine", 0.0)) * 1e-6
+            r["roofline"] = {"kernel": "attend_split+attend_combine", "bound": "hbm", "achieved": ab / dur / 1e9,
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ab / dur / 1e9 / PEAK_HBM_GBS,
+                             "traffic": None, "algorithmic_bytes": ab, "avg_us": kt.get("attend_split")}
+        results[name] = r
+        log(json.dumps(r))
+        leg.free()
+        del leg
+    main_name = legs[0]
+    m = results[main_name]
+    w = table[main_name]
+    line = {
+        "metric": METRIC, "value": m["value"], "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": m["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16+" + w.key_format if w.kind == "csa_decode" else "bf16",
+        "data": "synthetic (seeded N(0,1) caches/queries, U(0,1) indexer weights, 16 planted keys)",
+        "config": {"workload": w.name, "batch": w.B, "context": w.T, "entries": w.N, "topk": w.topk,
+                   "window": w.window, "heads": w.H, "head_dim": w.d, "indexer": f"{w.H_I}x{w.D_I} {w.key_format}",
+                   "step": "csa_index_topk + csa_attend, HIP graph"},
+        "hbm_frac_step": m["hbm_frac_step"],
+        "roofline": m["roofline"],
+        "kernel_us": m["kernel_us"],
+        "also": [results[k] for k in legs[1:]],
+    }
+    if not args.no_cpu and w.kind == "csa_decode":
+        log("timing the CPU oracle ...")
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -35,234 +35,314 @@ union Frag8 {      // 8 bf16 = 16 bytes
   v4s h[2];
 };
 
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+union Pack4 {
+  v4bf b;
+  v4s s;
+};
+
+// Round four floats to bf16 (v_cvt_pk_bf16_f32: round to nearest even).
 __device__ __forceinline__ v4s pack4(float a, float b, float c, float d) {
-  uint32_t lo = pack_bf16x2(a, b), hi = pack_bf16x2(c, d);
-  v4s r;
-  r[0] = short(lo & 0xffff); r[1] = short(lo >> 16); r[2] = short(hi & 0xffff); r[3] = short(hi >> 16);
-  return r;
+  Pack4 p;
+  p.b[0] = __bf16(a); p.b[1] = __bf16(b); p.b[2] = __bf16(c); p.b[3] = __bf16(d);
+  return p.s;
 }
 
-// Row pointer for slot `ri` of the query's row list, or nullptr when the slot is empty.
-__device__ __forceinline__ const uint16_t *row_ptr(const AttendArgs &a, int64_t qi, int b, int64_t t,
-                                                  int64_t n_vis, int64_t ri) {
+constexpr int kMaxRowsPerSplit = 2048;
+constexpr float kRescaleSlack = 8.0f;     // log2 units: the running max may lag the true max by 2^8
+
+// Row code of slot `ri` of the query's row list: an entry index (< N_cap), N_cap + window row, or
+// -1 when the slot is empty.
+__device__ __forceinline__ int row_code(const AttendArgs &a, int64_t qi, int b, int64_t t, int64_t n_vis,
+                                        int64_t ri) {
   if (ri < a.n_sel) {
     int64_t e;
     if (a.topk_idx) {
       e = a.topk_idx[qi * a.n_sel + ri];
-      if (e < 0 || e >= a.N_cap) return nullptr;
+      if (e < 0 || e >= a.N_cap) return -1;
     } else {
       e = ri;
-      if (e >= n_vis) return nullptr;
+      if (e >= n_vis) return -1;
     }
-    return a.entries + (int64_t(b) * a.N_cap + e) * a.D;
+    return int(e);
   }
   const int64_t w = ri - a.n_sel;
-  if (w >= a.window) return nullptr;
+  if (w >= a.window) return -1;
   const int64_t p = t - a.window + 1 + w;                  // window position
-  if (p < 0) return nullptr;
+  if (p < 0) return -1;
   const int64_t wr = p - a.win_pos0[b];
-  if (wr < 0 || wr >= a.W_cap) return nullptr;
-  return a.win_rows + (int64_t(b) * a.W_cap + wr) * a.D;
+  if (wr < 0 || wr >= a.W_cap) return -1;
+  return int(a.N_cap + wr);
 }
 
+// Workgroup -> (query, split, head block).  Workgroups are dispatched to the 8 XCDs round-robin by
+// linear id, so the head blocks of one (query, split) -- which read the same rows -- are given ids
+// that are equal modulo 8 and share that XCD's L2.
+struct AttendTile {
+  int64_t qi;
+  int split, hb;
+  bool valid;
+};
+__device__ __forceinline__ AttendTile attend_tile(const AttendArgs &a, int64_t n_queries) {
+  const int64_t L = blockIdx.x;
+  const int64_t x = L & 7, rest = L >> 3;
+  const int hb = int(rest % a.plan.n_hb);
+  const int64_t pair = (rest / a.plan.n_hb) * 8 + x;
+  AttendTile t;
+  t.valid = pair < n_queries * a.plan.n_splits;
+  t.qi = pair / a.plan.n_splits;
+  t.split = int(pair % a.plan.n_splits);
+  t.hb = hb;
+  return t;
+}
+
+// Waves per workgroup: each wave owns D/NW channels (at least 32).
 template <int D>
-__global__ void __launch_bounds__(256) attend_split_kernel(AttendArgs a) {
-  constexpr int NS = D / 32;          // 32-channel steps
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+constexpr int waves_of() { return D >= 128 ? 4 : D / 32; }
+
+template <int D>
+__global__ void __launch_bounds__(64 * waves_of<D>()) attend_split_kernel(AttendArgs a, int64_t n_queries) {
+  constexpr int NW = waves_of<D>();
+  constexpr int NT = 64 * NW;
+  constexpr int QD = D / NW;          // channels owned by one wave
+  constexpr int NSQ = QD / 32;        // its 32-channel steps
+  constexpr int QCH = D / 32;         // prologue: threads per head (32 channels each)
+  constexpr int RING = 4;             // 16-row chunks in flight per wave
+  __shared__ __align__(16) uint16_t s_q[16 * D];
+  __shared__ int s_row[kMaxRowsPerSplit];
+  __shared__ float s_cs[256], s_sn[256];
+  __shared__ __align__(16) float s_part[2][NW][64][4];   // partial S^T per wave, per lane
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
-  const int split = blockIdx.x, hb = blockIdx.y;
-  const int64_t qi = blockIdx.z;
+  const AttendTile tl = attend_tile(a, n_queries);
+  if (!tl.valid) return;
+  const int split = tl.split, hb = tl.hb;
+  const int64_t qi = tl.qi;
   const int b = int(qi / a.Sq), s_idx = int(qi % a.Sq);
   const int64_t t = a.q_pos0[b] + s_idx;
   const int64_t n_vis = a.topk_idx ? 0 : min(a.n_entries[b], (t + 1) / a.m);
-  const int head = hb * 16 + r;
-  const bool head_ok = head < a.H;
+  const int64_t r0 = int64_t(split) * a.plan.rows_per_split;
+  const int64_t r1 = min(int64_t(a.plan.n_rows), r0 + a.plan.rows_per_split);
+  const int nr = int(r1 - r0);
+  const int n_chunks = (nr + 15) >> 4;
+  const int ch0 = wave * QD;          // first channel of this wave
 
-  // ---- q^ = RoPE(RMSNorm(q)) * scale * log2(e), as B operands: lane holds channels 32s+8g..+7
-  Frag8 qf[NS];
-  {
-    float qv[NS][8];
-    const uint16_t *qrow = a.q + (qi * a.H + (head_ok ? head : 0)) * D;
-    float ss = 0.f;
+  // ---- prologue.  The raw q chunk (and norm weights) of this thread are loaded first: loads
+  // complete in issue order, so anything issued later (the row prefetch) does not delay them.
+  const bool qthread = tid < 16 * QCH;
+  const int qh = tid / QCH, qc = tid % QCH;
+  const int qhead = hb * 16 + qh;
+  uint4 qraw[4], wraw[4];
+  if (qthread) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(a.q + (qi * a.H + (qhead < a.H ? qhead : 0)) * D + 32 * qc);
+    const uint4 *wsrc = reinterpret_cast<const uint4 *>(a.q_norm_w ? a.q_norm_w + 32 * qc : a.q + 32 * qc);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      uint4 w = head_ok ? *reinterpret_cast<const uint4 *>(qrow + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0);
-      qv[s][0] = bf16lo(w.x); qv[s][1] = bf16hi(w.x); qv[s][2] = bf16lo(w.y); qv[s][3] = bf16hi(w.y);
-      qv[s][4] = bf16lo(w.z); qv[s][5] = bf16hi(w.z); qv[s][6] = bf16lo(w.w); qv[s][7] = bf16hi(w.w);
+    for (int k = 0; k < 4; ++k) { qraw[k] = src[k]; wraw[k] = wsrc[k]; }
+  }
+  // row codes and rotary angles; the first chunks' loads go out before q^ is built
+  for (int i = tid; i < nr; i += NT) s_row[i] = row_code(a, qi, b, t, n_vis, r0 + i);
+  const int npairs = a.rope_dim / 2;
+  for (int u = tid; u < npairs; u += NT) rope_cos_sin(t, u, a.rope_dim, a.log2_base, &s_cs[u], &s_sn[u]);
+  const uint16_t *ent_b = a.entries + int64_t(b) * a.N_cap * D;
+  const uint16_t *win_b = a.win_rows + int64_t(b) * a.W_cap * D;
+  __syncthreads();
+
+  // ring of row fragments: lane (r, g) holds row r of the chunk, channels ch0 + 32s + 8g .. +7
+  Frag8 ring[RING][NSQ];
+  int codes[RING];
+  // Loads are unconditional (an empty slot reads entry row 0, which exists and is finite; its
+  // softmax weight is exactly 0): branch-free code lets the compiler wait only for the chunk in use
+  // instead of every outstanding load.
+  auto issue = [&](int c, int slot) {
+    const int i = c * 16 + r;
+    const int code = (c < n_chunks && i < nr) ? s_row[i] : -1;
+    codes[slot] = code;
+    const uint16_t *rp = code < 0 ? ent_b
+                                  : (code < a.N_cap ? ent_b + int64_t(code) * D : win_b + (int64_t(code) - a.N_cap) * D);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ss += qv[s][j] * qv[s][j];
-    }
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
-    const float inv = rsqrtf(ss / float(D) + a.eps) * a.scale_log2;
-    const int rope0 = D - a.rope_dim;
+    for (int s = 0; s < NSQ; ++s) ring[slot][s].u = *reinterpret_cast<const uint4 *>(rp + ch0 + 32 * s + 8 * g);
+  };
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
+  for (int c = 0; c < RING - 1; ++c) issue(c, c);
+
+  // q^ = RoPE(RMSNorm(q)) * scale * log2(e) for the 16 heads, into LDS
+  if (qthread) {
+    {
+      const int h = qh, c = qc;
+      float v[32];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int ch = 32 * s + 8 * g + j;
-        qv[s][j] *= inv * (a.q_norm_w ? bf16_to_f32(a.q_norm_w[ch]) : 1.0f);
+      for (int k = 0; k < 4; ++k) {
+        const uint4 w = qraw[k];
+        v[8 * k + 0] = bf16lo(w.x); v[8 * k + 1] = bf16hi(w.x); v[8 * k + 2] = bf16lo(w.y);
+        v[8 * k + 3] = bf16hi(w.y); v[8 * k + 4] = bf16lo(w.z); v[8 * k + 5] = bf16hi(w.z);
+        v[8 * k + 6] = bf16lo(w.w); v[8 * k + 7] = bf16hi(w.w);
       }
-      if (32 * s + 8 * g + 8 > rope0) {
+      if (qhead >= a.H) {
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const int ch = 32 * s + 8 * g + j;
+        for (int k = 0; k < 32; ++k) v[k] = 0.f;
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) ss += v[k] * v[k];
+#pragma unroll
+      for (int o = 1; o < QCH; o <<= 1) ss += __shfl_xor(ss, o, 64);   // the head's QCH threads
+      const float inv = rsqrtf(ss / float(D) + a.eps) * a.scale_log2;
+      float gw[32];
+      const bool has_w = a.q_norm_w != nullptr;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 w = wraw[k];
+        gw[8 * k + 0] = bf16lo(w.x); gw[8 * k + 1] = bf16hi(w.x); gw[8 * k + 2] = bf16lo(w.y);
+        gw[8 * k + 3] = bf16hi(w.y); gw[8 * k + 4] = bf16lo(w.z); gw[8 * k + 5] = bf16hi(w.z);
+        gw[8 * k + 6] = bf16lo(w.w); gw[8 * k + 7] = bf16hi(w.w);
+      }
+      if (!has_w) {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) gw[k] = 1.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < 32; ++k) v[k] *= inv * gw[k];
+      const int rope0 = D - a.rope_dim;
+      if (32 * c + 32 > rope0) {
+#pragma unroll
+        for (int k = 0; k < 32; k += 2) {
+          const int ch = 32 * c + k;
           if (ch >= rope0) {
-            float cs, sn;
-            rope_cos_sin(t, (ch - rope0) >> 1, a.rope_dim, a.log2_base, &cs, &sn);
-            const float x0 = qv[s][j], x1 = qv[s][j + 1];
-            qv[s][j] = x0 * cs - x1 * sn;
-            qv[s][j + 1] = x0 * sn + x1 * cs;
+            const int u = (ch - rope0) >> 1;
+            const float cs = s_cs[u], sn = s_sn[u], x0 = v[k], x1 = v[k + 1];
+            v[k] = x0 * cs - x1 * sn;
+            v[k + 1] = x0 * sn + x1 * cs;
           }
         }
       }
-      qf[s].u = make_uint4(pack_bf16x2(qv[s][0], qv[s][1]), pack_bf16x2(qv[s][2], qv[s][3]),
-                           pack_bf16x2(qv[s][4], qv[s][5]), pack_bf16x2(qv[s][6], qv[s][7]));
+      uint4 *dst = reinterpret_cast<uint4 *>(s_q + h * D + 32 * c);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        Pack4 lo, hi;
+        lo.s = pack4(v[8 * k], v[8 * k + 1], v[8 * k + 2], v[8 * k + 3]);
+        hi.s = pack4(v[8 * k + 4], v[8 * k + 5], v[8 * k + 6], v[8 * k + 7]);
+        dst[k] = make_uint4(uint32_t(uint16_t(lo.s[0])) | (uint32_t(uint16_t(lo.s[1])) << 16),
+                            uint32_t(uint16_t(lo.s[2])) | (uint32_t(uint16_t(lo.s[3])) << 16),
+                            uint32_t(uint16_t(hi.s[0])) | (uint32_t(uint16_t(hi.s[1])) << 16),
+                            uint32_t(uint16_t(hi.s[2])) | (uint32_t(uint16_t(hi.s[3])) << 16));
+      }
     }
   }
+  __syncthreads();
+  Frag8 qf[NSQ];
+#pragma unroll
+  for (int s = 0; s < NSQ; ++s) qf[s].u = *reinterpret_cast<const uint4 *>(s_q + r * D + ch0 + 32 * s + 8 * g);
+
   // identity fragment for the V transposes: element j of lane (n, g) is 1 iff n = 4g + j
   v4s ident;
 #pragma unroll
   for (int j = 0; j < 4; ++j) ident[j] = ((r >> 2) == g && (r & 3) == j) ? short(0x3f80) : short(0);
 
-  v4f o[2 * NS];
+  v4f o[2 * NSQ];
 #pragma unroll
-  for (int k = 0; k < 2 * NS; ++k) o[k] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < 2 * NSQ; ++k) o[k] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int64_t r0 = int64_t(split) * a.plan.rows_per_split;
-  const int64_t r1 = min(int64_t(a.plan.n_rows), r0 + a.plan.rows_per_split);
-  const int n_chunks = int((r1 - r0 + 15) / 16);
-  Frag8 kv[NS];
-  const uint16_t *rp = nullptr;
-  int c = wave;
-  if (c < n_chunks) {
-    const int64_t ri = r0 + int64_t(c) * 16 + r;
-    rp = ri < r1 ? row_ptr(a, qi, b, t, n_vis, ri) : nullptr;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-      kv[s].u = rp ? *reinterpret_cast<const uint4 *>(rp + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0);
-  }
-  for (; c < n_chunks; c += 4) {
-    // row validity of the 16 rows of this chunk (lane r holds row r)
-    const uint64_t vmask = __ballot(rp != nullptr);
-    // prefetch the next chunk of this wave
-    Frag8 nx[NS];
-    const uint16_t *np = nullptr;
-    const int cn = c + 4;
-    if (cn < n_chunks) {
-      const int64_t ri = r0 + int64_t(cn) * 16 + r;
-      np = ri < r1 ? row_ptr(a, qi, b, t, n_vis, ri) : nullptr;
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        nx[s].u = np ? *reinterpret_cast<const uint4 *>(np + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0);
-    }
-    // S^T: lane (r, g) element v = <q^_head(r), row 4g+v>
+  // one chunk: all waves sum their partial S^T through LDS, update the (identical) softmax state
+  // and accumulate their channels of O.  `slot` is a compile-time ring position after unrolling.
+  auto chunk = [&](int c, int slot) {
+    const uint64_t vmask = __ballot(codes[slot] >= 0);
     v4f st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < NS; ++s) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[s].b, qf[s].b, st, 0, 0, 0);
+    for (int s = 0; s < NSQ; ++s) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[slot][s].b, qf[s].b, st, 0, 0, 0);
+    *reinterpret_cast<v4f *>(&s_part[c & 1][wave][lane][0]) = st;
+    __syncthreads();
+    v4f full = *reinterpret_cast<const v4f *>(&s_part[c & 1][0][lane][0]);
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      const v4f x = *reinterpret_cast<const v4f *>(&s_part[c & 1][w][lane][0]);
+      full[0] += x[0]; full[1] += x[1]; full[2] += x[2]; full[3] += x[3];
+    }
     float sv[4], cmax = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      sv[v] = ((vmask >> (4 * g + v)) & 1) ? st[v] : -INFINITY;
+      sv[v] = ((vmask >> (4 * g + v)) & 1) ? full[v] : -INFINITY;
       cmax = fmaxf(cmax, sv[v]);
     }
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+    // lazy running max: rescale only when some head's max grew past the slack
+    const bool grow = cmax > m_run + kRescaleSlack || (m_run == -INFINITY && cmax != -INFINITY);
+    if (__any(grow)) {
+      const float m_new = fmaxf(m_run, cmax);
+      const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+      float av[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) av[v] = __shfl(alpha, 4 * g + v, 64);
+#pragma unroll
+      for (int k = 0; k < 2 * NSQ; ++k) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[k][v] *= av[v];
+      }
+    }
     float p[4], psum = 0.f;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      p[v] = (sv[v] == -INFINITY) ? 0.f : exp2f(sv[v] - m_new);
+      p[v] = (sv[v] == -INFINITY) ? 0.f : exp2f(sv[v] - m_run);
       psum += p[v];
     }
     psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // O rows are heads 4g+v: fetch their rescale factors from lanes 4g+v
-    float av[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) av[v] = __shfl(alpha, 4 * g + v, 64);
-#pragma unroll
-    for (int k = 0; k < 2 * NS; ++k) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) o[k][v] *= av[v];
-    }
+    l_run += psum;
     const v4s pf = pack4(p[0], p[1], p[2], p[3]);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
+    for (int s = 0; s < NSQ; ++s) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         v4f vt = {0.f, 0.f, 0.f, 0.f};
-        vt = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kv[s].h[h], ident, vt, 0, 0, 0);
-        const v4s vb = pack4(vt[0], vt[1], vt[2], vt[3]);
+        vt = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ring[slot][s].h[h], ident, vt, 0, 0, 0);
+        const v4s vb = pack4(vt[0], vt[1], vt[2], vt[3]);     // exact: the values are bf16
         o[2 * s + h] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pf, vb, o[2 * s + h], 0, 0, 0);
       }
     }
-    if (cn < n_chunks) {
+  };
+  for (int c0 = 0; c0 < n_chunks; c0 += RING) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) kv[s] = nx[s];
-      rp = np;
+    for (int k = 0; k < RING; ++k) {
+      if (c0 + k < n_chunks) {
+        issue(c0 + k + RING - 1, (k + RING - 1) % RING);    // keep RING-1 chunks ahead in flight
+        chunk(c0 + k, k);
+      }
     }
   }
 
-  // ---- merge the four waves --------------------------------------------------------------
-  __shared__ float s_m[4][16], s_l[4][16];
-  __shared__ float s_o[16][D];
-  if (lane < 16) { s_m[wave][r] = m_run; s_l[wave][r] = l_run; }
-  __syncthreads();
-  float cw[4];                           // this wave's weight for heads 4g+v
+  // ---- every wave holds the same (m, l) and its own channels of O: normalise and write -------
+  // O element (block 2s+h, v) of lane (r, g): head 4g+v, channel ch0 + 32s + 8(r>>2) + 4h + (r&3)
+  float lv[4], mv[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) { lv[v] = __shfl(l_run, 4 * g + v, 64); mv[v] = __shfl(m_run, 4 * g + v, 64); }
+  const bool direct = a.plan.n_splits == 1;
+  float *po = static_cast<float *>(a.workspace);
+  float *plse = po + n_queries * a.H * a.plan.n_splits * D;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int h = 4 * g + v;
-    const float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
-    const float mw = s_m[wave][h];
-    cw[v] = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-  }
-  // O element (block 2s+h, v) of lane (r, g): head 4g+v, channel 32s + 8(r>>2) + 4h + (r&3)
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
+    const int gh = hb * 16 + 4 * g + v;
+    if (gh >= a.H) continue;
+    const float invL = lv[v] > 0.f ? 1.0f / lv[v] : 0.f;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
+    for (int s = 0; s < NSQ; ++s) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int ch = 32 * s + 8 * (r >> 2) + 4 * h + (r & 3);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float x = o[2 * s + h][v] * cw[v];
-            if (w == 0) s_o[4 * g + v][ch] = x; else s_o[4 * g + v][ch] += x;
-          }
-        }
+      for (int h = 0; h < 2; ++h) {
+        const int ch = ch0 + 32 * s + 8 * (r >> 2) + 4 * h + (r & 3);
+        const float x = o[2 * s + h][v] * invL;
+        if (direct) a.out[(qi * a.H + gh) * D + ch] = __builtin_bit_cast(uint16_t, __bf16(x));
+        else po[((qi * a.H + gh) * a.plan.n_splits + split) * int64_t(D) + ch] = x;
       }
     }
-    __syncthreads();
-  }
-  // normalise and write: the partial of this slice, or the final output when there is one slice
-  const bool direct = a.plan.n_splits == 1;
-  for (int i = threadIdx.x; i < 16 * D / 4; i += 256) {
-    const int h = i / (D / 4), ch = (i % (D / 4)) * 4;
-    const int gh = hb * 16 + h;
-    if (gh >= a.H) continue;
-    float L = 0.f, M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
-#pragma unroll
-    for (int w = 0; w < 4; ++w) L += (s_m[w][h] == -INFINITY) ? 0.f : s_l[w][h] * exp2f(s_m[w][h] - M);
-    const float invL = L > 0.f ? 1.0f / L : 0.f;
-    const float4 x = make_float4(s_o[h][ch] * invL, s_o[h][ch + 1] * invL, s_o[h][ch + 2] * invL,
-                                 s_o[h][ch + 3] * invL);
-    if (direct) {
-      uint16_t *dst = a.out + (qi * a.H + gh) * D + ch;
-      *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
-      if (a.lse && ch == 0) a.lse[qi * a.H + gh] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
-    } else {
-      float *po = static_cast<float *>(a.workspace) +
-                  ((qi * a.H + gh) * a.plan.n_splits + split) * int64_t(D);
-      *reinterpret_cast<float4 *>(po + ch) = x;
-      if (ch == 0) {
-        float *plse = static_cast<float *>(a.workspace) +
-                      int64_t(gridDim.z) * a.H * a.plan.n_splits * D;
-        plse[(qi * a.H + gh) * a.plan.n_splits + split] = L > 0.f ? M + log2f(L) : -INFINITY;
+    if (wave == 0 && r == 0) {
+      const float lse2 = lv[v] > 0.f ? mv[v] + log2f(lv[v]) : -INFINITY;
+      if (direct) {
+        if (a.lse) a.lse[qi * a.H + gh] = lse2 * 0.6931471805599453f;
+      } else {
+        plse[(qi * a.H + gh) * a.plan.n_splits + split] = lse2;
       }
     }
   }
@@ -289,8 +369,7 @@ __global__ void __launch_bounds__(D / 4) attend_combine_kernel(AttendArgs a, int
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   uint16_t *dst = a.out + qh * D + ch;
-  *reinterpret_cast<uint2 *>(dst) =
-      make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+  *reinterpret_cast<v4s *>(dst) = pack4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   if (a.lse && threadIdx.x == 0) a.lse[qh] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
 }
 
@@ -301,12 +380,13 @@ AttendPlan plan_attend(int64_t n_queries, int H, int64_t n_sel, int window) {
   p.n_hb = (H + 15) / 16;
   p.n_rows = int(n_sel + window);
   const int64_t pairs = n_queries * p.n_hb;
-  int64_t splits = (256 + pairs - 1) / pairs;
-  const int64_t max_splits = (p.n_rows + 63) / 64;
+  int64_t splits = (512 + pairs - 1) / pairs;
+  const int64_t max_splits = (p.n_rows + 127) / 128;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   int64_t rps = (p.n_rows + splits - 1) / splits;
-  rps = (rps + 63) / 64 * 64;
+  rps = (rps + 15) / 16 * 16;
+  if (rps > kMaxRowsPerSplit) rps = kMaxRowsPerSplit;
   p.rows_per_split = int(rps);
   p.n_splits = int((p.n_rows + rps - 1) / rps);
   return p;
@@ -319,12 +399,14 @@ size_t attend_workspace_bytes(int64_t n_queries, int H, int D, int64_t n_sel, in
 }
 
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream) {
-  dim3 grid(unsigned(a.plan.n_splits), unsigned(a.plan.n_hb), unsigned(int64_t(a.B) * a.Sq));
+  const int64_t nq = int64_t(a.B) * a.Sq;
+  const int64_t pairs = nq * a.plan.n_splits;
+  dim3 grid(unsigned(((pairs + 7) / 8) * 8 * a.plan.n_hb));
   switch (a.D) {
-    case 64: hipLaunchKernelGGL(attend_split_kernel<64>, grid, dim3(256), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL(attend_split_kernel<128>, grid, dim3(256), 0, stream, a); break;
-    case 256: hipLaunchKernelGGL(attend_split_kernel<256>, grid, dim3(256), 0, stream, a); break;
-    case 512: hipLaunchKernelGGL(attend_split_kernel<512>, grid, dim3(256), 0, stream, a); break;
+    case 64: hipLaunchKernelGGL(attend_split_kernel<64>, grid, dim3(64 * waves_of<64>()), 0, stream, a, nq); break;
+    case 128: hipLaunchKernelGGL(attend_split_kernel<128>, grid, dim3(64 * waves_of<128>()), 0, stream, a, nq); break;
+    case 256: hipLaunchKernelGGL(attend_split_kernel<256>, grid, dim3(64 * waves_of<256>()), 0, stream, a, nq); break;
+    case 512: hipLaunchKernelGGL(attend_split_kernel<512>, grid, dim3(64 * waves_of<512>()), 0, stream, a, nq); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

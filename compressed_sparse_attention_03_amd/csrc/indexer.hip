@@ -8,12 +8,12 @@
 //
 // score[i] = sum_h w[h] * max(0, <q~_h, k~_i>)  (the form stated in csa.h).
 //
-// Kernel 1 (index_score): grid (tiles, queries), 4 waves.  The query's 64x128 head matrix is
-// quantised once per workgroup into LDS and held as MFMA A-operands; key tiles stream from HBM
-// in groups of 16 entries, each group costing one v_mfma_scale_f32_16x16x128_f8f6f4 per 16 heads
-// (fp8 e4m3, or MXFP4 with its e8m0 block scales applied by the instruction).  The tile's scores
-// stay in LDS; a block radix select keeps the tile's `cand` best (score, index) keys, written in
-// ascending index order together with the smallest kept key.
+// Kernel 1 (index_score): grid (tiles, queries).  The query's [H_I x 128] head matrix is quantised
+// once per workgroup into LDS and held as MFMA A-operands; key tiles stream from HBM in groups of
+// 16 entries, each group costing one v_mfma_scale_f32_16x16x128_f8f6f4 per 16 heads (fp8 e4m3,
+// or MXFP4 with its e8m0 block scales applied by the instruction).  The tile's scores stay in LDS;
+// a block radix select keeps the tile's `cand` best (score, index) keys, written in ascending
+// index order together with the smallest kept key.
 // Kernel 2 (index_merge): one workgroup per query selects the k best keys among all candidates.
 // A tile whose smallest kept key beats the k-th best may hide further winners; such tiles are
 // re-scored in the merge workgroup (exact, slow, rare).
@@ -30,14 +30,18 @@ constexpr int kMaxCand = 8192;        // candidates per query seen by the merge 
 constexpr int kMergeThreads = 512;
 constexpr int kMaxTile = 2048;
 constexpr int kMaxK = 2048;
+// groups of 16 entries per wave per load batch: 4 KB of keys in flight per wave and batch
+template <int FMT>
+constexpr int batch_of() { return FMT == 1 ? 2 : 4; }
 
-struct QueryLds {                     // quantised query of one indexer query token
+struct alignas(16) QueryLds {         // quantised query of one indexer query token
   uint8_t codes[64 * 128];            // fp8: [head][128]; MXFP4: [head][64] packed
   uint8_t sbytes[64 * 4];             // MXFP4 block scales [head][4]
-  float f[64];                        // per-head factor: w_h * fp8 scale (w_h for MXFP4)
+  float f[64];                        // per-head factor: w_h * fp8 scale (w_h for MXFP4); 0 if absent
 };
 
-// Quantise one query's [H_I x 128] bf16 heads into LDS.  Threads 0 .. 4*H_I-1 each own 32 values.
+// Quantise one query's [H_I x 128] bf16 heads into LDS.  Thread t < 256 owns head t/4, values
+// 32*(t%4) .. +31; heads >= H_I are written as zeros (factor 0) so 4 head blocks are always valid.
 template <int FMT>
 __device__ void prep_query_lds(const uint16_t *q, const float *w, int H_I, QueryLds &ql) {
   const int t = threadIdx.x;
@@ -64,38 +68,34 @@ __device__ void prep_query_lds(const uint16_t *q, const float *w, int H_I, Query
       amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
       const int e = e4m3_row_exp(amax);
       const float inv = ldexpf(1.0f, -e);
-      if (act) {
-        uint32_t outw[8];
+      uint32_t outw[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          uint32_t b0 = f32_to_e4m3(bf16lo(wv[2 * k]) * inv), b1 = f32_to_e4m3(bf16hi(wv[2 * k]) * inv);
-          uint32_t b2 = f32_to_e4m3(bf16lo(wv[2 * k + 1]) * inv), b3 = f32_to_e4m3(bf16hi(wv[2 * k + 1]) * inv);
-          outw[k] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-        }
-        uint4 *dst = reinterpret_cast<uint4 *>(ql.codes + h * 128 + c * 32);
-        dst[0] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
-        dst[1] = make_uint4(outw[4], outw[5], outw[6], outw[7]);
-        if (c == 0) ql.f[h] = w[h] * ldexpf(1.0f, e);
+      for (int k = 0; k < 8; ++k) {
+        uint32_t b0 = f32_to_e4m3(bf16lo(wv[2 * k]) * inv), b1 = f32_to_e4m3(bf16hi(wv[2 * k]) * inv);
+        uint32_t b2 = f32_to_e4m3(bf16lo(wv[2 * k + 1]) * inv), b3 = f32_to_e4m3(bf16hi(wv[2 * k + 1]) * inv);
+        outw[k] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
       }
+      uint4 *dst = reinterpret_cast<uint4 *>(ql.codes + h * 128 + c * 32);
+      dst[0] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+      dst[1] = make_uint4(outw[4], outw[5], outw[6], outw[7]);
+      if (c == 0) ql.f[h] = act ? w[h] * ldexpf(1.0f, e) : 0.f;
     } else {
       const uint32_t sb = mx_scale_byte(amax);
       const float inv = ldexpf(1.0f, 127 - int(sb));
-      if (act) {
-        uint32_t outw[4];
+      uint32_t outw[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          uint32_t p = 0;
+      for (int k = 0; k < 4; ++k) {
+        uint32_t p = 0;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            uint32_t lo = f32_to_e2m1(bf16lo(wv[4 * k + j]) * inv), hi = f32_to_e2m1(bf16hi(wv[4 * k + j]) * inv);
-            p |= (lo | (hi << 4)) << (8 * j);
-          }
-          outw[k] = p;
+        for (int j = 0; j < 4; ++j) {
+          uint32_t lo = f32_to_e2m1(bf16lo(wv[4 * k + j]) * inv), hi = f32_to_e2m1(bf16hi(wv[4 * k + j]) * inv);
+          p |= (lo | (hi << 4)) << (8 * j);
         }
-        *reinterpret_cast<uint4 *>(ql.codes + h * 64 + c * 16) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
-        ql.sbytes[h * 4 + c] = uint8_t(sb);
-        if (c == 0) ql.f[h] = w[h];
+        outw[k] = p;
       }
+      *reinterpret_cast<uint4 *>(ql.codes + h * 64 + c * 16) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+      ql.sbytes[h * 4 + c] = uint8_t(sb);
+      if (c == 0) ql.f[h] = act ? w[h] : 0.f;
     }
   }
 }
@@ -129,88 +129,125 @@ __device__ __forceinline__ void load_query_frag(const QueryLds &ql, int lane, Qu
   }
 }
 
-// Key operand of one lane for the group of 16 entries starting at e0: entry e0 + (lane & 15),
-// K-chunk (lane >> 4).  Rows past the allocation are clamped (their scores are discarded).
+// Key operand of one lane for a group of 16 entries: entry (lane & 15), K-chunk (lane >> 4).
+// Held exactly as loaded (no arithmetic on the loaded values until they are used, so issuing a
+// batch never waits for it).
 template <int FMT>
 struct KeyFrag {
-  v8i b;
-  int sb;
-  float ks;
+  uint4 c0, c1;     // codes (c1 unused for MXFP4)
+  uint32_t s;       // fp8: the row scale's bits; MXFP4: the row's four e8m0 scale bytes
+};
+
+// The key rows of one tile, read through buffer resources.  The whole byte offset goes in the
+// per-lane offset operand, which the hardware range check always covers: rows past the tile's last
+// valid row, and whole groups past the tile, read as zeros without touching memory (their scores are
+// discarded), so loads are issued unconditionally and nothing is clamped.
+constexpr int kRawBufferWord3 = 0x00020000;   // gfx9 raw-buffer descriptor word 3 (32-bit data format)
+
+template <int FMT>
+struct TileKeys {
+  __amdgpu_buffer_rsrc_t codes, scales;
+  uint32_t code_off, scale_off;   // this lane's byte offsets inside a group
 };
 
 template <int FMT>
-__device__ __forceinline__ void load_key_frag(const uint8_t *codes, const void *scales, int64_t row,
-                                              int lane, KeyFrag<FMT> &kf) {
-  const int g = lane >> 4;
-  if (FMT == 1) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(codes + row * 128 + g * 32);
-    uint4 x0 = p[0], x1 = p[1];
-    kf.b = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
-    kf.sb = 127;
-    kf.ks = static_cast<const float *>(scales)[row];
-  } else {
-    uint4 x0 = *reinterpret_cast<const uint4 *>(codes + row * 64 + g * 16);
-    kf.b = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), 0, 0, 0, 0};
-    uint32_t s4 = static_cast<const uint32_t *>(scales)[row];
-    kf.sb = int((s4 >> (8 * g)) & 0xff);
-    kf.ks = 1.0f;
-  }
+__device__ __forceinline__ TileKeys<FMT> make_tile_keys(const void *codes, const void *scales, int64_t row0,
+                                                        int rows, int lane) {
+  constexpr int RB = FMT == 1 ? 128 : 64;     // code bytes per row
+  TileKeys<FMT> tk;
+  tk.codes = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(static_cast<const uint8_t *>(codes) + row0 * RB), short(0), rows * RB, kRawBufferWord3);
+  tk.scales = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(static_cast<const uint8_t *>(scales) + row0 * 4), short(0), rows * 4, kRawBufferWord3);
+  tk.code_off = uint32_t((lane & 15) * RB + (lane >> 4) * (FMT == 1 ? 32 : 16));
+  tk.scale_off = uint32_t((lane & 15) * 4);
+  return tk;
 }
 
-// Score of entry (e0 + lane%16) for every lane (the 4 lanes of one entry agree).
+template <int FMT>
+__device__ __forceinline__ void load_key_frag(const TileKeys<FMT> &tk, int grp, int lane, KeyFrag<FMT> &kf) {
+  constexpr int RB = FMT == 1 ? 128 : 64;
+  const uint32_t goff = uint32_t(grp) * (16 * RB);
+  kf.c0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(tk.codes, tk.code_off + goff, 0, 0));
+  if (FMT == 1)
+    kf.c1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(tk.codes, tk.code_off + goff + 16, 0, 0));
+  kf.s = __builtin_amdgcn_raw_buffer_load_b32(tk.scales, tk.scale_off + uint32_t(grp) * 64, 0, 0);
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_batch(const TileKeys<FMT> &tk, int g0, int lane, KeyFrag<FMT> (&kf)[batch_of<FMT>()]) {
+#pragma unroll
+  for (int u = 0; u < batch_of<FMT>(); ++u) load_key_frag<FMT>(tk, g0 + u, lane, kf[u]);
+}
+
+// max(x, 0) for a float: non-negative floats order like their bit patterns as signed integers, and
+// every negative float (and -0) is a negative integer.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Scores of one batch of groups: every MFMA first, then the per-head ReLU/weight epilogues, so the
+// epilogues do not wait on MFMA latency.  Each entry's score is reduced across its 4 lanes and
+// written to s_scores by lanes 0..15; entries at tile-local index >= vis get -inf.
 template <int FMT, int NHB>
-__device__ __forceinline__ float score_group(const QueryFrag<NHB> &qf, const KeyFrag<FMT> &kf) {
+__device__ __forceinline__ void score_batch(const QueryFrag<NHB> &qf, const KeyFrag<FMT> (&kf)[batch_of<FMT>()], int g0,
+                                            int ngroups, int vis, int lane, float *s_scores) {
   constexpr int fmt = FMT == 1 ? 0 : 4;   // instruction format code: 0 = fp8 e4m3, 4 = fp4 e2m1
-  float acc = 0.f;
+  v4f c[batch_of<FMT>()][NHB];
 #pragma unroll
-  for (int hb = 0; hb < NHB; ++hb) {
-    v4f c = {0.f, 0.f, 0.f, 0.f};
-    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf.a[hb], kf.b, c, fmt, fmt, 0, qf.sa[hb], 0, kf.sb);
+  for (int u = 0; u < batch_of<FMT>(); ++u) {
+    const uint4 x0 = kf[u].c0, x1 = FMT == 1 ? kf[u].c1 : make_uint4(0, 0, 0, 0);
+    const v8i bop = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+    const int sb = FMT == 1 ? 127 : int((kf[u].s >> (8 * (lane >> 4))) & 0xff);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc += qf.f[hb][v] * fmaxf(c[v], 0.f);
+    for (int hb = 0; hb < NHB; ++hb)
+      c[u][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf.a[hb], bop, v4f{0.f, 0.f, 0.f, 0.f}, fmt,
+                                                                  fmt, 0, qf.sa[hb], 0, sb);
   }
-  acc += __shfl_xor(acc, 16, 64);
-  acc += __shfl_xor(acc, 32, 64);
-  return acc * kf.ks;
+#pragma unroll
+  for (int u = 0; u < batch_of<FMT>(); ++u) {
+    float acc = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc = fmaf(qf.f[hb][v], relu(c[u][hb][v]), acc);
+    acc += __shfl_xor(acc, 16, 64);
+    acc += __shfl_xor(acc, 32, 64);
+    const int el = (g0 + u) * 16 + (lane & 15);
+    const float ks = FMT == 1 ? __uint_as_float(kf[u].s) : 1.0f;
+    if (lane < 16 && g0 + u < ngroups) s_scores[el] = el < vis ? acc * ks : -INFINITY;
+  }
 }
 
-// Score `tile` entries starting at entry e_begin into s_scores (LDS) -- quantised formats.
-// Invisible entries (>= n_vis) are written as -inf.  Work is split over all waves of the block.
+// Score the `tile` entries of a tile into s_scores (LDS); entries at tile-local index >= vis are
+// written as -inf.  The block's waves split the groups; each wave alternates two load batches so the
+// next batch is in flight while the current one is scored.  `ka` holds the wave's first batch,
+// issued by the caller.
 template <int FMT, int NHB>
-__device__ void score_tile_mfma(const QueryFrag<NHB> &qf, const uint8_t *codes, const void *scales,
-                                int64_t row_base, int64_t N_cap, int64_t e_begin, int tile,
-                                int64_t n_vis, float *s_scores) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+__device__ void score_tile_mfma(const QueryFrag<NHB> &qf, KeyFrag<FMT> (&ka)[batch_of<FMT>()], const TileKeys<FMT> &tk,
+                                int tile, int vis, float *s_scores) {
+  // the wave index is uniform: say so, so group offsets stay scalar (no per-lane loop over them)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
   const int ngroups = tile >> 4;
-  constexpr int U = 4;
-  for (int g0 = wave * U; g0 < ngroups; g0 += nwaves * U) {
-    KeyFrag<FMT> kf[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int64_t e = e_begin + int64_t(g0 + u) * 16 + (lane & 15);
-      int64_t row = e < N_cap ? e : N_cap - 1;
-      load_key_frag<FMT>(codes, scales, row_base + row, lane, kf[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (g0 + u < ngroups) {
-        float s = score_group<FMT, NHB>(qf, kf[u]);
-        int64_t e = e_begin + int64_t(g0 + u) * 16 + (lane & 15);
-        if (lane < 16) s_scores[(g0 + u) * 16 + lane] = e < n_vis ? s : -INFINITY;
-      }
-    }
+  const int stride = nwaves * batch_of<FMT>();
+  KeyFrag<FMT> kb[batch_of<FMT>()];
+  for (int g0 = wave * batch_of<FMT>(); g0 < ngroups; g0 += 2 * stride) {
+    const int g1 = g0 + stride;
+    // unconditional loads keep the count of loads in flight the same on every path, so each wait
+    // covers only the batch about to be scored
+    load_batch<FMT>(tk, g1, lane, kb);
+    score_batch<FMT, NHB>(qf, ka, g0, ngroups, vis, lane, s_scores);
+    load_batch<FMT>(tk, g1 + stride, lane, ka);
+    if (g1 < ngroups) score_batch<FMT, NHB>(qf, kb, g1, ngroups, vis, lane, s_scores);
   }
 }
 
 // fp32 keys: one thread per entry, query heads from LDS.
 __device__ void score_tile_f32(const float *q_lds, const float *w, int H_I, int D_I, const float *keys,
-                               int64_t row_base, int64_t e_begin, int tile, int64_t n_vis,
-                               float *s_scores) {
+                               int64_t row0, int tile, int vis, float *s_scores) {
   for (int i = threadIdx.x; i < tile; i += blockDim.x) {
-    const int64_t e = e_begin + i;
     float s = -INFINITY;
-    if (e < n_vis) {
-      const float4 *kr = reinterpret_cast<const float4 *>(keys + (row_base + e) * D_I);
+    if (i < vis) {
+      const float4 *kr = reinterpret_cast<const float4 *>(keys + (row0 + i) * D_I);
       s = 0.f;
       for (int h = 0; h < H_I; ++h) {
         const float4 *qh = reinterpret_cast<const float4 *>(q_lds + h * D_I);
@@ -260,77 +297,105 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
   uint32_t lo = __shfl_xor(uint32_t(v), o, 64), hi = __shfl_xor(uint32_t(v >> 32), o, 64);
   return (uint64_t(hi) << 32) | lo;
 }
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+struct alignas(16) SelectLds {
+  uint32_t hist[3][256];
+  uint64_t u64[16];
+};
 
 // Rank-`need` (1 = largest) key among the non-zero keys held by the block (KPT per thread).
 // Keys are distinct.  The caller guarantees 1 <= need <= number of non-zero keys.
+// MSB-first radix select that starts at the highest bit where the keys differ (the bits above it
+// are shared by every key, so histogramming them would pile every key into one bin), resolves up
+// to 8 bits per pass and stops as soon as the answer's bucket is exactly filled.  Every wave scans
+// the histogram itself and the histograms rotate over three buffers (pass p zeroes the buffer of
+// pass p+2, whose last readers finished before pass p's barrier), so a pass costs one barrier.
 template <int NT, int KPT>
-__device__ uint64_t block_select(const uint64_t (&keys)[KPT], int need, uint32_t *s_hist,
-                                 uint64_t *s_u64, int *s_sel) {
+__device__ uint64_t block_select(const uint64_t (&keys)[KPT], int need, SelectLds &sl) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint64_t prefix = 0, mask = 0;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += NT) s_hist[i] = 0;
-    __syncthreads();
+  for (int i = tid; i < 768; i += NT) (&sl.hist[0][0])[i] = 0;
+  uint64_t mn = ~uint64_t(0), mx = 0;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k)
+    if (keys[k] != 0) { mn = umin64(mn, keys[k]); mx = umax64(mx, keys[k]); }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = umin64(mn, shfl_xor_u64(mn, o));
+    mx = umax64(mx, shfl_xor_u64(mx, o));
+  }
+  if (lane == 0) { sl.u64[wave] = mn; sl.u64[8 + wave] = mx; }
+  __syncthreads();
+  mn = ~uint64_t(0); mx = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) { mn = umin64(mn, sl.u64[w]); mx = umax64(mx, sl.u64[8 + w]); }
+  if (mn == mx) { __syncthreads(); return mn; }
+  int hi = 63 - __clzll(mn ^ mx);                 // highest bit where keys differ
+  uint64_t mask = hi == 63 ? 0 : ~((uint64_t(2) << hi) - 1);
+  uint64_t prefix = mn & mask;
+  for (int pass = 0;; ++pass) {
+    uint32_t *H = sl.hist[pass % 3];
+    const int width = hi + 1 < 8 ? hi + 1 : 8;
+    const int shift = hi - width + 1;
+    const uint64_t dmask = (uint64_t(1) << width) - 1;
 #pragma unroll
     for (int k = 0; k < KPT; ++k)
-      if (keys[k] != 0 && (keys[k] & mask) == prefix) atomicAdd(&s_hist[(keys[k] >> shift) & 255u], 1u);
+      if (keys[k] != 0 && (keys[k] & mask) == prefix) atomicAdd(&H[(keys[k] >> shift) & dmask], 1u);
     __syncthreads();
-    if (wave == 0) {
-      int c[4], sum = 0;
+    // every wave finds the digit holding rank `need`, scanning bins from the top
+    const uint4 c4 = *reinterpret_cast<const uint4 *>(&H[252 - 4 * lane]);
+    const int c[4] = {int(c4.w), int(c4.z), int(c4.y), int(c4.x)};   // bins 255-4l .. 252-4l
+    const int sum = c[0] + c[1] + c[2] + c[3];
+    int cum = wave_incl_scan(sum, lane) - sum;
+    int hit = 0, d_sel = 0, above = 0, bucket = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { c[j] = int(s_hist[255 - 4 * lane - j]); sum += c[j]; }
-      int cum = wave_incl_scan(sum, lane) - sum;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (cum < need && need <= cum + c[j]) {
-          s_sel[0] = 255 - 4 * lane - j;
-          s_sel[1] = cum;
-          s_sel[2] = c[j];
-        }
-        cum += c[j];
-      }
+    for (int j = 0; j < 4; ++j) {
+      if (!hit && cum < need && need <= cum + c[j]) { hit = 1; d_sel = 255 - 4 * lane - j; above = cum; bucket = c[j]; }
+      cum += c[j];
     }
-    __syncthreads();
-    const uint64_t digit = uint64_t(s_sel[0]);
-    need -= s_sel[1];
-    const int bucket = s_sel[2];
-    prefix |= digit << shift;
-    mask |= uint64_t(255) << shift;
-    __syncthreads();
-    if (bucket == need) {
+    const uint64_t bal = __ballot(hit);
+    const int src = __ffsll((unsigned long long)bal) - 1;
+    d_sel = __shfl(d_sel, src, 64);
+    above = __shfl(above, src, 64);
+    bucket = __shfl(bucket, src, 64);
+    // pass p-1's buffer (= pass p+2's) was last read before this pass's barrier: clear it
+    uint32_t *Hn = sl.hist[(pass + 2) % 3];
+    for (int i = tid; i < 256; i += NT) Hn[i] = 0;
+    need -= above;
+    prefix |= uint64_t(d_sel) << shift;
+    mask |= dmask << shift;
+    if (bucket == need || shift == 0) {
       // every key of this bucket is in; the answer is the smallest of them
-      uint64_t mn = ~uint64_t(0);
+      uint64_t m2 = ~uint64_t(0);
 #pragma unroll
       for (int k = 0; k < KPT; ++k)
-        if (keys[k] != 0 && (keys[k] & mask) == prefix && keys[k] < mn) mn = keys[k];
+        if (keys[k] != 0 && (keys[k] & mask) == prefix) m2 = umin64(m2, keys[k]);
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        uint64_t t = shfl_xor_u64(mn, o);
-        mn = t < mn ? t : mn;
-      }
-      if (lane == 0) s_u64[wave] = mn;
+      for (int o = 32; o > 0; o >>= 1) m2 = umin64(m2, shfl_xor_u64(m2, o));
+      if (lane == 0) sl.u64[wave] = m2;
       __syncthreads();
-      uint64_t r = ~uint64_t(0);
-      for (int w = 0; w < NT / 64; ++w) r = s_u64[w] < r ? s_u64[w] : r;
+      uint64_t res = ~uint64_t(0);
+#pragma unroll
+      for (int w = 0; w < NW; ++w) res = umin64(res, sl.u64[w]);
       __syncthreads();
-      return r;
+      return res;
     }
+    hi = shift - 1;
   }
-  return prefix;
 }
 
 // ---- kernel 1: scores and per-tile candidates ------------------------------------------------
-struct ScoreShared {
+struct alignas(16) ScoreShared {
   QueryLds ql;
   float scores[kMaxTile];
-  uint32_t hist[256];
-  uint64_t u64[16];
-  int sel[4];
+  SelectLds sel;
   int tmp[16];
 };
 
-template <int FMT, int NHB, int KPT>
-__global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
+template <int FMT, int NHB, int NT, int KPT>
+__global__ void __launch_bounds__(NT) index_score_kernel(IndexArgs a) {
   __shared__ ScoreShared sh;
   const int tile_id = blockIdx.x;
   const int64_t qi = blockIdx.y;                               // query = b * Sq + s
@@ -339,37 +404,43 @@ __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
   const int64_t e_begin = int64_t(tile_id) * tile;
   const int64_t t = a.q_pos0[b] + s;
   const int64_t n_vis = min(a.n_entries[b], (t + 1) / a.m);
+  const int vis = int(max(int64_t(0), min(int64_t(tile), n_vis - e_begin)));
   const int64_t out_slot = qi * a.plan.n_tiles + tile_id;
+  const int64_t n_q = int64_t(a.B) * a.Sq;
   uint64_t *cand_keys = static_cast<uint64_t *>(a.workspace);
-  uint64_t *cand_bound = cand_keys + int64_t(gridDim.y) * a.plan.n_tiles * cand;
-  int *cand_count = reinterpret_cast<int *>(cand_bound + int64_t(gridDim.y) * a.plan.n_tiles);
+  uint64_t *cand_bound = cand_keys + n_q * a.plan.n_tiles * cand;
+  int *cand_count = reinterpret_cast<int *>(cand_bound + n_q * a.plan.n_tiles);
 
-  if (e_begin >= n_vis && a.scores == nullptr) {              // nothing visible in this tile
+  if (vis == 0 && a.scores == nullptr) {                      // nothing visible in this tile
     if (threadIdx.x == 0) { cand_count[out_slot] = 0; cand_bound[out_slot] = 0; }
     return;
   }
-  const int64_t row_base = int64_t(b) * a.N_cap;
+  const int64_t row0 = int64_t(b) * a.N_cap + e_begin;
   if (FMT == 0) {
     float *q_lds = reinterpret_cast<float *>(sh.ql.codes);    // H_I * D_I <= 2048 floats
     const float *qsrc = static_cast<const float *>(a.q_idx) + qi * a.H_I * a.D_I;
-    for (int i = threadIdx.x; i < a.H_I * a.D_I; i += blockDim.x) q_lds[i] = qsrc[i];
+    for (int i = threadIdx.x; i < a.H_I * a.D_I; i += NT) q_lds[i] = qsrc[i];
     if (threadIdx.x < a.H_I) sh.ql.f[threadIdx.x] = a.w_idx[qi * a.H_I + threadIdx.x];
     __syncthreads();
-    score_tile_f32(q_lds, sh.ql.f, a.H_I, a.D_I, static_cast<const float *>(a.k_codes), row_base,
-                   e_begin, tile, n_vis, sh.scores);
+    score_tile_f32(q_lds, sh.ql.f, a.H_I, a.D_I, static_cast<const float *>(a.k_codes), row0, tile, vis,
+                   sh.scores);
   } else {
+    const int rows = int(min(int64_t(tile), a.N_cap - e_begin));
+    const TileKeys<FMT> tk = make_tile_keys<FMT>(a.k_codes, a.k_scales, row0, rows, threadIdx.x & 63);
+    KeyFrag<FMT> kf[batch_of<FMT>()];
+    const int g_first = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * batch_of<FMT>();
+    load_batch<FMT>(tk, g_first, threadIdx.x & 63, kf);   // stream before prep
     prep_query_lds<FMT>(static_cast<const uint16_t *>(a.q_idx) + qi * a.H_I * 128, a.w_idx + qi * a.H_I,
                         a.H_I, sh.ql);
     __syncthreads();
     QueryFrag<NHB> qf;
     load_query_frag<FMT, NHB>(sh.ql, threadIdx.x & 63, qf);
-    score_tile_mfma<FMT, NHB>(qf, static_cast<const uint8_t *>(a.k_codes), a.k_scales, row_base, a.N_cap,
-                              e_begin, tile, n_vis, sh.scores);
+    score_tile_mfma<FMT, NHB>(qf, kf, tk, tile, vis, sh.scores);
   }
   __syncthreads();
   if (a.scores) {
     float *dst = a.scores + qi * a.N_cap;
-    for (int i = threadIdx.x; i < tile; i += blockDim.x)
+    for (int i = threadIdx.x; i < tile; i += NT)
       if (e_begin + i < a.N_cap) dst[e_begin + i] = sh.scores[i];
   }
   // keys of this thread's KPT consecutive entries
@@ -378,42 +449,38 @@ __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
     const int i = threadIdx.x * KPT + k;
-    const int64_t e = e_begin + i;
-    const bool ok = i < tile && e < n_vis;
-    keys[k] = ok ? make_key(sh.scores[i], uint32_t(e)) : 0;
+    const bool ok = i < vis;
+    keys[k] = ok ? make_key(sh.scores[i], uint32_t(e_begin + i)) : 0;
     nvalid_local += ok;
   }
-  int nvalid;
-  (void)block_excl_scan<256>(nvalid_local, sh.tmp, nvalid);
   uint64_t bound = 0;
-  if (nvalid > cand) bound = block_select<256, KPT>(keys, cand, sh.hist, sh.u64, sh.sel);
+  if (vis > cand) bound = block_select<NT, KPT>(keys, cand, sh.sel);
   int mine = 0;
 #pragma unroll
   for (int k = 0; k < KPT; ++k) mine += (keys[k] != 0 && keys[k] >= bound);
   int total;
-  int pos = block_excl_scan<256>(mine, sh.tmp, total);
+  int pos = block_excl_scan<NT>(mine, sh.tmp, total);
   uint64_t *dst = cand_keys + out_slot * cand;
 #pragma unroll
   for (int k = 0; k < KPT; ++k)
     if (keys[k] != 0 && keys[k] >= bound) dst[pos++] = keys[k];
   if (threadIdx.x == 0) { cand_count[out_slot] = total; cand_bound[out_slot] = bound; }
+  (void)nvalid_local;
 }
 
 // ---- kernel 2: merge ----------------------------------------------------------------------
-struct MergeShared {
+struct alignas(16) MergeShared {
   QueryLds ql;
   float scores[kMaxTile];
   uint64_t work[kMaxK + kMaxTile];
   int counts[kMaxCand / 8];
   uint64_t bounds[kMaxCand / 8];
-  uint32_t hist[256];
-  uint64_t u64[16];
-  int sel[4];
+  SelectLds sel;
   int tmp[16];
   int flag;
 };
 
-// Sort `n` (<= kMaxK, padded to a power of two P) entry indices ascending, in LDS (as keys).
+// Sort P (a power of two) entry indices ascending in LDS.
 __device__ void bitonic_sort_u32(uint32_t *v, int P) {
   for (int k = 2; k <= P; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
@@ -430,124 +497,73 @@ __device__ void bitonic_sort_u32(uint32_t *v, int P) {
   }
 }
 
-template <int FMT, int NHB>
-__global__ void __launch_bounds__(kMergeThreads) index_merge_kernel(IndexArgs a) {
-  __shared__ MergeShared sh;
-  constexpr int KPT = kMaxCand / kMergeThreads;
+// Exact fallback: the candidate set may miss winners hidden in tiles whose kept keys all beat
+// `tau`.  Keep a working set W (the k_eff best so far) in LDS and merge in every such tile,
+// re-scored from its keys.  Writes the final selection in ascending index order.
+template <int FMT, int KPT>
+__device__ void merge_fallback(const IndexArgs &a, MergeShared &sh, const uint64_t (&keys)[KPT], uint64_t tau,
+                               int64_t qi, int b, int64_t n_vis, int k_eff, int32_t *out) {
+  constexpr int NT = kMergeThreads;
   const int tid = threadIdx.x;
-  const int64_t qi = blockIdx.x;
-  const int b = int(qi / a.Sq), s = int(qi % a.Sq);
-  const int tile = a.plan.tile, cand = a.plan.cand, n_tiles = a.plan.n_tiles;
-  const int64_t t = a.q_pos0[b] + s;
-  const int64_t n_vis = min(a.n_entries[b], (t + 1) / a.m);
-  const int k_eff = int(min(int64_t(a.topk), n_vis));
-  const uint64_t *cand_keys = static_cast<const uint64_t *>(a.workspace);
-  const uint64_t *cand_bound = cand_keys + int64_t(gridDim.x) * n_tiles * cand;
-  const int *cand_count = reinterpret_cast<const int *>(cand_bound + int64_t(gridDim.x) * n_tiles);
-  int32_t *out = a.topk_idx + qi * a.topk;
-
-  for (int i = tid; i < n_tiles; i += kMergeThreads) {
-    sh.counts[i] = cand_count[qi * n_tiles + i];
-    sh.bounds[i] = cand_bound[qi * n_tiles + i];
-  }
-  __syncthreads();
-  uint64_t keys[KPT];
-  int nvalid_local = 0;
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const int slot = tid * KPT + k;
-    const int tl = slot / cand, j = slot - tl * cand;
-    uint64_t key = 0;
-    if (tl < n_tiles && j < sh.counts[tl]) key = cand_keys[(qi * n_tiles + tl) * cand + j];
-    keys[k] = key;
-    nvalid_local += key != 0;
-  }
-  int nvalid;
-  (void)block_excl_scan<kMergeThreads>(nvalid_local, sh.tmp, nvalid);
-  if (k_eff == 0) {
-    for (int i = tid; i < a.topk; i += kMergeThreads) out[i] = -1;
-    return;
-  }
-  uint64_t tau = 0;                                            // k-th best candidate (0: need all)
-  if (nvalid >= k_eff) tau = block_select<kMergeThreads, KPT>(keys, k_eff, sh.hist, sh.u64, sh.sel);
-  // a truncated tile whose smallest kept key beats tau may hold further winners
-  if (tid == 0) sh.flag = 0;
-  __syncthreads();
-  for (int i = tid; i < n_tiles; i += kMergeThreads)
-    if (sh.bounds[i] != 0 && sh.bounds[i] > tau) sh.flag = 1;
-  __syncthreads();
-  if (!sh.flag) {
-    int mine = 0;
-#pragma unroll
-    for (int k = 0; k < KPT; ++k) mine += (keys[k] != 0 && keys[k] >= tau);
-    int total;
-    int pos = block_excl_scan<kMergeThreads>(mine, sh.tmp, total);
-#pragma unroll
-    for (int k = 0; k < KPT; ++k)
-      if (keys[k] != 0 && keys[k] >= tau) out[pos++] = int32_t(key_index(keys[k]));
-    for (int i = k_eff + tid; i < a.topk; i += kMergeThreads) out[i] = -1;
-    return;
-  }
-
-  // ---- exact fallback: working set W (<= k_eff keys) in LDS, re-score each suspicious tile ----
+  const int tile = a.plan.tile, n_tiles = a.plan.n_tiles;
   int wn;
   {
     int mine = 0;
 #pragma unroll
     for (int k = 0; k < KPT; ++k) mine += (keys[k] != 0 && keys[k] >= tau);
-    int pos = block_excl_scan<kMergeThreads>(mine, sh.tmp, wn);
+    int pos = block_excl_scan<NT>(mine, sh.tmp, wn);
 #pragma unroll
     for (int k = 0; k < KPT; ++k)
       if (keys[k] != 0 && keys[k] >= tau) sh.work[pos++] = keys[k];
   }
   __syncthreads();
-  QueryFrag<NHB> qf;
+  QueryFrag<4> qf;
   float *q_lds = reinterpret_cast<float *>(sh.ql.codes);
   if (FMT == 0) {
     const float *qsrc = static_cast<const float *>(a.q_idx) + qi * a.H_I * a.D_I;
-    for (int i = tid; i < a.H_I * a.D_I; i += kMergeThreads) q_lds[i] = qsrc[i];
+    for (int i = tid; i < a.H_I * a.D_I; i += NT) q_lds[i] = qsrc[i];
     if (tid < a.H_I) sh.ql.f[tid] = a.w_idx[qi * a.H_I + tid];
     __syncthreads();
   } else {
     prep_query_lds<FMT>(static_cast<const uint16_t *>(a.q_idx) + qi * a.H_I * 128, a.w_idx + qi * a.H_I,
                         a.H_I, sh.ql);
     __syncthreads();
-    load_query_frag<FMT, NHB>(sh.ql, tid & 63, qf);
+    load_query_frag<FMT, 4>(sh.ql, tid & 63, qf);
   }
-  const int64_t row_base = int64_t(b) * a.N_cap;
-  constexpr int KW = (kMaxK + kMaxTile) / kMergeThreads;
+  constexpr int KW = (kMaxK + kMaxTile) / NT;
   for (int tl = 0; tl < n_tiles; ++tl) {
     const uint64_t bt = sh.bounds[tl];
     if (bt == 0 || bt <= tau) continue;                        // complete, or cannot hold winners
     const int64_t e_begin = int64_t(tl) * tile;
-    if (FMT == 0)
-      score_tile_f32(q_lds, sh.ql.f, a.H_I, a.D_I, static_cast<const float *>(a.k_codes), row_base,
-                     e_begin, tile, n_vis, sh.scores);
-    else
-      score_tile_mfma<FMT, NHB>(qf, static_cast<const uint8_t *>(a.k_codes), a.k_scales, row_base,
-                                a.N_cap, e_begin, tile, n_vis, sh.scores);
+    const int vis = int(max(int64_t(0), min(int64_t(tile), n_vis - e_begin)));
+    const int64_t row0 = int64_t(b) * a.N_cap + e_begin;
+    if (FMT == 0) {
+      score_tile_f32(q_lds, sh.ql.f, a.H_I, a.D_I, static_cast<const float *>(a.k_codes), row0, tile, vis,
+                     sh.scores);
+    } else {
+      const int rows = int(min(int64_t(tile), a.N_cap - e_begin));
+      const TileKeys<FMT> tk = make_tile_keys<FMT>(a.k_codes, a.k_scales, row0, rows, tid & 63);
+      KeyFrag<FMT> kf[batch_of<FMT>()];
+      const int g_first = __builtin_amdgcn_readfirstlane(tid >> 6) * batch_of<FMT>();
+      if (g_first < tile / 16) load_batch<FMT>(tk, g_first, tid & 63, kf);
+      score_tile_mfma<FMT, 4>(qf, kf, tk, tile, vis, sh.scores);
+    }
     __syncthreads();
     // append the tile's entries below its bound (the ones not already candidates) and above tau
     int mine = 0;
-    for (int i = tid; i < tile; i += kMergeThreads) {
-      const int64_t e = e_begin + i;
-      if (e < n_vis) {
-        uint64_t key = make_key(sh.scores[i], uint32_t(e));
-        mine += (key < bt && key > tau);
-      }
+    for (int i = tid; i < vis; i += NT) {
+      const uint64_t key = make_key(sh.scores[i], uint32_t(e_begin + i));
+      mine += (key < bt && key > tau);
     }
     int total;
-    int pos = block_excl_scan<kMergeThreads>(mine, sh.tmp, total) + wn;
-    for (int i = tid; i < tile; i += kMergeThreads) {
-      const int64_t e = e_begin + i;
-      if (e < n_vis) {
-        uint64_t key = make_key(sh.scores[i], uint32_t(e));
-        if (key < bt && key > tau) sh.work[pos++] = key;
-      }
+    int pos = block_excl_scan<NT>(mine, sh.tmp, total) + wn;
+    for (int i = tid; i < vis; i += NT) {
+      const uint64_t key = make_key(sh.scores[i], uint32_t(e_begin + i));
+      if (key < bt && key > tau) sh.work[pos++] = key;
     }
     wn += total;
     __syncthreads();
-    if (wn > k_eff) {                                           // shrink W back to the k_eff best
+    if (wn >= k_eff) {                                          // shrink W back to the k_eff best
       uint64_t wk[KW];
 #pragma unroll
       for (int k = 0; k < KW; ++k) {
@@ -555,27 +571,17 @@ __global__ void __launch_bounds__(kMergeThreads) index_merge_kernel(IndexArgs a)
         wk[k] = i < wn ? sh.work[i] : 0;
       }
       __syncthreads();
-      tau = block_select<kMergeThreads, KW>(wk, k_eff, sh.hist, sh.u64, sh.sel);
+      tau = block_select<NT, KW>(wk, k_eff, sh.sel);
       int m2 = 0;
 #pragma unroll
       for (int k = 0; k < KW; ++k) m2 += (wk[k] != 0 && wk[k] >= tau);
       int tot2;
-      int p2 = block_excl_scan<kMergeThreads>(m2, sh.tmp, tot2);
+      int p2 = block_excl_scan<NT>(m2, sh.tmp, tot2);
 #pragma unroll
       for (int k = 0; k < KW; ++k)
         if (wk[k] != 0 && wk[k] >= tau) sh.work[p2++] = wk[k];
       wn = tot2;
       __syncthreads();
-    } else if (wn == k_eff && tau == 0) {
-      // W just reached k_eff: its smallest key is the new threshold
-      uint64_t wk[KW];
-#pragma unroll
-      for (int k = 0; k < KW; ++k) {
-        const int i = tid * KW + k;
-        wk[k] = i < wn ? sh.work[i] : 0;
-      }
-      __syncthreads();
-      tau = block_select<kMergeThreads, KW>(wk, k_eff, sh.hist, sh.u64, sh.sel);
     }
   }
   // ascending indices
@@ -596,27 +602,103 @@ __global__ void __launch_bounds__(kMergeThreads) index_merge_kernel(IndexArgs a)
   }
   __syncthreads();
   bitonic_sort_u32(idx, P);
-  for (int i = tid; i < a.topk; i += kMergeThreads) out[i] = i < wn ? int32_t(idx[i]) : -1;
+  for (int i = tid; i < a.topk; i += NT) out[i] = i < wn ? int32_t(idx[i]) : -1;
+}
+
+template <int FMT, int KPT>
+__global__ void __launch_bounds__(kMergeThreads) index_merge_kernel(IndexArgs a) {
+  __shared__ MergeShared sh;
+  constexpr int NT = kMergeThreads;
+  const int tid = threadIdx.x;
+  const int64_t qi = blockIdx.x;
+  const int b = int(qi / a.Sq), s = int(qi % a.Sq);
+  const int cand = a.plan.cand, n_tiles = a.plan.n_tiles;
+  const int64_t t = a.q_pos0[b] + s;
+  const int64_t n_vis = min(a.n_entries[b], (t + 1) / a.m);
+  const int k_eff = int(min(int64_t(a.topk), n_vis));
+  const int64_t n_q = int64_t(a.B) * a.Sq;
+  const uint64_t *cand_keys = static_cast<const uint64_t *>(a.workspace);
+  const uint64_t *cand_bound = cand_keys + n_q * n_tiles * cand;
+  const int *cand_count = reinterpret_cast<const int *>(cand_bound + n_q * n_tiles);
+  int32_t *out = a.topk_idx + qi * a.topk;
+
+  // candidate slots and per-tile counts are loaded together; slots past a tile's count are masked
+  uint64_t keys[KPT];
+  const int slots = n_tiles * cand;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int slot = tid * KPT + k;
+    keys[k] = slot < slots ? cand_keys[qi * slots + slot] : 0;
+  }
+  for (int i = tid; i < n_tiles; i += NT) {
+    sh.counts[i] = cand_count[qi * n_tiles + i];
+    sh.bounds[i] = cand_bound[qi * n_tiles + i];
+  }
+  if (tid == 0) sh.flag = 0;
+  __syncthreads();
+  int nvalid_local = 0;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int slot = tid * KPT + k;
+    const int tl = slot / cand, j = slot - tl * cand;
+    if (slot >= slots || j >= sh.counts[tl]) keys[k] = 0;
+    nvalid_local += keys[k] != 0;
+  }
+  int nvalid;
+  (void)block_excl_scan<NT>(nvalid_local, sh.tmp, nvalid);
+  if (k_eff == 0) {
+    for (int i = tid; i < a.topk; i += NT) out[i] = -1;
+    return;
+  }
+  uint64_t tau = 0;                                            // k-th best candidate (0: need all)
+  if (nvalid >= k_eff) tau = block_select<NT, KPT>(keys, k_eff, sh.sel);
+  // a truncated tile whose smallest kept key beats tau may hold further winners
+  for (int i = tid; i < n_tiles; i += NT)
+    if (sh.bounds[i] != 0 && sh.bounds[i] > tau) sh.flag = 1;
+  __syncthreads();
+  if (sh.flag) {
+    merge_fallback<FMT, KPT>(a, sh, keys, tau, qi, b, n_vis, k_eff, out);
+    return;
+  }
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) mine += (keys[k] != 0 && keys[k] >= tau);
+  int total;
+  int pos = block_excl_scan<NT>(mine, sh.tmp, total);
+#pragma unroll
+  for (int k = 0; k < KPT; ++k)
+    if (keys[k] != 0 && keys[k] >= tau) out[pos++] = int32_t(key_index(keys[k]));
+  for (int i = k_eff + tid; i < a.topk; i += NT) out[i] = -1;
 }
 
 template <int FMT, int NHB>
 hipError_t launch_score_t(const IndexArgs &a, hipStream_t stream) {
   dim3 grid(unsigned(a.plan.n_tiles), unsigned(int64_t(a.B) * a.Sq));
-  switch (a.plan.tile / 256) {
-    case 0: hipLaunchKernelGGL((index_score_kernel<FMT, NHB, 1>), grid, dim3(256), 0, stream, a); break;
-    case 1: hipLaunchKernelGGL((index_score_kernel<FMT, NHB, 1>), grid, dim3(256), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((index_score_kernel<FMT, NHB, 2>), grid, dim3(256), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((index_score_kernel<FMT, NHB, 4>), grid, dim3(256), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((index_score_kernel<FMT, NHB, 8>), grid, dim3(256), 0, stream, a); break;
+  switch (a.plan.tile) {
+    case 64: case 128: case 256:
+      hipLaunchKernelGGL((index_score_kernel<FMT, NHB, 256, 1>), grid, dim3(256), 0, stream, a); break;
+    case 512: hipLaunchKernelGGL((index_score_kernel<FMT, NHB, 256, 2>), grid, dim3(256), 0, stream, a); break;
+    case 1024: hipLaunchKernelGGL((index_score_kernel<FMT, NHB, 512, 2>), grid, dim3(512), 0, stream, a); break;
+    case 2048: hipLaunchKernelGGL((index_score_kernel<FMT, NHB, 512, 4>), grid, dim3(512), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int FMT, int NHB>
+template <int FMT>
 hipError_t launch_merge_t(const IndexArgs &a, hipStream_t stream) {
   dim3 grid(unsigned(int64_t(a.B) * a.Sq));
-  hipLaunchKernelGGL((index_merge_kernel<FMT, NHB>), grid, dim3(kMergeThreads), 0, stream, a);
+  const int slots = a.plan.n_tiles * a.plan.cand;
+  if (slots <= 512)
+    hipLaunchKernelGGL((index_merge_kernel<FMT, 1>), grid, dim3(kMergeThreads), 0, stream, a);
+  else if (slots <= 1024)
+    hipLaunchKernelGGL((index_merge_kernel<FMT, 2>), grid, dim3(kMergeThreads), 0, stream, a);
+  else if (slots <= 2048)
+    hipLaunchKernelGGL((index_merge_kernel<FMT, 4>), grid, dim3(kMergeThreads), 0, stream, a);
+  else if (slots <= 4096)
+    hipLaunchKernelGGL((index_merge_kernel<FMT, 8>), grid, dim3(kMergeThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((index_merge_kernel<FMT, 16>), grid, dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -667,24 +749,9 @@ hipError_t launch_index_score(const IndexArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_index_merge(const IndexArgs &a, hipStream_t stream) {
-  const int nhb = a.H_I / 16;
-  if (a.format == 0) return launch_merge_t<0, 1>(a, stream);
-  if (a.format == 1) {
-    switch (nhb) {
-      case 1: return launch_merge_t<1, 1>(a, stream);
-      case 2: return launch_merge_t<1, 2>(a, stream);
-      case 3: return launch_merge_t<1, 3>(a, stream);
-      case 4: return launch_merge_t<1, 4>(a, stream);
-    }
-  } else {
-    switch (nhb) {
-      case 1: return launch_merge_t<2, 1>(a, stream);
-      case 2: return launch_merge_t<2, 2>(a, stream);
-      case 3: return launch_merge_t<2, 3>(a, stream);
-      case 4: return launch_merge_t<2, 4>(a, stream);
-    }
-  }
-  return hipErrorInvalidValue;
+  if (a.format == 0) return launch_merge_t<0>(a, stream);
+  if (a.format == 1) return launch_merge_t<1>(a, stream);
+  return launch_merge_t<2>(a, stream);
 }
 
 }  // namespace csa
