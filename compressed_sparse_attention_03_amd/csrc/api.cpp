@@ -71,19 +71,13 @@ hipEvent_t take_event() {
 }  // namespace
 
 namespace csa {
-void timing_begin(const char *name, hipStream_t stream) {
+TimingEvents timing_events(const char *name) {
   std::lock_guard<std::mutex> lk(g_tmu);
-  if (!g_timing) return;
+  if (!g_timing) return {};
   TimedLaunch t{name, take_event(), take_event()};
-  (void)hipEventRecord(t.start, stream);
+  if (!t.start || !t.stop) return {};
   g_pending.push_back(t);
-}
-void timing_end(const char *name, hipStream_t stream) {
-  std::lock_guard<std::mutex> lk(g_tmu);
-  if (!g_timing) return;
-  for (auto it = g_pending.rbegin(); it != g_pending.rend(); ++it) {
-    if (it->name == name) { (void)hipEventRecord(it->stop, stream); return; }
-  }
+  return {t.start, t.stop};
 }
 }  // namespace csa
 
@@ -155,9 +149,7 @@ csa_status csa_compress(const uint16_t *c, const uint16_t *z, const uint16_t *bi
   csa::CompressArgs a{c, z, bias, norm_w, entries, win_rows, B, d, m, overlap, rope_dim, halo,
                       n_new, pos0, std::log2(double(rope_base)), eps};
   hipStream_t st = static_cast<hipStream_t>(stream);
-  csa::timing_begin("compress", st);
   hipError_t e = csa::launch_compress(a, st);
-  csa::timing_end("compress", st);
   return launched(e, "compress launch");
 }
 
@@ -171,9 +163,7 @@ csa_status csa_quantize_keys(const uint16_t *x, int64_t rows, int dim, int forma
   REQUIRE_PTR(x); REQUIRE_PTR(codes); REQUIRE_PTR(scales);
   csa::QuantizeArgs a{x, codes, scales, rows, dim, format};
   hipStream_t st = static_cast<hipStream_t>(stream);
-  csa::timing_begin("quantize", st);
   hipError_t e = csa::launch_quantize(a, st);
-  csa::timing_end("quantize", st);
   return launched(e, "quantize launch");
 }
 
@@ -218,13 +208,9 @@ csa_status csa_index_topk(const void *q_idx, const float *w_idx, const void *k_c
   a.m = m; a.topk = topk; a.N_cap = N_cap;
   a.plan = csa::plan_index(int64_t(B) * Sq, N_cap, topk);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  csa::timing_begin("index_score", st);
   hipError_t e = csa::launch_index_score(a, st);
-  csa::timing_end("index_score", st);
   if (e != hipSuccess) return launched(e, "index_score launch");
-  csa::timing_begin("index_merge", st);
   e = csa::launch_index_merge(a, st);
-  csa::timing_end("index_merge", st);
   return launched(e, "index_merge launch");
 }
 
@@ -252,14 +238,10 @@ static csa_status check_attend_common(const uint16_t *q, const uint16_t *q_norm_
 
 static csa_status run_attend(csa::AttendArgs &a, void *stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  csa::timing_begin("attend_split", st);
   hipError_t e = csa::launch_attend(a, st);
-  csa::timing_end("attend_split", st);
   if (e != hipSuccess) return launched(e, "attend launch");
   if (a.plan.n_splits > 1) {
-    csa::timing_begin("attend_combine", st);
-    e = csa::launch_combine(a, st);
-    csa::timing_end("attend_combine", st);
+      e = csa::launch_combine(a, st);
   }
   return launched(e, "combine launch");
 }

@@ -399,31 +399,33 @@ size_t attend_workspace_bytes(int64_t n_queries, int H, int D, int64_t n_sel, in
 }
 
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream) {
+  hipError_t e = hipSuccess;
   const int64_t nq = int64_t(a.B) * a.Sq;
   const int64_t pairs = nq * a.plan.n_splits;
   dim3 grid(unsigned(((pairs + 7) / 8) * 8 * a.plan.n_hb));
   switch (a.D) {
-    case 64: hipLaunchKernelGGL(attend_split_kernel<64>, grid, dim3(64 * waves_of<64>()), 0, stream, a, nq); break;
-    case 128: hipLaunchKernelGGL(attend_split_kernel<128>, grid, dim3(64 * waves_of<128>()), 0, stream, a, nq); break;
-    case 256: hipLaunchKernelGGL(attend_split_kernel<256>, grid, dim3(64 * waves_of<256>()), 0, stream, a, nq); break;
-    case 512: hipLaunchKernelGGL(attend_split_kernel<512>, grid, dim3(64 * waves_of<512>()), 0, stream, a, nq); break;
+    case 64: e = launch("attend_split", attend_split_kernel<64>, grid, dim3(64 * waves_of<64>()), stream, a, nq); break;
+    case 128: e = launch("attend_split", attend_split_kernel<128>, grid, dim3(64 * waves_of<128>()), stream, a, nq); break;
+    case 256: e = launch("attend_split", attend_split_kernel<256>, grid, dim3(64 * waves_of<256>()), stream, a, nq); break;
+    case 512: e = launch("attend_split", attend_split_kernel<512>, grid, dim3(64 * waves_of<512>()), stream, a, nq); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return e;
 }
 
 hipError_t launch_combine(const AttendArgs &a, hipStream_t stream) {
+  hipError_t e = hipSuccess;
   if (a.plan.n_splits == 1) return hipSuccess;
   const int64_t nq = int64_t(a.B) * a.Sq;
   dim3 grid(unsigned(nq * a.H));
   switch (a.D) {
-    case 64: hipLaunchKernelGGL(attend_combine_kernel<64>, grid, dim3(16), 0, stream, a, nq); break;
-    case 128: hipLaunchKernelGGL(attend_combine_kernel<128>, grid, dim3(32), 0, stream, a, nq); break;
-    case 256: hipLaunchKernelGGL(attend_combine_kernel<256>, grid, dim3(64), 0, stream, a, nq); break;
-    case 512: hipLaunchKernelGGL(attend_combine_kernel<512>, grid, dim3(128), 0, stream, a, nq); break;
+    case 64: e = launch("attend_combine", attend_combine_kernel<64>, grid, dim3(16), stream, a, nq); break;
+    case 128: e = launch("attend_combine", attend_combine_kernel<128>, grid, dim3(32), stream, a, nq); break;
+    case 256: e = launch("attend_combine", attend_combine_kernel<256>, grid, dim3(64), stream, a, nq); break;
+    case 512: e = launch("attend_combine", attend_combine_kernel<512>, grid, dim3(128), stream, a, nq); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace csa

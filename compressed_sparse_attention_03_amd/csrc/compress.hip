@@ -172,17 +172,18 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
 }  // namespace
 
 hipError_t launch_compress(const CompressArgs &a, hipStream_t stream) {
+  hipError_t e = hipSuccess;
   dim3 grid(unsigned(a.n_new / a.m), unsigned(a.B));
   dim3 block(256);
   switch (a.d / 64) {
-    case 1: hipLaunchKernelGGL(compress_kernel<1>, grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(compress_kernel<2>, grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(compress_kernel<4>, grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(compress_kernel<8>, grid, block, 0, stream, a); break;
-    case 16: hipLaunchKernelGGL(compress_kernel<16>, grid, block, 0, stream, a); break;
+    case 1: e = launch("compress", compress_kernel<1>, grid, block, stream, a); break;
+    case 2: e = launch("compress", compress_kernel<2>, grid, block, stream, a); break;
+    case 4: e = launch("compress", compress_kernel<4>, grid, block, stream, a); break;
+    case 8: e = launch("compress", compress_kernel<8>, grid, block, stream, a); break;
+    case 16: e = launch("compress", compress_kernel<16>, grid, block, stream, a); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace csa

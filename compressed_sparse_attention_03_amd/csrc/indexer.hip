@@ -34,38 +34,80 @@ constexpr int kMaxK = 2048;
 template <int FMT>
 constexpr int batch_of() { return FMT == 1 ? 2 : 4; }
 
+// Cross-lane moves use DPP (a VALU operand modifier: no LDS round trip) inside rows of 16 lanes and
+// v_readlane for the four row results, so a scan or reduction is a short VALU chain.
+constexpr int kDppRowShr = 0x110;            // row_shr:n = kDppRowShr + n
+constexpr int kDppQuadXor1 = 0xb1;           // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4e;           // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {   // lanes without a source read 0
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = uint32_t(dpp<CTRL>(int(uint32_t(v)))), hi = uint32_t(dpp<CTRL>(int(uint32_t(v >> 32))));
+  return (uint64_t(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), l));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), l));
+  return (uint64_t(hi) << 32) | lo;
+}
+
+// Sum over lanes l, l^16, l^32 and l^48, in every lane (gfx950 half-wave and row swaps).
+__device__ __forceinline__ float lane_group_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 struct alignas(16) QueryLds {         // quantised query of one indexer query token
   uint8_t codes[64 * 128];            // fp8: [head][128]; MXFP4: [head][64] packed
   uint8_t sbytes[64 * 4];             // MXFP4 block scales [head][4]
   float f[64];                        // per-head factor: w_h * fp8 scale (w_h for MXFP4); 0 if absent
 };
 
+// Raw bf16 values of one indexer query for thread t: head t/4 (clamped to the last head), values
+// 32*(t%4) .. +31, and that head's weight.  Every thread loads (threads >= 256 repeat threads
+// t - 256), so the number of loads in flight is the same in every wave.
+struct QueryRaw {
+  uint32_t wv[16];
+  float w;
+};
+__device__ __forceinline__ void load_query_raw(const uint16_t *q, const float *w, int H_I, QueryRaw &raw) {
+  const int t = threadIdx.x & 255;
+  const int h = min(t >> 2, H_I - 1), c = t & 3;
+  const uint4 *src = reinterpret_cast<const uint4 *>(q + h * 128 + c * 32);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint4 v = src[k];
+    raw.wv[4 * k] = v.x; raw.wv[4 * k + 1] = v.y; raw.wv[4 * k + 2] = v.z; raw.wv[4 * k + 3] = v.w;
+  }
+  raw.w = w[h];
+}
+
 // Quantise one query's [H_I x 128] bf16 heads into LDS.  Thread t < 256 owns head t/4, values
 // 32*(t%4) .. +31; heads >= H_I are written as zeros (factor 0) so 4 head blocks are always valid.
 template <int FMT>
-__device__ void prep_query_lds(const uint16_t *q, const float *w, int H_I, QueryLds &ql) {
+__device__ void prep_query_lds(const QueryRaw &raw, int H_I, QueryLds &ql) {
   const int t = threadIdx.x;
   if (t < 256) {
     const bool act = t < 4 * H_I;
     const int h = t >> 2, c = t & 3;
     uint32_t wv[16];
-    if (act) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(q + h * 128 + c * 32);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint4 v = src[k];
-        wv[4 * k] = v.x; wv[4 * k + 1] = v.y; wv[4 * k + 2] = v.z; wv[4 * k + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) wv[k] = 0;
-    }
+    for (int k = 0; k < 16; ++k) wv[k] = act ? raw.wv[k] : 0u;
+    const float wh = raw.w;
     float amax = 0.f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fmaxf(fabsf(bf16lo(wv[k])), fabsf(bf16hi(wv[k]))));
     if (FMT == 1) {
-      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      amax = fmaxf(amax, __int_as_float(dpp<kDppQuadXor1>(__float_as_int(amax))));
+      amax = fmaxf(amax, __int_as_float(dpp<kDppQuadXor2>(__float_as_int(amax))));
       const int e = e4m3_row_exp(amax);
       const float inv = ldexpf(1.0f, -e);
       uint32_t outw[8];
@@ -78,7 +120,7 @@ __device__ void prep_query_lds(const uint16_t *q, const float *w, int H_I, Query
       uint4 *dst = reinterpret_cast<uint4 *>(ql.codes + h * 128 + c * 32);
       dst[0] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
       dst[1] = make_uint4(outw[4], outw[5], outw[6], outw[7]);
-      if (c == 0) ql.f[h] = act ? w[h] * ldexpf(1.0f, e) : 0.f;
+      if (c == 0) ql.f[h] = act ? wh * ldexpf(1.0f, e) : 0.f;
     } else {
       const uint32_t sb = mx_scale_byte(amax);
       const float inv = ldexpf(1.0f, 127 - int(sb));
@@ -95,7 +137,7 @@ __device__ void prep_query_lds(const uint16_t *q, const float *w, int H_I, Query
       }
       *reinterpret_cast<uint4 *>(ql.codes + h * 64 + c * 16) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
       ql.sbytes[h * 4 + c] = uint8_t(sb);
-      if (c == 0) ql.f[h] = act ? w[h] : 0.f;
+      if (c == 0) ql.f[h] = act ? wh : 0.f;
     }
   }
 }
@@ -209,8 +251,7 @@ __device__ __forceinline__ void score_batch(const QueryFrag<NHB> &qf, const KeyF
     for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc = fmaf(qf.f[hb][v], relu(c[u][hb][v]), acc);
-    acc += __shfl_xor(acc, 16, 64);
-    acc += __shfl_xor(acc, 32, 64);
+    acc = lane_group_sum(acc);
     const int el = (g0 + u) * 16 + (lane & 15);
     const float ks = FMT == 1 ? __uint_as_float(kf[u].s) : 1.0f;
     if (lane < 16 && g0 + u < ngroups) s_scores[el] = el < vis ? acc * ks : -INFINITY;
@@ -222,22 +263,23 @@ __device__ __forceinline__ void score_batch(const QueryFrag<NHB> &qf, const KeyF
 // next batch is in flight while the current one is scored.  `ka` holds the wave's first batch,
 // issued by the caller.
 template <int FMT, int NHB>
-__device__ void score_tile_mfma(const QueryFrag<NHB> &qf, KeyFrag<FMT> (&ka)[batch_of<FMT>()], const TileKeys<FMT> &tk,
-                                int tile, int vis, float *s_scores) {
+__device__ void score_tile_mfma(const QueryFrag<NHB> &qf, KeyFrag<FMT> (&ka)[batch_of<FMT>()],
+                                KeyFrag<FMT> (&kb)[batch_of<FMT>()], const TileKeys<FMT> &tk, int tile, int vis,
+                                float *s_scores) {
   // the wave index is uniform: say so, so group offsets stay scalar (no per-lane loop over them)
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
   const int ngroups = tile >> 4;
   const int stride = nwaves * batch_of<FMT>();
-  KeyFrag<FMT> kb[batch_of<FMT>()];
+  // On entry ka holds groups from wave * batch and kb the batch one stride later (both in flight).
+  // Each batch is scored while the other one's loads are in flight; loads are unconditional, so
+  // the count of loads in flight is the same on every path and each wait covers only the batch
+  // about to be scored.
   for (int g0 = wave * batch_of<FMT>(); g0 < ngroups; g0 += 2 * stride) {
-    const int g1 = g0 + stride;
-    // unconditional loads keep the count of loads in flight the same on every path, so each wait
-    // covers only the batch about to be scored
-    load_batch<FMT>(tk, g1, lane, kb);
     score_batch<FMT, NHB>(qf, ka, g0, ngroups, vis, lane, s_scores);
-    load_batch<FMT>(tk, g1 + stride, lane, ka);
-    if (g1 < ngroups) score_batch<FMT, NHB>(qf, kb, g1, ngroups, vis, lane, s_scores);
+    load_batch<FMT>(tk, g0 + 2 * stride, lane, ka);
+    if (g0 + stride < ngroups) score_batch<FMT, NHB>(qf, kb, g0 + stride, ngroups, vis, lane, s_scores);
+    load_batch<FMT>(tk, g0 + 3 * stride, lane, kb);
   }
 }
 
@@ -263,14 +305,31 @@ __device__ void score_tile_f32(const float *q_lds, const float *w, int H_I, int 
   }
 }
 
-// ---- block-wide helpers -----------------------------------------------------------------------
+// ---- wave and block helpers ------------------------------------------------------------------
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Inclusive prefix sum over the wave's 64 lanes.
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
-  return v;
+  v += dpp<kDppRowShr + 1>(v);
+  v += dpp<kDppRowShr + 2>(v);
+  v += dpp<kDppRowShr + 4>(v);
+  v += dpp<kDppRowShr + 8>(v);
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row == 0 ? 0 : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2);
+}
+
+// Wave-uniform minimum / maximum of a u64 over the 64 lanes.
+template <bool MIN>
+__device__ __forceinline__ uint64_t wave_minmax_u64(uint64_t v) {
+  auto pick = [](uint64_t a, uint64_t b) { return MIN ? umin64(a, b) : umax64(a, b); };
+  v = pick(v, dpp64<kDppQuadXor1>(v));
+  v = pick(v, dpp64<kDppQuadXor2>(v));
+  v = pick(v, dpp64<kDppRowHalfMirror>(v));
+  v = pick(v, dpp64<kDppRowMirror>(v));
+  return pick(pick(readlane64(v, 0), readlane64(v, 16)), pick(readlane64(v, 32), readlane64(v, 48)));
 }
 
 // Exclusive prefix over the block of one int per thread; returns (prefix, total).
@@ -293,39 +352,33 @@ __device__ __forceinline__ int block_excl_scan(int v, int *s_tmp, int &total) {
   return base + incl - v;
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
-  uint32_t lo = __shfl_xor(uint32_t(v), o, 64), hi = __shfl_xor(uint32_t(v >> 32), o, 64);
-  return (uint64_t(hi) << 32) | lo;
-}
-__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
 struct alignas(16) SelectLds {
   uint32_t hist[3][256];
   uint64_t u64[16];
 };
 
-// Rank-`need` (1 = largest) key among the non-zero keys held by the block (KPT per thread).
-// Keys are distinct.  The caller guarantees 1 <= need <= number of non-zero keys.
+// Threshold over the non-zero keys held by the block (KPT per thread; keys are distinct; the
+// caller guarantees 1 <= need <= number of non-zero keys).  Returns E such that the keys >= E are
+// the largest ones and number
+//   exactly `need` (E is then the need-th largest key itself), or
+//   between keep_min and need - 1 (E is then a bin edge), when keep_min < need and a histogram
+//   pass already separates at least keep_min of the largest keys from the rest.
 // MSB-first radix select that starts at the highest bit where the keys differ (the bits above it
-// are shared by every key, so histogramming them would pile every key into one bin), resolves up
-// to 8 bits per pass and stops as soon as the answer's bucket is exactly filled.  Every wave scans
-// the histogram itself and the histograms rotate over three buffers (pass p zeroes the buffer of
-// pass p+2, whose last readers finished before pass p's barrier), so a pass costs one barrier.
+// are shared by every key, so histogramming them would pile every key into one bin) and resolves
+// up to 8 bits per pass.  Every wave scans the histogram itself and the histograms rotate over
+// three buffers (pass p zeroes the buffer of pass p+2, whose last readers finished before pass p's
+// barrier), so a pass costs one barrier.
 template <int NT, int KPT>
-__device__ uint64_t block_select(const uint64_t (&keys)[KPT], int need, SelectLds &sl) {
+__device__ uint64_t block_cut(const uint64_t (&keys)[KPT], int need, int keep_min, SelectLds &sl) {
   constexpr int NW = NT / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int i = tid; i < 768; i += NT) (&sl.hist[0][0])[i] = 0;
   uint64_t mn = ~uint64_t(0), mx = 0;
 #pragma unroll
   for (int k = 0; k < KPT; ++k)
     if (keys[k] != 0) { mn = umin64(mn, keys[k]); mx = umax64(mx, keys[k]); }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = umin64(mn, shfl_xor_u64(mn, o));
-    mx = umax64(mx, shfl_xor_u64(mx, o));
-  }
+  mn = wave_minmax_u64<true>(mn);
+  mx = wave_minmax_u64<false>(mx);
   if (lane == 0) { sl.u64[wave] = mn; sl.u64[8 + wave] = mx; }
   __syncthreads();
   mn = ~uint64_t(0); mx = 0;
@@ -335,6 +388,7 @@ __device__ uint64_t block_select(const uint64_t (&keys)[KPT], int need, SelectLd
   int hi = 63 - __clzll(mn ^ mx);                 // highest bit where keys differ
   uint64_t mask = hi == 63 ? 0 : ~((uint64_t(2) << hi) - 1);
   uint64_t prefix = mn & mask;
+  int got = 0;                                    // keys already known to lie above the prefix
   for (int pass = 0;; ++pass) {
     uint32_t *H = sl.hist[pass % 3];
     const int width = hi + 1 < 8 ? hi + 1 : 8;
@@ -355,14 +409,19 @@ __device__ uint64_t block_select(const uint64_t (&keys)[KPT], int need, SelectLd
       if (!hit && cum < need && need <= cum + c[j]) { hit = 1; d_sel = 255 - 4 * lane - j; above = cum; bucket = c[j]; }
       cum += c[j];
     }
-    const uint64_t bal = __ballot(hit);
-    const int src = __ffsll((unsigned long long)bal) - 1;
-    d_sel = __shfl(d_sel, src, 64);
-    above = __shfl(above, src, 64);
-    bucket = __shfl(bucket, src, 64);
+    const int src = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)__ballot(hit)) - 1);
+    d_sel = __builtin_amdgcn_readlane(d_sel, src);
+    above = __builtin_amdgcn_readlane(above, src);
+    bucket = __builtin_amdgcn_readlane(bucket, src);
     // pass p-1's buffer (= pass p+2's) was last read before this pass's barrier: clear it
     uint32_t *Hn = sl.hist[(pass + 2) % 3];
     for (int i = tid; i < 256; i += NT) Hn[i] = 0;
+    if (bucket != need - above && got + above >= keep_min) {
+      // enough keys lie in the bins above d_sel: cut at that bin's upper edge
+      __syncthreads();
+      return (prefix | (uint64_t(d_sel) << shift)) + (uint64_t(1) << shift);
+    }
+    got += above;
     need -= above;
     prefix |= uint64_t(d_sel) << shift;
     mask |= dmask << shift;
@@ -372,8 +431,7 @@ __device__ uint64_t block_select(const uint64_t (&keys)[KPT], int need, SelectLd
 #pragma unroll
       for (int k = 0; k < KPT; ++k)
         if (keys[k] != 0 && (keys[k] & mask) == prefix) m2 = umin64(m2, keys[k]);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) m2 = umin64(m2, shfl_xor_u64(m2, o));
+      m2 = wave_minmax_u64<true>(m2);
       if (lane == 0) sl.u64[wave] = m2;
       __syncthreads();
       uint64_t res = ~uint64_t(0);
@@ -384,6 +442,12 @@ __device__ uint64_t block_select(const uint64_t (&keys)[KPT], int need, SelectLd
     }
     hi = shift - 1;
   }
+}
+
+// Exact rank-`need` (1 = largest) key among the block's non-zero keys.
+template <int NT, int KPT>
+__device__ __forceinline__ uint64_t block_select(const uint64_t (&keys)[KPT], int need, SelectLds &sl) {
+  return block_cut<NT, KPT>(keys, need, need, sl);
 }
 
 // ---- kernel 1: scores and per-tile candidates ------------------------------------------------
@@ -425,17 +489,22 @@ __global__ void __launch_bounds__(NT) index_score_kernel(IndexArgs a) {
     score_tile_f32(q_lds, sh.ql.f, a.H_I, a.D_I, static_cast<const float *>(a.k_codes), row0, tile, vis,
                    sh.scores);
   } else {
+    // the query's loads go first (loads complete in issue order), then two batches of keys, which
+    // stream while the query is quantised
+    QueryRaw raw;
+    load_query_raw(static_cast<const uint16_t *>(a.q_idx) + qi * a.H_I * 128, a.w_idx + qi * a.H_I, a.H_I, raw);
+    __builtin_amdgcn_sched_barrier(0);                         // keep the query loads first
     const int rows = int(min(int64_t(tile), a.N_cap - e_begin));
     const TileKeys<FMT> tk = make_tile_keys<FMT>(a.k_codes, a.k_scales, row0, rows, threadIdx.x & 63);
-    KeyFrag<FMT> kf[batch_of<FMT>()];
+    KeyFrag<FMT> ka[batch_of<FMT>()], kb[batch_of<FMT>()];
     const int g_first = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * batch_of<FMT>();
-    load_batch<FMT>(tk, g_first, threadIdx.x & 63, kf);   // stream before prep
-    prep_query_lds<FMT>(static_cast<const uint16_t *>(a.q_idx) + qi * a.H_I * 128, a.w_idx + qi * a.H_I,
-                        a.H_I, sh.ql);
+    load_batch<FMT>(tk, g_first, threadIdx.x & 63, ka);
+    load_batch<FMT>(tk, g_first + (NT / 64) * batch_of<FMT>(), threadIdx.x & 63, kb);
+    prep_query_lds<FMT>(raw, a.H_I, sh.ql);
     __syncthreads();
     QueryFrag<NHB> qf;
     load_query_frag<FMT, NHB>(sh.ql, threadIdx.x & 63, qf);
-    score_tile_mfma<FMT, NHB>(qf, kf, tk, tile, vis, sh.scores);
+    score_tile_mfma<FMT, NHB>(qf, ka, kb, tk, tile, vis, sh.scores);
   }
   __syncthreads();
   if (a.scores) {
@@ -454,7 +523,10 @@ __global__ void __launch_bounds__(NT) index_score_kernel(IndexArgs a) {
     nvalid_local += ok;
   }
   uint64_t bound = 0;
-  if (vis > cand) bound = block_select<NT, KPT>(keys, cand, sh.sel);
+  // keep the tile's largest keys: all `cand` of them, or at least half as many when one histogram
+  // pass already separates them (the merge checks every truncated tile's bound against its
+  // threshold and rescans the tile when the bound is not below it)
+  if (vis > cand) bound = block_cut<NT, KPT>(keys, cand, cand / 2, sh.sel);
   int mine = 0;
 #pragma unroll
   for (int k = 0; k < KPT; ++k) mine += (keys[k] != 0 && keys[k] >= bound);
@@ -525,8 +597,9 @@ __device__ void merge_fallback(const IndexArgs &a, MergeShared &sh, const uint64
     if (tid < a.H_I) sh.ql.f[tid] = a.w_idx[qi * a.H_I + tid];
     __syncthreads();
   } else {
-    prep_query_lds<FMT>(static_cast<const uint16_t *>(a.q_idx) + qi * a.H_I * 128, a.w_idx + qi * a.H_I,
-                        a.H_I, sh.ql);
+    QueryRaw raw;
+    load_query_raw(static_cast<const uint16_t *>(a.q_idx) + qi * a.H_I * 128, a.w_idx + qi * a.H_I, a.H_I, raw);
+    prep_query_lds<FMT>(raw, a.H_I, sh.ql);
     __syncthreads();
     load_query_frag<FMT, 4>(sh.ql, tid & 63, qf);
   }
@@ -543,10 +616,11 @@ __device__ void merge_fallback(const IndexArgs &a, MergeShared &sh, const uint64
     } else {
       const int rows = int(min(int64_t(tile), a.N_cap - e_begin));
       const TileKeys<FMT> tk = make_tile_keys<FMT>(a.k_codes, a.k_scales, row0, rows, tid & 63);
-      KeyFrag<FMT> kf[batch_of<FMT>()];
+      KeyFrag<FMT> ka[batch_of<FMT>()], kb[batch_of<FMT>()];
       const int g_first = __builtin_amdgcn_readfirstlane(tid >> 6) * batch_of<FMT>();
-      if (g_first < tile / 16) load_batch<FMT>(tk, g_first, tid & 63, kf);
-      score_tile_mfma<FMT, 4>(qf, kf, tk, tile, vis, sh.scores);
+      load_batch<FMT>(tk, g_first, tid & 63, ka);
+      load_batch<FMT>(tk, g_first + (NT / 64) * batch_of<FMT>(), tid & 63, kb);
+      score_tile_mfma<FMT, 4>(qf, ka, kb, tk, tile, vis, sh.scores);
     }
     __syncthreads();
     // append the tile's entries below its bound (the ones not already candidates) and above tau
@@ -624,11 +698,21 @@ __global__ void __launch_bounds__(kMergeThreads) index_merge_kernel(IndexArgs a)
 
   // candidate slots and per-tile counts are loaded together; slots past a tile's count are masked
   uint64_t keys[KPT];
-  const int slots = n_tiles * cand;
+  const int slots = n_tiles * cand;                            // a multiple of 8
+  if constexpr (KPT % 2 == 0) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(cand_keys + qi * slots + tid * KPT);
 #pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const int slot = tid * KPT + k;
-    keys[k] = slot < slots ? cand_keys[qi * slots + slot] : 0;
+    for (int k = 0; k < KPT; k += 2) {
+      const uint4 v = tid * KPT + k < slots ? src[k / 2] : make_uint4(0, 0, 0, 0);
+      keys[k] = (uint64_t(v.y) << 32) | v.x;
+      keys[k + 1] = (uint64_t(v.w) << 32) | v.z;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const int slot = tid * KPT + k;
+      keys[k] = slot < slots ? cand_keys[qi * slots + slot] : 0;
+    }
   }
   for (int i = tid; i < n_tiles; i += NT) {
     sh.counts[i] = cand_count[qi * n_tiles + i];
@@ -673,33 +757,35 @@ __global__ void __launch_bounds__(kMergeThreads) index_merge_kernel(IndexArgs a)
 
 template <int FMT, int NHB>
 hipError_t launch_score_t(const IndexArgs &a, hipStream_t stream) {
+  hipError_t e = hipSuccess;
   dim3 grid(unsigned(a.plan.n_tiles), unsigned(int64_t(a.B) * a.Sq));
   switch (a.plan.tile) {
     case 64: case 128: case 256:
-      hipLaunchKernelGGL((index_score_kernel<FMT, NHB, 256, 1>), grid, dim3(256), 0, stream, a); break;
-    case 512: hipLaunchKernelGGL((index_score_kernel<FMT, NHB, 256, 2>), grid, dim3(256), 0, stream, a); break;
-    case 1024: hipLaunchKernelGGL((index_score_kernel<FMT, NHB, 512, 2>), grid, dim3(512), 0, stream, a); break;
-    case 2048: hipLaunchKernelGGL((index_score_kernel<FMT, NHB, 512, 4>), grid, dim3(512), 0, stream, a); break;
+      e = launch("index_score", index_score_kernel<FMT, NHB, 256, 1>, grid, dim3(256), stream, a); break;
+    case 512: e = launch("index_score", index_score_kernel<FMT, NHB, 256, 2>, grid, dim3(256), stream, a); break;
+    case 1024: e = launch("index_score", index_score_kernel<FMT, NHB, 512, 2>, grid, dim3(512), stream, a); break;
+    case 2048: e = launch("index_score", index_score_kernel<FMT, NHB, 512, 4>, grid, dim3(512), stream, a); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return e;
 }
 
 template <int FMT>
 hipError_t launch_merge_t(const IndexArgs &a, hipStream_t stream) {
+  hipError_t e = hipSuccess;
   dim3 grid(unsigned(int64_t(a.B) * a.Sq));
   const int slots = a.plan.n_tiles * a.plan.cand;
   if (slots <= 512)
-    hipLaunchKernelGGL((index_merge_kernel<FMT, 1>), grid, dim3(kMergeThreads), 0, stream, a);
+    e = launch("index_merge", index_merge_kernel<FMT, 1>, grid, dim3(kMergeThreads), stream, a);
   else if (slots <= 1024)
-    hipLaunchKernelGGL((index_merge_kernel<FMT, 2>), grid, dim3(kMergeThreads), 0, stream, a);
+    e = launch("index_merge", index_merge_kernel<FMT, 2>, grid, dim3(kMergeThreads), stream, a);
   else if (slots <= 2048)
-    hipLaunchKernelGGL((index_merge_kernel<FMT, 4>), grid, dim3(kMergeThreads), 0, stream, a);
+    e = launch("index_merge", index_merge_kernel<FMT, 4>, grid, dim3(kMergeThreads), stream, a);
   else if (slots <= 4096)
-    hipLaunchKernelGGL((index_merge_kernel<FMT, 8>), grid, dim3(kMergeThreads), 0, stream, a);
+    e = launch("index_merge", index_merge_kernel<FMT, 8>, grid, dim3(kMergeThreads), stream, a);
   else
-    hipLaunchKernelGGL((index_merge_kernel<FMT, 16>), grid, dim3(kMergeThreads), 0, stream, a);
-  return hipGetLastError();
+    e = launch("index_merge", index_merge_kernel<FMT, 16>, grid, dim3(kMergeThreads), stream, a);
+  return e;
 }
 
 }  // namespace

@@ -1,6 +1,7 @@
 // Internal launcher interface between the C-ABI front (api.cpp) and the kernel sources.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -81,8 +82,22 @@ struct AttendArgs {
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream);
 hipError_t launch_combine(const AttendArgs &a, hipStream_t stream);
 
-// Kernel timing hooks (api.cpp): bracket a launch with events when timing is on.
-void timing_begin(const char *name, hipStream_t stream);
-void timing_end(const char *name, hipStream_t stream);
+// Kernel timing (api.cpp).  When timing is on, timing_events hands out a start/stop event pair
+// filed under `name`; launch() then passes them in the kernel's own dispatch, so they take the
+// kernel's start and end timestamps (no separate marker packets around it).
+struct TimingEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+TimingEvents timing_events(const char *name);
+
+template <typename F, typename... Args>
+hipError_t launch(const char *name, F kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+  const TimingEvents t = timing_events(name);
+  if (t.start)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, t.start, t.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+  return hipGetLastError();
+}
 
 }  // namespace csa

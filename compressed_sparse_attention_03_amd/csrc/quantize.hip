@@ -69,18 +69,19 @@ __global__ void __launch_bounds__(256) quantize_mxfp4_kernel(const uint16_t *x, 
 }  // namespace
 
 hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t stream) {
+  hipError_t e = hipSuccess;
   if (a.rows == 0) return hipSuccess;
   if (a.format == 1) {
     dim3 grid(unsigned((a.rows + 3) / 4));
-    hipLaunchKernelGGL(quantize_fp8_kernel, grid, dim3(256), 0, stream, a.x,
+    e = launch("quantize", quantize_fp8_kernel, grid, dim3(256), stream, a.x,
                        static_cast<uint8_t *>(a.codes), static_cast<float *>(a.scales), a.rows, a.dim);
   } else {
     const int64_t nb = a.rows * (a.dim / 32);
     dim3 grid(unsigned((nb + 255) / 256));
-    hipLaunchKernelGGL(quantize_mxfp4_kernel, grid, dim3(256), 0, stream, a.x,
+    e = launch("quantize", quantize_mxfp4_kernel, grid, dim3(256), stream, a.x,
                        static_cast<uint8_t *>(a.codes), static_cast<uint8_t *>(a.scales), nb);
   }
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace csa
