@@ -278,7 +278,7 @@ csa_status csa_attend(const uint16_t *q, const uint16_t *q_norm_w, const uint16_
   a.H = H; a.D = D; a.rope_dim = rope_dim; a.window = window; a.m = 1;
   a.scale_log2 = softmax_scale * 1.4426950408889634f; a.log2_base = std::log2(double(rope_base));
   a.eps = eps;
-  a.plan = csa::plan_attend(int64_t(B) * Sq, H, topk, window);
+  a.plan = csa::plan_attend(int64_t(B) * Sq, H, topk, window, D);
   return run_attend(a, stream);
 }
 
@@ -304,7 +304,7 @@ csa_status hca_attend(const uint16_t *q, const uint16_t *q_norm_w, const uint16_
   a.H = H; a.D = D; a.rope_dim = rope_dim; a.window = window; a.m = m;
   a.scale_log2 = softmax_scale * 1.4426950408889634f; a.log2_base = std::log2(double(rope_base));
   a.eps = eps;
-  a.plan = csa::plan_attend(int64_t(B) * Sq, H, N_cap, window);
+  a.plan = csa::plan_attend(int64_t(B) * Sq, H, N_cap, window, D);
   return run_attend(a, stream);
 }
 

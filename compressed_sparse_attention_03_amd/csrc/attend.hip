@@ -96,22 +96,47 @@ __device__ __forceinline__ AttendTile attend_tile(const AttendArgs &a, int64_t n
   return t;
 }
 
-// Waves per workgroup: each wave owns D/NW channels (at least 32).
+// Sum / maximum over lanes l, l^16, l^32 and l^48 (the four row groups of one head), in every lane,
+// with the gfx950 half-wave and row swaps.
+__device__ __forceinline__ float group4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float group4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+constexpr int kWaves = 4;                  // waves per workgroup; each takes whole 16-row chunks
 template <int D>
-constexpr int waves_of() { return D >= 128 ? 4 : D / 32; }
+constexpr int ring_of() { return D == 512 ? 2 : 4; }   // chunks in flight per wave (registers)
+
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 template <int D>
-__global__ void __launch_bounds__(64 * waves_of<D>()) attend_split_kernel(AttendArgs a, int64_t n_queries) {
-  constexpr int NW = waves_of<D>();
-  constexpr int NT = 64 * NW;
-  constexpr int QD = D / NW;          // channels owned by one wave
-  constexpr int NSQ = QD / 32;        // its 32-channel steps
+__global__ void __launch_bounds__(64 * kWaves) attend_split_kernel(AttendArgs a, int64_t n_queries) {
+  constexpr int NT = 64 * kWaves;
+  constexpr int NS = D / 32;          // 32-channel steps of a row (QK^T)
+  constexpr int NB = D / 16;          // 16-channel blocks of O (PV)
   constexpr int QCH = D / 32;         // prologue: threads per head (32 channels each)
-  constexpr int RING = 4;             // 16-row chunks in flight per wave
-  __shared__ __align__(16) uint16_t s_q[16 * D];
+  constexpr int RING = ring_of<D>();
+  constexpr int RS = 2 * D + 16;      // staging row stride in bytes: 16 B of padding per row, so
+                                      // the rows one wide LDS access touches fall in different banks
+  constexpr int QS = D + 8;           // q^ row stride (bf16), padded likewise
+  constexpr int HD = D / 2;           // the merge runs over two halves of the channels
+  constexpr int OS = HD + 4;          // merge row stride (fp32)
+  // LDS: per-wave staging of the current chunk (for the transposing V reads), q^, row codes.
+  // After the row loop the staging area holds the four waves' scaled O, half the channels at a time.
+  __shared__ __align__(16) unsigned char s_stage[kWaves * 16 * RS];
+  __shared__ __align__(16) uint16_t s_q[16 * QS];
   __shared__ int s_row[kMaxRowsPerSplit];
   __shared__ float s_cs[256], s_sn[256];
-  __shared__ __align__(16) float s_part[2][NW][64][4];   // partial S^T per wave, per lane
+  __shared__ float s_m[kWaves][16], s_l[kWaves][16];
+  static_assert(kWaves * 16 * OS * 4 <= kWaves * 16 * RS, "merge buffers must fit in the staging area");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
@@ -126,7 +151,7 @@ __global__ void __launch_bounds__(64 * waves_of<D>()) attend_split_kernel(Attend
   const int64_t r1 = min(int64_t(a.plan.n_rows), r0 + a.plan.rows_per_split);
   const int nr = int(r1 - r0);
   const int n_chunks = (nr + 15) >> 4;
-  const int ch0 = wave * QD;          // first channel of this wave
+  const int my_chunks = n_chunks > wave ? (n_chunks - wave + kWaves - 1) / kWaves : 0;   // chunks wave, wave+4, ...
 
   // ---- prologue.  The raw q chunk (and norm weights) of this thread are loaded first: loads
   // complete in issue order, so anything issued later (the row prefetch) does not delay them.
@@ -134,9 +159,11 @@ __global__ void __launch_bounds__(64 * waves_of<D>()) attend_split_kernel(Attend
   const int qh = tid / QCH, qc = tid % QCH;
   const int qhead = hb * 16 + qh;
   uint4 qraw[4], wraw[4];
-  if (qthread) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(a.q + (qi * a.H + (qhead < a.H ? qhead : 0)) * D + 32 * qc);
-    const uint4 *wsrc = reinterpret_cast<const uint4 *>(a.q_norm_w ? a.q_norm_w + 32 * qc : a.q + 32 * qc);
+  {
+    const int qt = qthread ? tid : 0;
+    const int h0 = hb * 16 + qt / QCH, c0 = qt % QCH;
+    const uint4 *src = reinterpret_cast<const uint4 *>(a.q + (qi * a.H + (h0 < a.H ? h0 : 0)) * D + 32 * c0);
+    const uint4 *wsrc = reinterpret_cast<const uint4 *>(a.q_norm_w ? a.q_norm_w + 32 * c0 : a.q + 32 * c0);
 #pragma unroll
     for (int k = 0; k < 4; ++k) { qraw[k] = src[k]; wraw[k] = wsrc[k]; }
   }
@@ -148,139 +175,141 @@ __global__ void __launch_bounds__(64 * waves_of<D>()) attend_split_kernel(Attend
   const uint16_t *win_b = a.win_rows + int64_t(b) * a.W_cap * D;
   __syncthreads();
 
-  // ring of row fragments: lane (r, g) holds row r of the chunk, channels ch0 + 32s + 8g .. +7
-  Frag8 ring[RING][NSQ];
+  // ring of row fragments: lane (r, g) holds row r of the chunk, channels 32s + 8g .. +7 for every s
+  Frag8 ring[RING][NS];
   int codes[RING];
   // Loads are unconditional (an empty slot reads entry row 0, which exists and is finite; its
   // softmax weight is exactly 0): branch-free code lets the compiler wait only for the chunk in use
   // instead of every outstanding load.
-  auto issue = [&](int c, int slot) {
-    const int i = c * 16 + r;
-    const int code = (c < n_chunks && i < nr) ? s_row[i] : -1;
+  auto issue = [&](int j, int slot) {            // this wave's j-th chunk
+    const int i = (wave + kWaves * j) * 16 + r;
+    const int code = (j < my_chunks && i < nr) ? s_row[i] : -1;
     codes[slot] = code;
     const uint16_t *rp = code < 0 ? ent_b
                                   : (code < a.N_cap ? ent_b + int64_t(code) * D : win_b + (int64_t(code) - a.N_cap) * D);
 #pragma unroll
-    for (int s = 0; s < NSQ; ++s) ring[slot][s].u = *reinterpret_cast<const uint4 *>(rp + ch0 + 32 * s + 8 * g);
+    for (int s = 0; s < NS; ++s) ring[slot][s].u = *reinterpret_cast<const uint4 *>(rp + 32 * s + 8 * g);
   };
 #pragma unroll
-  for (int c = 0; c < RING - 1; ++c) issue(c, c);
+  for (int j = 0; j < RING; ++j) issue(j, j);
 
   // q^ = RoPE(RMSNorm(q)) * scale * log2(e) for the 16 heads, into LDS
   if (qthread) {
-    {
-      const int h = qh, c = qc;
-      float v[32];
+    const int h = qh, c = qc;
+    float v[32];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint4 w = qraw[k];
-        v[8 * k + 0] = bf16lo(w.x); v[8 * k + 1] = bf16hi(w.x); v[8 * k + 2] = bf16lo(w.y);
-        v[8 * k + 3] = bf16hi(w.y); v[8 * k + 4] = bf16lo(w.z); v[8 * k + 5] = bf16hi(w.z);
-        v[8 * k + 6] = bf16lo(w.w); v[8 * k + 7] = bf16hi(w.w);
-      }
-      if (qhead >= a.H) {
+    for (int k = 0; k < 4; ++k) {
+      const uint4 w = qraw[k];
+      v[8 * k + 0] = bf16lo(w.x); v[8 * k + 1] = bf16hi(w.x); v[8 * k + 2] = bf16lo(w.y);
+      v[8 * k + 3] = bf16hi(w.y); v[8 * k + 4] = bf16lo(w.z); v[8 * k + 5] = bf16hi(w.z);
+      v[8 * k + 6] = bf16lo(w.w); v[8 * k + 7] = bf16hi(w.w);
+    }
+    if (qhead >= a.H) {
 #pragma unroll
-        for (int k = 0; k < 32; ++k) v[k] = 0.f;
-      }
-      float ss = 0.f;
+      for (int k = 0; k < 32; ++k) v[k] = 0.f;
+    }
+    float ss = 0.f;
 #pragma unroll
-      for (int k = 0; k < 32; ++k) ss += v[k] * v[k];
+    for (int k = 0; k < 32; ++k) ss += v[k] * v[k];
 #pragma unroll
-      for (int o = 1; o < QCH; o <<= 1) ss += __shfl_xor(ss, o, 64);   // the head's QCH threads
-      const float inv = rsqrtf(ss / float(D) + a.eps) * a.scale_log2;
-      float gw[32];
-      const bool has_w = a.q_norm_w != nullptr;
+    for (int o = 1; o < QCH; o <<= 1) ss += __shfl_xor(ss, o, 64);   // the head's QCH threads
+    const float inv = rsqrtf(ss / float(D) + a.eps) * a.scale_log2;
+    float gw[32];
+    const bool has_w = a.q_norm_w != nullptr;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint4 w = wraw[k];
-        gw[8 * k + 0] = bf16lo(w.x); gw[8 * k + 1] = bf16hi(w.x); gw[8 * k + 2] = bf16lo(w.y);
-        gw[8 * k + 3] = bf16hi(w.y); gw[8 * k + 4] = bf16lo(w.z); gw[8 * k + 5] = bf16hi(w.z);
-        gw[8 * k + 6] = bf16lo(w.w); gw[8 * k + 7] = bf16hi(w.w);
-      }
-      if (!has_w) {
+    for (int k = 0; k < 4; ++k) {
+      const uint4 w = wraw[k];
+      gw[8 * k + 0] = bf16lo(w.x); gw[8 * k + 1] = bf16hi(w.x); gw[8 * k + 2] = bf16lo(w.y);
+      gw[8 * k + 3] = bf16hi(w.y); gw[8 * k + 4] = bf16lo(w.z); gw[8 * k + 5] = bf16hi(w.z);
+      gw[8 * k + 6] = bf16lo(w.w); gw[8 * k + 7] = bf16hi(w.w);
+    }
+    if (!has_w) {
 #pragma unroll
-        for (int k = 0; k < 32; ++k) gw[k] = 1.0f;
-      }
+      for (int k = 0; k < 32; ++k) gw[k] = 1.0f;
+    }
 #pragma unroll
-      for (int k = 0; k < 32; ++k) v[k] *= inv * gw[k];
-      const int rope0 = D - a.rope_dim;
-      if (32 * c + 32 > rope0) {
+    for (int k = 0; k < 32; ++k) v[k] *= inv * gw[k];
+    const int rope0 = D - a.rope_dim;
+    if (32 * c + 32 > rope0) {
 #pragma unroll
-        for (int k = 0; k < 32; k += 2) {
-          const int ch = 32 * c + k;
-          if (ch >= rope0) {
-            const int u = (ch - rope0) >> 1;
-            const float cs = s_cs[u], sn = s_sn[u], x0 = v[k], x1 = v[k + 1];
-            v[k] = x0 * cs - x1 * sn;
-            v[k + 1] = x0 * sn + x1 * cs;
-          }
+      for (int k = 0; k < 32; k += 2) {
+        const int ch = 32 * c + k;
+        if (ch >= rope0) {
+          const int u = (ch - rope0) >> 1;
+          const float cs = s_cs[u], sn = s_sn[u], x0 = v[k], x1 = v[k + 1];
+          v[k] = x0 * cs - x1 * sn;
+          v[k + 1] = x0 * sn + x1 * cs;
         }
       }
-      uint4 *dst = reinterpret_cast<uint4 *>(s_q + h * D + 32 * c);
+    }
+    uint4 *dst = reinterpret_cast<uint4 *>(s_q + h * QS + 32 * c);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        Pack4 lo, hi;
-        lo.s = pack4(v[8 * k], v[8 * k + 1], v[8 * k + 2], v[8 * k + 3]);
-        hi.s = pack4(v[8 * k + 4], v[8 * k + 5], v[8 * k + 6], v[8 * k + 7]);
-        dst[k] = make_uint4(uint32_t(uint16_t(lo.s[0])) | (uint32_t(uint16_t(lo.s[1])) << 16),
-                            uint32_t(uint16_t(lo.s[2])) | (uint32_t(uint16_t(lo.s[3])) << 16),
-                            uint32_t(uint16_t(hi.s[0])) | (uint32_t(uint16_t(hi.s[1])) << 16),
-                            uint32_t(uint16_t(hi.s[2])) | (uint32_t(uint16_t(hi.s[3])) << 16));
-      }
+    for (int k = 0; k < 4; ++k) {
+      Pack4 lo, hi;
+      lo.s = pack4(v[8 * k], v[8 * k + 1], v[8 * k + 2], v[8 * k + 3]);
+      hi.s = pack4(v[8 * k + 4], v[8 * k + 5], v[8 * k + 6], v[8 * k + 7]);
+      dst[k] = make_uint4(uint32_t(uint16_t(lo.s[0])) | (uint32_t(uint16_t(lo.s[1])) << 16),
+                          uint32_t(uint16_t(lo.s[2])) | (uint32_t(uint16_t(lo.s[3])) << 16),
+                          uint32_t(uint16_t(hi.s[0])) | (uint32_t(uint16_t(hi.s[1])) << 16),
+                          uint32_t(uint16_t(hi.s[2])) | (uint32_t(uint16_t(hi.s[3])) << 16));
     }
   }
   __syncthreads();
-  Frag8 qf[NSQ];
-#pragma unroll
-  for (int s = 0; s < NSQ; ++s) qf[s].u = *reinterpret_cast<const uint4 *>(s_q + r * D + ch0 + 32 * s + 8 * g);
 
-  // identity fragment for the V transposes: element j of lane (n, g) is 1 iff n = 4g + j
-  v4s ident;
+  // O block nb: lane (r, g) element v = head 4g+v, channel 16 nb + r
+  v4f o[NB];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) ident[j] = ((r >> 2) == g && (r & 3) == j) ? short(0x3f80) : short(0);
+  for (int k = 0; k < NB; ++k) o[k] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;           // of head r (same in the four lanes of head r)
+  unsigned char *stage = s_stage + wave * 16 * RS;
 
-  v4f o[2 * NSQ];
-#pragma unroll
-  for (int k = 0; k < 2 * NSQ; ++k) o[k] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // one chunk: all waves sum their partial S^T through LDS, update the (identical) softmax state
-  // and accumulate their channels of O.  `slot` is a compile-time ring position after unrolling.
-  auto chunk = [&](int c, int slot) {
+  // One chunk of 16 rows: S^T = K q^T over all D channels (K from registers, q^ from LDS), online
+  // softmax, then the rows go to the wave's staging area once and O += P V takes V^T fragments
+  // from it with the transposing LDS read.  `slot` is a compile-time ring position.
+  auto chunk = [&](int slot) {
     const uint64_t vmask = __ballot(codes[slot] >= 0);
-    v4f st = {0.f, 0.f, 0.f, 0.f};
+    // four independent accumulation chains over the channel steps, summed at the end
+    constexpr int NCH = NS < 4 ? NS : 4;
+    v4f sp[NCH];
 #pragma unroll
-    for (int s = 0; s < NSQ; ++s) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[slot][s].b, qf[s].b, st, 0, 0, 0);
-    *reinterpret_cast<v4f *>(&s_part[c & 1][wave][lane][0]) = st;
-    __syncthreads();
-    v4f full = *reinterpret_cast<const v4f *>(&s_part[c & 1][0][lane][0]);
+    for (int c = 0; c < NCH; ++c) sp[c] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      const v4f x = *reinterpret_cast<const v4f *>(&s_part[c & 1][w][lane][0]);
-      full[0] += x[0]; full[1] += x[1]; full[2] += x[2]; full[3] += x[3];
+    for (int s = 0; s < NS; ++s) {
+      Frag8 qf;
+      qf.u = *reinterpret_cast<const uint4 *>(s_q + r * QS + 32 * s + 8 * g);
+      sp[s % NCH] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[slot][s].b, qf.b, sp[s % NCH], 0, 0, 0);
     }
+    v4f st = sp[0];
+#pragma unroll
+    for (int c = 1; c < NCH; ++c) { st[0] += sp[c][0]; st[1] += sp[c][1]; st[2] += sp[c][2]; st[3] += sp[c][3]; }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      *reinterpret_cast<uint4 *>(stage + r * RS + (32 * s + 8 * g) * 2) = ring[slot][s].u;
+    // st[v] = logit of row 4g+v for head r
     float sv[4], cmax = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      sv[v] = ((vmask >> (4 * g + v)) & 1) ? full[v] : -INFINITY;
+      sv[v] = ((vmask >> (4 * g + v)) & 1) ? st[v] : -INFINITY;
       cmax = fmaxf(cmax, sv[v]);
     }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    cmax = group4_max(cmax);
     // lazy running max: rescale only when some head's max grew past the slack
     const bool grow = cmax > m_run + kRescaleSlack || (m_run == -INFINITY && cmax != -INFINITY);
     if (__any(grow)) {
+      const bool empty = __all(m_run == -INFINITY);        // nothing accumulated yet: O is zero
       const float m_new = fmaxf(m_run, cmax);
       const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
       l_run *= alpha;
       m_run = m_new;
-      float av[4];
+      if (!empty) {
+        float av[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) av[v] = __shfl(alpha, 4 * g + v, 64);
+        for (int v = 0; v < 4; ++v) av[v] = __shfl(alpha, 4 * g + v, 64);
 #pragma unroll
-      for (int k = 0; k < 2 * NSQ; ++k) {
+        for (int k = 0; k < NB; ++k) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) o[k][v] *= av[v];
+          for (int v = 0; v < 4; ++v) o[k][v] *= av[v];
+        }
       }
     }
     float p[4], psum = 0.f;
@@ -289,60 +318,86 @@ __global__ void __launch_bounds__(64 * waves_of<D>()) attend_split_kernel(Attend
       p[v] = (sv[v] == -INFINITY) ? 0.f : exp2f(sv[v] - m_run);
       psum += p[v];
     }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    l_run += psum;
+    l_run += group4_sum(psum);
     const v4s pf = pack4(p[0], p[1], p[2], p[3]);
+    // V^T fragment of block nb: lane (n, g) reads row 4g + n/4, channels 16 nb + 4(n%4) .. +3;
+    // the transposing read hands lane (n, g) rows 4g .. 4g+3 of channel 16 nb + n
+    const unsigned char *vbase = stage + (4 * g + (r >> 2)) * RS + 8 * (r & 3);
 #pragma unroll
-    for (int s = 0; s < NSQ; ++s) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        v4f vt = {0.f, 0.f, 0.f, 0.f};
-        vt = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ring[slot][s].h[h], ident, vt, 0, 0, 0);
-        const v4s vb = pack4(vt[0], vt[1], vt[2], vt[3]);     // exact: the values are bf16
-        o[2 * s + h] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pf, vb, o[2 * s + h], 0, 0, 0);
-      }
+    for (int nb = 0; nb < NB; ++nb) {
+      const v4s vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vbase + 32 * nb));
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pf, vt, o[nb], 0, 0, 0);
     }
   };
-  for (int c0 = 0; c0 < n_chunks; c0 += RING) {
+  for (int j0 = 0; j0 < my_chunks; j0 += RING) {
 #pragma unroll
     for (int k = 0; k < RING; ++k) {
-      if (c0 + k < n_chunks) {
-        issue(c0 + k + RING - 1, (k + RING - 1) % RING);    // keep RING-1 chunks ahead in flight
-        chunk(c0 + k, k);
+      if (j0 + k < my_chunks) {
+        chunk(k);
+        issue(j0 + k + RING, k);     // refill the slot
       }
     }
   }
 
-  // ---- every wave holds the same (m, l) and its own channels of O: normalise and write -------
-  // O element (block 2s+h, v) of lane (r, g): head 4g+v, channel ch0 + 32s + 8(r>>2) + 4h + (r&3)
-  float lv[4], mv[4];
+  // ---- merge the four waves' (m, l, O) states, half of the channels at a time -----------------
+  if (g == 0) { s_m[wave][r] = m_run; s_l[wave][r] = l_run; }
+  __syncthreads();                                   // every wave is done with its staging area
+  float sc[4], invL[4], lse2[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) { lv[v] = __shfl(l_run, 4 * g + v, 64); mv[v] = __shfl(m_run, 4 * g + v, 64); }
+  for (int v = 0; v < 4; ++v) {
+    const int h = 4 * g + v;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) L += s_m[w][h] == -INFINITY ? 0.f : s_l[w][h] * exp2f(s_m[w][h] - M);
+    sc[v] = s_m[wave][h] == -INFINITY ? 0.f : exp2f(s_m[wave][h] - M);
+    invL[v] = L > 0.f ? 1.0f / L : 0.f;
+    lse2[v] = L > 0.f ? M + log2f(L) : -INFINITY;
+  }
   const bool direct = a.plan.n_splits == 1;
   float *po = static_cast<float *>(a.workspace);
   float *plse = po + n_queries * a.H * a.plan.n_splits * D;
+  float *mb = reinterpret_cast<float *>(s_stage);
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int gh = hb * 16 + 4 * g + v;
-    if (gh >= a.H) continue;
-    const float invL = lv[v] > 0.f ? 1.0f / lv[v] : 0.f;
+  for (int half = 0; half < 2; ++half) {
+    // each wave writes its O (scaled to the common per-head maximum and by 1/L) as [head][channel]
+    float *mine = mb + wave * 16 * OS;
 #pragma unroll
-    for (int s = 0; s < NSQ; ++s) {
+    for (int v = 0; v < 4; ++v)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int ch = ch0 + 32 * s + 8 * (r >> 2) + 4 * h + (r & 3);
-        const float x = o[2 * s + h][v] * invL;
-        if (direct) a.out[(qi * a.H + gh) * D + ch] = __builtin_bit_cast(uint16_t, __bf16(x));
-        else po[((qi * a.H + gh) * a.plan.n_splits + split) * int64_t(D) + ch] = x;
+      for (int k = 0; k < NB / 2; ++k) mine[(4 * g + v) * OS + 16 * k + r] = o[half * (NB / 2) + k][v] * (sc[v] * invL[v]);
+    __syncthreads();
+    // every thread sums four consecutive channels of one head over the waves and writes them
+    constexpr int Q4 = HD / 4;
+    for (int e = tid; e < 16 * Q4; e += NT) {
+      const int h = e / Q4, c4 = (e - h * Q4) * 4;
+      const int gh = hb * 16 + h;
+      if (gh >= a.H) continue;
+      float4 acc = *reinterpret_cast<const float4 *>(mb + h * OS + c4);
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) {
+        const float4 x = *reinterpret_cast<const float4 *>(mb + (w * 16 + h) * OS + c4);
+        acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
       }
+      const int ch = half * HD + c4;
+      if (direct)
+        *reinterpret_cast<v4s *>(a.out + (qi * a.H + gh) * D + ch) = pack4(acc.x, acc.y, acc.z, acc.w);
+      else
+        *reinterpret_cast<float4 *>(po + ((qi * a.H + gh) * a.plan.n_splits + split) * int64_t(D) + ch) = acc;
     }
-    if (wave == 0 && r == 0) {
-      const float lse2 = lv[v] > 0.f ? mv[v] + log2f(lv[v]) : -INFINITY;
+    if (half == 0) __syncthreads();
+  }
+  if (wave == 0 && r == 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int gh = hb * 16 + 4 * g + v;
+      if (gh >= a.H) continue;
       if (direct) {
-        if (a.lse) a.lse[qi * a.H + gh] = lse2 * 0.6931471805599453f;
+        if (a.lse) a.lse[qi * a.H + gh] = lse2[v] * 0.6931471805599453f;
       } else {
-        plse[(qi * a.H + gh) * a.plan.n_splits + split] = lse2;
+        plse[(qi * a.H + gh) * a.plan.n_splits + split] = lse2[v];
       }
     }
   }
@@ -375,17 +430,21 @@ __global__ void __launch_bounds__(D / 4) attend_combine_kernel(AttendArgs a, int
 
 }  // namespace
 
-AttendPlan plan_attend(int64_t n_queries, int H, int64_t n_sel, int window) {
+AttendPlan plan_attend(int64_t n_queries, int H, int64_t n_sel, int window, int D) {
   AttendPlan p;
   p.n_hb = (H + 15) / 16;
   p.n_rows = int(n_sel + window);
-  const int64_t pairs = n_queries * p.n_hb;
-  int64_t splits = (512 + pairs - 1) / pairs;
-  const int64_t max_splits = (p.n_rows + 127) / 128;
-  if (splits > max_splits) splits = max_splits;
+  // A split is a multiple of 64 rows (four waves x 16-row chunks).  Aim at two chunks per wave,
+  // but no more splits than keep the grid within one round of resident workgroups (one per CU at
+  // D = 512, two below); every split costs a partial [16 x D] fp32 write and read.
+  const int64_t units = n_queries * p.n_hb;
+  const int64_t resident = D == 512 ? 256 : 512;
+  int64_t splits = (p.n_rows + 127) / 128;
+  const int64_t by_grid = resident / units;
+  if (splits > by_grid) splits = by_grid;
   if (splits < 1) splits = 1;
   int64_t rps = (p.n_rows + splits - 1) / splits;
-  rps = (rps + 15) / 16 * 16;
+  rps = (rps + 63) / 64 * 64;
   if (rps > kMaxRowsPerSplit) rps = kMaxRowsPerSplit;
   p.rows_per_split = int(rps);
   p.n_splits = int((p.n_rows + rps - 1) / rps);
@@ -393,7 +452,7 @@ AttendPlan plan_attend(int64_t n_queries, int H, int64_t n_sel, int window) {
 }
 
 size_t attend_workspace_bytes(int64_t n_queries, int H, int D, int64_t n_sel, int window) {
-  AttendPlan p = plan_attend(n_queries, H, n_sel, window);
+  AttendPlan p = plan_attend(n_queries, H, n_sel, window, D);
   if (p.n_splits == 1) return 256;
   return size_t(n_queries * H * p.n_splits * (int64_t(D) + 1) * 4 + 256);
 }
@@ -404,10 +463,10 @@ hipError_t launch_attend(const AttendArgs &a, hipStream_t stream) {
   const int64_t pairs = nq * a.plan.n_splits;
   dim3 grid(unsigned(((pairs + 7) / 8) * 8 * a.plan.n_hb));
   switch (a.D) {
-    case 64: e = launch("attend_split", attend_split_kernel<64>, grid, dim3(64 * waves_of<64>()), stream, a, nq); break;
-    case 128: e = launch("attend_split", attend_split_kernel<128>, grid, dim3(64 * waves_of<128>()), stream, a, nq); break;
-    case 256: e = launch("attend_split", attend_split_kernel<256>, grid, dim3(64 * waves_of<256>()), stream, a, nq); break;
-    case 512: e = launch("attend_split", attend_split_kernel<512>, grid, dim3(64 * waves_of<512>()), stream, a, nq); break;
+    case 64: e = launch("attend_split", attend_split_kernel<64>, grid, dim3(64 * kWaves), stream, a, nq); break;
+    case 128: e = launch("attend_split", attend_split_kernel<128>, grid, dim3(64 * kWaves), stream, a, nq); break;
+    case 256: e = launch("attend_split", attend_split_kernel<256>, grid, dim3(64 * kWaves), stream, a, nq); break;
+    case 512: e = launch("attend_split", attend_split_kernel<512>, grid, dim3(64 * kWaves), stream, a, nq); break;
     default: return hipErrorInvalidValue;
   }
   return e;

@@ -60,7 +60,7 @@ struct AttendPlan {
   int rows_per_split;
   int n_rows;       // row-list length per query: n_sel + window
 };
-AttendPlan plan_attend(int64_t n_queries, int H, int64_t n_sel, int window);
+AttendPlan plan_attend(int64_t n_queries, int H, int64_t n_sel, int window, int D);
 size_t attend_workspace_bytes(int64_t n_queries, int H, int D, int64_t n_sel, int window);
 
 struct AttendArgs {
