@@ -228,16 +228,70 @@ def cpu_baseline(w: gen.Workload, budget_s: float = 12.0):
                       f"top-{w.topk}, attention over {w.topk}+{w.window} rows); keys pre-quantised"}
 
 
+COPY_BYTES, COPY_LAUNCHES = 1 << 30, 5
+
+
 def copy_calibration():
-    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE."""
-    n = 1 << 30
-    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    """Plain device copies of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE."""
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     a.fill_(1)
-    for _ in range(5):
+    for _ in range(COPY_LAUNCHES):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "launches": COPY_LAUNCHES}))
+
+
+# ---- rocprofv3 summaries (text for profiles/) -----------------------------------------------------
+def _short_kernel(name: str) -> str:
+    name = name.replace("void ", "").replace("csa::(anonymous namespace)::", "")
+    return name.split("(")[0]
+
+
+def summarize_trace(db: str, min_calls: int = 3) -> str:
+    """Per-kernel duration table of a `rocprofv3 --kernel-trace` database (one row per kernel and
+    grid size: launches of one kernel on different workloads differ in grid)."""
+    import sqlite3
+    cur = sqlite3.connect(db).cursor()
+    rows = cur.execute("select name, grid_x, grid_y, workgroup_x, count(*), avg(duration), min(duration), "
+                       "max(duration) from kernels group by name, grid_x, grid_y order by min(start)").fetchall()
+    out = ["| kernel | grid (threads) | block | launches | avg us | min us | max us |", "|---|---|---|---|---|---|---|"]
+    for n, gx, gy, wx, c, a, mn, mx in rows:
+        if c >= min_calls:
+            out.append(f"| {_short_kernel(n)} | {gx}x{gy} | {wx} | {c} | {a / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} |")
+    return "\n".join(out)
+
+
+def _counter_stats(db: str, counter: str, kernel_substr: str):
+    """(average per dispatch, sum, dispatches) of one counter over the dispatches of a kernel."""
+    import sqlite3
+    cur = sqlite3.connect(db).cursor()
+    r = cur.execute("select avg(counter_value), sum(counter_value), count(*) from pmc_events "
+                    "where counter_name = ? and name like ?", (counter, f"%{kernel_substr}%")).fetchone()
+    return (r[0], r[1], r[2]) if r and r[2] else (None, None, 0)
+
+
+def summarize_traffic(fetch_db: str, write_db: str, copy_fetch_db: str, copy_write_db: str, kernel: str,
+                      source: str) -> str:
+    """key = value summary of HBM traffic per dispatch of `kernel` (FETCH_SIZE and WRITE_SIZE in KiB,
+    each scaled by what the counter reads for a plain copy of known size)."""
+    copy_bytes = COPY_BYTES * COPY_LAUNCHES          # every device copy `--mode copy` makes
+    _, cf, _ = _counter_stats(copy_fetch_db, "FETCH_SIZE", "copyBuffer")
+    _, cw, _ = _counter_stats(copy_write_db, "WRITE_SIZE", "copyBuffer")
+    kf, _, nf = _counter_stats(fetch_db, "FETCH_SIZE", kernel)
+    kw, _, nw = _counter_stats(write_db, "WRITE_SIZE", kernel)
+    ff = copy_bytes / (cf * 1024.0)
+    fw = copy_bytes / (cw * 1024.0)
+    src = os.path.join(ROOT, "compressed_sparse_attention_03_amd", "csrc", source)
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    traffic = kf * 1024.0 * ff + kw * 1024.0 * fw
+    return "\n".join([
+        f"kernel = {kernel}", f"source = {source}", f"source_sha256_16 = {sha}",
+        f"fetch_kib_per_dispatch = {kf:.1f}", f"fetch_dispatches = {nf}",
+        f"write_kib_per_dispatch = {kw:.1f}", f"write_dispatches = {nw}",
+        f"copy_bytes = {copy_bytes}", f"copy_fetch_kib = {cf:.1f}", f"copy_write_kib = {cw:.1f}",
+        f"fetch_factor = {ff:.3f}", f"write_factor = {fw:.3f}",
+        f"traffic_bytes_per_dispatch = {traffic:.0f}"])
 
 
 def main():
@@ -246,7 +300,11 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--legs", default="main,d128,c32k,hca")
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "summarize-trace", "summarize-traffic"])
+    ap.add_argument("--db", nargs="*", default=[], help="rocprofv3 databases for the summarize modes: one "
+                    "kernel-trace db; or FETCH, WRITE, copy-FETCH, copy-WRITE dbs")
+    ap.add_argument("--kernel", default="index_score_kernel")
+    ap.add_argument("--source", default="indexer.hip")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -255,6 +313,12 @@ def main():
         sys.exit(2)
     if args.mode == "copy":
         copy_calibration()
+        return
+    if args.mode == "summarize-trace":
+        print(summarize_trace(args.db[0]))
+        return
+    if args.mode == "summarize-traffic":
+        print(summarize_traffic(*args.db[:4], kernel=args.kernel, source=args.source))
         return
     legs = args.legs.split(",")
     table = {"main": gen.CSA_DECODE_1M, "d128": gen.CSA_DECODE_128K, "c32k": gen.CSA_DECODE_32K,
