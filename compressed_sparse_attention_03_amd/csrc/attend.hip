@@ -256,7 +256,8 @@ __global__ void __launch_bounds__(64 * kWaves) attend_split_kernel(AttendArgs a,
   }
   __syncthreads();
 
-  // O block nb: lane (r, g) element v = head 4g+v, channel 16 nb + r
+  // O^T block nb (O^T = V^T P^T): lane (r, g) element v = head r, channel 16 nb + 4g + v, so a
+  // lane owns one head: the rescale is lane-local and the merge writes 16 B per block
   v4f o[NB];
 #pragma unroll
   for (int k = 0; k < NB; ++k) o[k] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -302,13 +303,10 @@ __global__ void __launch_bounds__(64 * kWaves) attend_split_kernel(AttendArgs a,
       l_run *= alpha;
       m_run = m_new;
       if (!empty) {
-        float av[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) av[v] = __shfl(alpha, 4 * g + v, 64);
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) o[k][v] *= av[v];
+          for (int v = 0; v < 4; ++v) o[k][v] *= alpha;
         }
       }
     }
@@ -321,12 +319,13 @@ __global__ void __launch_bounds__(64 * kWaves) attend_split_kernel(AttendArgs a,
     l_run += group4_sum(psum);
     const v4s pf = pack4(p[0], p[1], p[2], p[3]);
     // V^T fragment of block nb: lane (n, g) reads row 4g + n/4, channels 16 nb + 4(n%4) .. +3;
-    // the transposing read hands lane (n, g) rows 4g .. 4g+3 of channel 16 nb + n
+    // the transposing read hands lane (n, g) rows 4g .. 4g+3 of channel 16 nb + n -- the A
+    // operand (channel n, rows 4g..) of O^T += V^T P^T, with P^T as B (lane (r, g): head r, rows 4g..)
     const unsigned char *vbase = stage + (4 * g + (r >> 2)) * RS + 8 * (r & 3);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const v4s vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vbase + 32 * nb));
-      o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pf, vt, o[nb], 0, 0, 0);
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pf, o[nb], 0, 0, 0);
     }
   };
   for (int j0 = 0; j0 < my_chunks; j0 += RING) {
@@ -342,32 +341,28 @@ __global__ void __launch_bounds__(64 * kWaves) attend_split_kernel(AttendArgs a,
   // ---- merge the four waves' (m, l, O) states, half of the channels at a time -----------------
   if (g == 0) { s_m[wave][r] = m_run; s_l[wave][r] = l_run; }
   __syncthreads();                                   // every wave is done with its staging area
-  float sc[4], invL[4], lse2[4];
+  // head r's merged maximum, sum and this wave's share (every lane of head r computes the same)
+  float M = -INFINITY;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int h = 4 * g + v;
-    float M = -INFINITY;
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
+  float L = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) L += s_m[w][h] == -INFINITY ? 0.f : s_l[w][h] * exp2f(s_m[w][h] - M);
-    sc[v] = s_m[wave][h] == -INFINITY ? 0.f : exp2f(s_m[wave][h] - M);
-    invL[v] = L > 0.f ? 1.0f / L : 0.f;
-    lse2[v] = L > 0.f ? M + log2f(L) : -INFINITY;
-  }
+  for (int w = 0; w < kWaves; ++w) L += s_m[w][r] == -INFINITY ? 0.f : s_l[w][r] * exp2f(s_m[w][r] - M);
+  const float share = (s_m[wave][r] == -INFINITY || !(L > 0.f)) ? 0.f : exp2f(s_m[wave][r] - M) / L;
   const bool direct = a.plan.n_splits == 1;
   float *po = static_cast<float *>(a.workspace);
   float *plse = po + n_queries * a.H * a.plan.n_splits * D;
   float *mb = reinterpret_cast<float *>(s_stage);
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    // each wave writes its O (scaled to the common per-head maximum and by 1/L) as [head][channel]
+    // each wave writes its O^T blocks of this half, scaled by its share, as [head][channel]
     float *mine = mb + wave * 16 * OS;
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-#pragma unroll
-      for (int k = 0; k < NB / 2; ++k) mine[(4 * g + v) * OS + 16 * k + r] = o[half * (NB / 2) + k][v] * (sc[v] * invL[v]);
+    for (int k = 0; k < NB / 2; ++k) {
+      const v4f x = o[half * (NB / 2) + k];
+      *reinterpret_cast<float4 *>(mine + r * OS + 16 * k + 4 * g) =
+          make_float4(x[0] * share, x[1] * share, x[2] * share, x[3] * share);
+    }
     __syncthreads();
     // every thread sums four consecutive channels of one head over the waves and writes them
     constexpr int Q4 = HD / 4;
@@ -389,15 +384,14 @@ __global__ void __launch_bounds__(64 * kWaves) attend_split_kernel(AttendArgs a,
     }
     if (half == 0) __syncthreads();
   }
-  if (wave == 0 && r == 0) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int gh = hb * 16 + 4 * g + v;
-      if (gh >= a.H) continue;
+  if (wave == 0 && g == 0) {
+    const int gh = hb * 16 + r;
+    if (gh < a.H) {
+      const float lse2 = L > 0.f ? M + log2f(L) : -INFINITY;
       if (direct) {
-        if (a.lse) a.lse[qi * a.H + gh] = lse2[v] * 0.6931471805599453f;
+        if (a.lse) a.lse[qi * a.H + gh] = lse2 * 0.6931471805599453f;
       } else {
-        plse[(qi * a.H + gh) * a.plan.n_splits + split] = lse2[v];
+        plse[(qi * a.H + gh) * a.plan.n_splits + split] = lse2;
       }
     }
   }
@@ -406,21 +400,35 @@ __global__ void __launch_bounds__(64 * kWaves) attend_split_kernel(AttendArgs a,
 // One workgroup per (query, head): merge the slices in order.
 template <int D>
 __global__ void __launch_bounds__(D / 4) attend_combine_kernel(AttendArgs a, int64_t n_queries) {
+  constexpr int kBatch = 8;                       // slices whose loads are in flight together
   const int64_t qh = blockIdx.x;                  // query * H + head
   const int ns = a.plan.n_splits;
   const float *po = static_cast<const float *>(a.workspace) + qh * ns * int64_t(D);
   const float *plse = static_cast<const float *>(a.workspace) + n_queries * a.H * ns * int64_t(D) + qh * ns;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, plse[s]);
-  float L = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   const int ch = threadIdx.x * 4;
-  for (int s = 0; s < ns; ++s) {
-    const float ls = plse[s];
-    const float wgt = (ls == -INFINITY) ? 0.f : exp2f(ls - M);
-    L += wgt;
-    const float4 x = *reinterpret_cast<const float4 *>(po + s * int64_t(D) + ch);
-    acc.x += wgt * x.x; acc.y += wgt * x.y; acc.z += wgt * x.z; acc.w += wgt * x.w;
+  // every slice's log2-sum-exp and partial are loaded before any is used (one round trip per
+  // batch of slices), then merged in slice order with a running maximum
+  float M = -INFINITY, L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < ns; s0 += kBatch) {
+    float ls[kBatch];
+    float4 x[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int s = s0 + j < ns ? s0 + j : ns - 1;
+      ls[j] = plse[s];
+      x[j] = *reinterpret_cast<const float4 *>(po + s * int64_t(D) + ch);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (s0 + j >= ns || ls[j] == -INFINITY) continue;
+      const float Mn = fmaxf(M, ls[j]);
+      const float c = M == -INFINITY ? 0.f : exp2f(M - Mn), w = exp2f(ls[j] - Mn);
+      L = L * c + w;
+      acc.x = acc.x * c + w * x[j].x; acc.y = acc.y * c + w * x[j].y;
+      acc.z = acc.z * c + w * x[j].z; acc.w = acc.w * c + w * x[j].w;
+      M = Mn;
+    }
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   uint16_t *dst = a.out + qh * D + ch;
