@@ -1,7 +1,8 @@
 """Benchmark: CSA decode query-tokens/s at 1M and 128K context on one MI355X, with the roofline of
 the dominant kernel and the CPU oracle timed beside it.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs main,d128,c32k,hca] [--mode bench|copy]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs main,d128,c32k,hca,prefill,compress]
+                    [--mode bench|copy|summarize-trace|summarize-traffic]
 
 One step = one decode pass of the whole hot path over one batch: csa_index_topk (lightning-indexer
 scores + top-k) then csa_attend (shared-KV attention over the selected entries + window) for CSA;
@@ -242,6 +243,133 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "launches": COPY_LAUNCHES}))
 
 
+# ---- prefill chunk and compressor legs ------------------------------------------------------------
+class PrefillLeg:
+    """One prefill chunk: compress 4,096 new tokens (plus the m-token halo) into 1,024 entries
+    appended after the 32,768 existing ones (and their prepared window rows), quantise the new
+    entries' indexer keys, then csa_index_topk and csa_attend for all 4,096 query tokens."""
+
+    def __init__(self, w: gen.Workload):
+        self.w = w
+        n, m, d = w.Sq, w.m, w.d
+        self.N0, self.Wp = w.N, w.window - 1                # existing entries, earlier window rows
+        self.N_cap, self.W_cap = w.N + n // m, w.window - 1 + n
+        log(f"[{w.name}] generating inputs")
+        t0 = time.time()
+        self.c = dev_bf16(gen.normal_bf16(w.cfg, gen.T_C, (n + m, d))).view(1, n + m, d)
+        self.z = dev_bf16(gen.normal_bf16(w.cfg, gen.T_Z, (n + m, d))).view(1, n + m, d)
+        self.bias = dev_bf16(gen.normal_bf16(w.cfg, gen.T_BIAS, (2 * m, d), std=0.1))
+        self.q = dev_bf16(gen.normal_bf16(w.cfg, gen.T_Q, (n * w.H, d))).view(1, n, w.H, d)
+        self.q_idx = dev_bf16(gen.normal_bf16(w.cfg, gen.T_QIDX, (n * w.H_I, w.D_I))).view(1, n, w.H_I, w.D_I)
+        self.w_idx = dev(gen.uniform_f32(w.cfg, gen.T_W, (n * w.H_I,))).view(1, n, w.H_I)
+        self.k_idx = dev_bf16(gen.normal_bf16(w.cfg, gen.T_KIDX, (self.N_cap, w.D_I))).view(1, self.N_cap, w.D_I)
+        self.entries = torch.empty((1, self.N_cap, d), dtype=torch.bfloat16, device="cuda")
+        self.entries[:, :self.N0] = dev_bf16(gen.normal_bf16(w.cfg, gen.T_ENTRIES, (self.N0, d))).view(1, self.N0, d)
+        self.win = torch.empty((1, self.W_cap, d), dtype=torch.bfloat16, device="cuda")
+        self.win[:, :self.Wp] = dev_bf16(gen.normal_bf16(w.cfg, gen.T_WIN, (self.Wp, d))).view(1, self.Wp, d)
+        self.codes, self.scales = ops.csa_quantize_keys(self.k_idx, w.key_format)   # existing keys
+        self.n_ent = torch.tensor([self.N_cap], dtype=torch.int64, device="cuda")
+        self.t = torch.tensor([w.T], dtype=torch.int64, device="cuda")
+        self.win_pos0 = torch.tensor([w.T - self.Wp], dtype=torch.int64, device="cuda")
+        self.sel = torch.empty((1, n, w.topk), dtype=torch.int32, device="cuda")
+        self.out = torch.empty_like(self.q)
+        self.ws_i = ops.index_topk_workspace(1, n, self.N_cap, w.topk)
+        self.ws_a = ops.attend_workspace(1, n, w.H, d, w.topk, w.window)
+        torch.cuda.synchronize()
+        log(f"[{w.name}] inputs ready in {time.time() - t0:.1f}s")
+        # work per chunk: indexer scores over every visible entry, attention over k + W rows
+        vis = np.minimum(self.N_cap, (w.T + np.arange(n) + 1) // m)
+        self.index_flops = float(vis.sum()) * w.H_I * w.D_I * 2
+        self.attend_flops = float(n) * w.H * (w.topk + w.window) * d * 4
+
+    def step(self, i=0):
+        w = self.w
+        ops.csa_compress(self.c, self.z, self.bias, m=w.m, overlap=w.overlap, rope_dim=w.rope_dim, pos0=w.T,
+                         win_rows=True, entries_out=self.entries[:, self.N0:], win_rows_out=self.win[:, self.Wp:])
+        ops.csa_quantize_keys(self.k_idx[:, self.N0:], w.key_format, codes_out=self.codes[:, self.N0:],
+                              scales_out=self.scales[:, self.N0:])
+        ops.csa_index_topk(self.q_idx, self.w_idx, self.codes, self.scales, key_format=w.key_format,
+                           n_entries=self.n_ent, q_pos0=self.t, m=w.m, topk=w.topk, workspace=self.ws_i,
+                           topk_out=self.sel)
+        ops.csa_attend(self.q, self.entries, self.sel, self.win, self.win_pos0, self.t, rope_dim=w.rope_dim,
+                       window=w.window, workspace=self.ws_a, out=self.out)
+
+    def measure(self, steps):
+        for _ in range(3):
+            self.step()
+        torch.cuda.synchronize()
+        ops.timing_enable(True)
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        kt = {}
+        for k in ("compress", "quantize", "index_score", "index_merge", "attend_split", "attend_combine"):
+            ms, cnt = ops.timing_read(k)
+            if cnt:
+                kt[k] = 1000.0 * ms / cnt
+        ops.timing_enable(False)
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.step()
+            with torch.cuda.graph(g, stream=s):
+                self.step()
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / steps
+        w = self.w
+        return {"workload": w.name, "value": w.Sq / sec, "unit": "chunk query-tokens/s", "ms_per_step": 1000 * sec,
+                "kernel_us": kt,
+                "index_mfma": {"bound": "mfma", "dtype": "fp8", "flops": self.index_flops,
+                               "achieved_tflops": self.index_flops / (kt["index_score"] * 1e-6) / 1e12,
+                               "peak_tflops": 5000.0,
+                               "frac": self.index_flops / (kt["index_score"] * 1e-6) / 5.0e15},
+                "attend_mfma": {"bound": "mfma", "dtype": "bf16", "flops": self.attend_flops,
+                                "achieved_tflops": self.attend_flops / (kt["attend_split"] * 1e-6) / 1e12,
+                                "peak_tflops": 2500.0,
+                                "frac": self.attend_flops / (kt["attend_split"] * 1e-6) / 2.5e15}}
+
+
+def compress_leg(steps: int):
+    """The 1M-token HCA compression (8 sequences x 1,048,576 tokens, m = 128, d = 512): HBM-bound
+    streaming of c and z.  The 17 GB of inputs are drawn on the GPU with a seeded torch generator
+    (N(0,1); bias N(0, 0.1)); the parity tests use the host generator on sampled sequences."""
+    w = gen.HCA_DECODE_1M
+    gpu = torch.Generator(device="cuda")
+    gpu.manual_seed(1000 + w.cfg)
+    c = torch.randn((w.B, w.T, w.d), generator=gpu, device="cuda", dtype=torch.bfloat16)
+    z = torch.randn((w.B, w.T, w.d), generator=gpu, device="cuda", dtype=torch.bfloat16)
+    bias = (0.1 * torch.randn((w.m, w.d), generator=gpu, device="cuda")).to(torch.bfloat16)
+    ent = torch.empty((w.B, w.T // w.m, w.d), dtype=torch.bfloat16, device="cuda")
+    run = lambda: ops.csa_compress(c, z, bias, m=w.m, overlap=0, rope_dim=w.rope_dim, pos0=0, entries_out=ent)
+    run()
+    torch.cuda.synchronize()
+    ops.timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    ms, cnt = ops.timing_read("compress")
+    ops.timing_enable(False)
+    kus = 1000.0 * ms / max(cnt, 1)
+    nbytes = 2 * c.numel() * 2 + ent.numel() * 2
+    del c, z
+    torch.cuda.empty_cache()
+    return {"workload": "hca_compress_1m_b8", "value": w.B * w.T / sec, "unit": "tokens/s", "ms_per_step": 1000 * sec,
+            "kernel_us": {"compress": kus},
+            "roofline": {"kernel": "compress", "bound": "hbm", "achieved": nbytes / (kus * 1e-6) / 1e9,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": nbytes / (kus * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                         "algorithmic_bytes": nbytes},
+            "data": "seeded torch generator on the GPU"}
+
+
 # ---- rocprofv3 summaries (text for profiles/) -----------------------------------------------------
 def _short_kernel(name: str) -> str:
     name = name.replace("void ", "").replace("csa::(anonymous namespace)::", "")
@@ -299,7 +427,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--legs", default="main,d128,c32k,hca")
+    ap.add_argument("--legs", default="main,d128,c32k,hca,prefill,compress")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy", "summarize-trace", "summarize-traffic"])
     ap.add_argument("--db", nargs="*", default=[], help="rocprofv3 databases for the summarize modes: one "
                     "kernel-trace db; or FETCH, WRITE, copy-FETCH, copy-WRITE dbs")
@@ -325,6 +453,17 @@ def main():
              "hca": gen.HCA_DECODE_1M}
     results = {}
     for name in legs:
+        if name == "prefill":
+            leg = PrefillLeg(gen.CSA_PREFILL_128K)
+            results[name] = leg.measure(max(3, min(args.steps // 100, 20)))
+            log(json.dumps(results[name]))
+            del leg
+            torch.cuda.empty_cache()
+            continue
+        if name == "compress":
+            results[name] = compress_leg(max(3, min(args.steps // 200, 10)))
+            log(json.dumps(results[name]))
+            continue
         w = table[name]
         leg = Leg(w)
         kt = leg.kernel_times()

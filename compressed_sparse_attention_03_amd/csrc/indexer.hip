@@ -466,20 +466,36 @@ __global__ void __launch_bounds__(NT) index_score_kernel(IndexArgs a) {
   const int b = int(qi / a.Sq), s = int(qi % a.Sq);
   const int tile = a.plan.tile, cand = a.plan.cand;
   const int64_t e_begin = int64_t(tile_id) * tile;
-  const int64_t t = a.q_pos0[b] + s;
-  const int64_t n_vis = min(a.n_entries[b], (t + 1) / a.m);
-  const int vis = int(max(int64_t(0), min(int64_t(tile), n_vis - e_begin)));
   const int64_t out_slot = qi * a.plan.n_tiles + tile_id;
   const int64_t n_q = int64_t(a.B) * a.Sq;
   uint64_t *cand_keys = static_cast<uint64_t *>(a.workspace);
   uint64_t *cand_bound = cand_keys + n_q * a.plan.n_tiles * cand;
   int *cand_count = reinterpret_cast<int *>(cand_bound + n_q * a.plan.n_tiles);
+  const int64_t row0 = int64_t(b) * a.N_cap + e_begin;
+  // The quantised-key loads are range-checked by their buffer resources, so they are issued
+  // before the visible count (which waits on two scalar loads and a division) is known.
+  QueryRaw raw;
+  KeyFrag<FMT> ka[batch_of<FMT>()], kb[batch_of<FMT>()];
+  TileKeys<FMT> tk;
+  if (FMT != 0) {
+    // the query's loads go first (loads complete in issue order), then two batches of keys,
+    // which stream while the query is quantised
+    load_query_raw(static_cast<const uint16_t *>(a.q_idx) + qi * a.H_I * 128, a.w_idx + qi * a.H_I, a.H_I, raw);
+    __builtin_amdgcn_sched_barrier(0);                       // keep the query loads first
+    const int rows = int(min(int64_t(tile), a.N_cap - e_begin));
+    tk = make_tile_keys<FMT>(a.k_codes, a.k_scales, row0, rows, threadIdx.x & 63);
+    const int g_first = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * batch_of<FMT>();
+    load_batch<FMT>(tk, g_first, threadIdx.x & 63, ka);
+    load_batch<FMT>(tk, g_first + (NT / 64) * batch_of<FMT>(), threadIdx.x & 63, kb);
+  }
+  const int64_t t = a.q_pos0[b] + s;
+  const int64_t n_vis = min(a.n_entries[b], (t + 1) / a.m);
+  const int vis = int(max(int64_t(0), min(int64_t(tile), n_vis - e_begin)));
 
   if (vis == 0 && a.scores == nullptr) {                      // nothing visible in this tile
     if (threadIdx.x == 0) { cand_count[out_slot] = 0; cand_bound[out_slot] = 0; }
     return;
   }
-  const int64_t row0 = int64_t(b) * a.N_cap + e_begin;
   if (FMT == 0) {
     float *q_lds = reinterpret_cast<float *>(sh.ql.codes);    // H_I * D_I <= 2048 floats
     const float *qsrc = static_cast<const float *>(a.q_idx) + qi * a.H_I * a.D_I;
@@ -489,17 +505,6 @@ __global__ void __launch_bounds__(NT) index_score_kernel(IndexArgs a) {
     score_tile_f32(q_lds, sh.ql.f, a.H_I, a.D_I, static_cast<const float *>(a.k_codes), row0, tile, vis,
                    sh.scores);
   } else {
-    // the query's loads go first (loads complete in issue order), then two batches of keys, which
-    // stream while the query is quantised
-    QueryRaw raw;
-    load_query_raw(static_cast<const uint16_t *>(a.q_idx) + qi * a.H_I * 128, a.w_idx + qi * a.H_I, a.H_I, raw);
-    __builtin_amdgcn_sched_barrier(0);                         // keep the query loads first
-    const int rows = int(min(int64_t(tile), a.N_cap - e_begin));
-    const TileKeys<FMT> tk = make_tile_keys<FMT>(a.k_codes, a.k_scales, row0, rows, threadIdx.x & 63);
-    KeyFrag<FMT> ka[batch_of<FMT>()], kb[batch_of<FMT>()];
-    const int g_first = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * batch_of<FMT>();
-    load_batch<FMT>(tk, g_first, threadIdx.x & 63, ka);
-    load_batch<FMT>(tk, g_first + (NT / 64) * batch_of<FMT>(), threadIdx.x & 63, kb);
     prep_query_lds<FMT>(raw, a.H_I, sh.ql);
     __syncthreads();
     QueryFrag<NHB> qf;

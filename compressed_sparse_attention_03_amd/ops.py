@@ -119,19 +119,24 @@ def csa_compress(c, z, bias, *, m, overlap, rope_dim, pos0=0, norm_w=None, rope_
     return ent, wr
 
 
-def csa_quantize_keys(x, fmt):
-    """Keys bf16 [..., dim] -> (codes, scales) in the storage format ``fmt`` ("fp8" | "mxfp4")."""
+def csa_quantize_keys(x, fmt, codes_out=None, scales_out=None):
+    """Keys bf16 [..., dim] -> (codes, scales) in the storage format ``fmt`` ("fp8" | "mxfp4").
+    ``codes_out`` / ``scales_out`` (contiguous, of the output shapes) receive the result in place."""
     _dev(x, "x", torch.bfloat16)
     dim = x.shape[-1]
     rows = x.numel() // dim
     f = KEY_FORMATS[fmt]
     lead = tuple(x.shape[:-1])
     if f == KEY_FP8_E4M3:
-        codes = torch.empty(lead + (dim,), dtype=torch.uint8, device=x.device)
-        scales = torch.empty(lead, dtype=torch.float32, device=x.device)
+        cshape, sshape, sdtype = lead + (dim,), lead, torch.float32
     else:
-        codes = torch.empty(lead + (dim // 2,), dtype=torch.uint8, device=x.device)
-        scales = torch.empty(lead + (dim // 32,), dtype=torch.uint8, device=x.device)
+        cshape, sshape, sdtype = lead + (dim // 2,), lead + (dim // 32,), torch.uint8
+    codes = codes_out if codes_out is not None else torch.empty(cshape, dtype=torch.uint8, device=x.device)
+    scales = scales_out if scales_out is not None else torch.empty(sshape, dtype=sdtype, device=x.device)
+    _dev(codes, "codes_out", torch.uint8)
+    _dev(scales, "scales_out", sdtype)
+    if tuple(codes.shape) != cshape or tuple(scales.shape) != sshape:
+        raise ValueError(f"outputs must have shapes {cshape} and {sshape}")
     st = lib().csa_quantize_keys(_ptr(x), rows, dim, f, _ptr(codes), _ptr(scales), _stream())
     _check(st, "csa_quantize_keys")
     return codes, scales

@@ -21,8 +21,9 @@ def _oracle_keys(k_bf16_seq: np.ndarray, fmt: str, chunk=32768):
 
 
 def run_quantised(q_idx, w_idx, k_idx, fmt, m, topk, t_first, n_entries=None, tag="", check_scores=True,
-                  planted=None):
-    """q_idx bf16 [B, Sq, H_I, 128], w_idx f32 [B, Sq, H_I], k_idx bf16 [B, N, 128]."""
+                  planted=None, sample=None):
+    """q_idx bf16 [B, Sq, H_I, 128], w_idx f32 [B, Sq, H_I], k_idx bf16 [B, N, 128].  Every query is
+    computed on the GPU; the ones in ``sample`` (all if None) are checked against the oracle."""
     B, Sq, H_I, D_I = q_idx.shape
     N = k_idx.shape[1]
     n_entries = np.full(B, N) if n_entries is None else np.asarray(n_entries)
@@ -38,7 +39,7 @@ def run_quantised(q_idx, w_idx, k_idx, fmt, m, topk, t_first, n_entries=None, ta
         nv_max = oi.visible_count(t_first[b] + Sq - 1, int(n_entries[b]), m)
         kt = np.zeros((N, D_I))
         kt[:nv_max] = _oracle_keys(k_idx[b, :nv_max], fmt)
-        for s in range(Sq):
+        for s in (range(Sq) if sample is None else sample):
             t = t_first[b] + s
             nv = oi.visible_count(t, int(n_entries[b]), m)
             qt = oi.quantize_query(f64(q_idx[b, s]), fmt)
@@ -130,6 +131,20 @@ def test_csa_decode_128k_full():
 
 def test_csa_decode_1m_mxfp4_planted_full():
     _decode_case(gen.CSA_DECODE_1M)
+
+
+def test_prefill_chunk_full_size_sampled():
+    # 4,096 query tokens at positions 131,072.. over 33,792 entries (the 32,768 existing ones plus
+    # the chunk's 1,024), fp8 keys; every query runs, 12 seeded ones (first and last included) are
+    # checked against the oracle -- scores and selected sets.
+    w = gen.CSA_PREFILL_128K
+    Sq, N = w.Sq, w.N + w.Sq // w.m
+    q_idx = gen.normal_bf16(w.cfg, gen.T_QIDX, (Sq * w.H_I, w.D_I)).reshape(1, Sq, w.H_I, w.D_I)
+    w_idx = gen.uniform_f32(w.cfg, gen.T_W, (Sq * w.H_I,)).reshape(1, Sq, w.H_I)
+    k_idx = gen.normal_bf16(w.cfg, gen.T_KIDX, (N, w.D_I)).reshape(1, N, w.D_I)
+    g = np.random.default_rng(7)
+    sample = sorted(set([0, 1, Sq - 1] + g.integers(0, Sq, 9).tolist()))
+    run_quantised(q_idx, w_idx, k_idx, w.key_format, w.m, w.topk, [w.T], tag="prefill", sample=sample)
 
 
 def test_deterministic_repeat():
