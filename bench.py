@@ -492,7 +492,10 @@ def main():
         log(json.dumps(r))
         leg.free()
         del leg
-    main_name = legs[0]
+    table_legs = [k for k in legs if k in table]
+    if not table_legs:                                           # only side legs were asked for
+        return
+    main_name = table_legs[0]
     m = results[main_name]
     w = table[main_name]
     line = {
@@ -506,7 +509,7 @@ def main():
         "hbm_frac_step": m["hbm_frac_step"],
         "roofline": m["roofline"],
         "kernel_us": m["kernel_us"],
-        "also": [results[k] for k in legs[1:]],
+        "also": [results[k] for k in legs if k != main_name],
     }
     if not args.no_cpu and w.kind == "csa_decode":
         log("timing the CPU oracle ...")

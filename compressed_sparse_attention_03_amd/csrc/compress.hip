@@ -41,6 +41,28 @@ __device__ __forceinline__ void load_row(const uint16_t *p, float (&v)[CPL]) {
   }
 }
 
+// A token row's CPL bf16 values as loaded (CPL >= 2), unpacked at use.
+template <int CPL>
+struct RawRow {
+  uint32_t w[CPL / 2];
+  __device__ __forceinline__ float at(int j) const { return (j & 1) ? bf16hi(w[j >> 1]) : bf16lo(w[j >> 1]); }
+};
+template <int CPL>
+__device__ __forceinline__ void load_raw(const uint16_t *p, RawRow<CPL> &r) {
+  if constexpr (CPL == 2) {
+    r.w[0] = *reinterpret_cast<const uint32_t *>(p);
+  } else if constexpr (CPL == 4) {
+    const uint2 x = *reinterpret_cast<const uint2 *>(p);
+    r.w[0] = x.x; r.w[1] = x.y;
+  } else {
+#pragma unroll
+    for (int q = 0; q < CPL / 8; ++q) {
+      const uint4 x = reinterpret_cast<const uint4 *>(p)[q];
+      r.w[4 * q] = x.x; r.w[4 * q + 1] = x.y; r.w[4 * q + 2] = x.z; r.w[4 * q + 3] = x.w;
+    }
+  }
+}
+
 template <int CPL>
 __device__ __forceinline__ void store_row(uint16_t *p, const float (&v)[CPL]) {
   if constexpr (CPL == 1) {
@@ -96,7 +118,7 @@ __device__ __forceinline__ void norm_rope(float (&v)[CPL], const uint16_t *g, in
   }
 }
 
-template <int CPL>
+template <int CPL, int U>
 __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
   const int d = a.d, m = a.m;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -118,26 +140,67 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
 
   const int per = (nt + 3) >> 2;
   const int k0 = wave * per, k1 = min(nt, k0 + per);
-  for (int k = k0; k < k1; ++k) {
-    float cv[CPL], zv[CPL], bv[CPL];
-    const int64_t row = row_first + k;
-    load_row<CPL>(cb + row * d, cv);
-    load_row<CPL>(zb + row * d, zv);
-    load_row<CPL>(a.bias + int64_t(slot_first + k) * d + lane * CPL, bv);
+  // Tokens go in groups of U (at most the wave's token count): the group's loads are all in
+  // flight together, and the running maximum is updated once per group (one rescale for U
+  // tokens).  Past the wave's last token the loads repeat that token (in bounds) and its logit
+  // is -inf.
+  for (int k = k0; k < k1; k += U) {
+    float cv[U][CPL], zv[U][CPL], bv[U][CPL];
+    if constexpr (CPL >= 2) {
+      RawRow<CPL> rc[U], rz[U], rb[U];                        // as loaded: unpacked per channel below
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kk = min(k + u, k1 - 1);
+        const int64_t row = row_first + kk;
+        load_raw<CPL>(cb + row * d, rc[u]);
+        load_raw<CPL>(zb + row * d, rz[u]);
+        load_raw<CPL>(a.bias + int64_t(slot_first + kk) * d + lane * CPL, rb[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) { cv[u][j] = rc[u].at(j); zv[u][j] = rz[u].at(j); bv[u][j] = rb[u].at(j); }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kk = min(k + u, k1 - 1);
+        const int64_t row = row_first + kk;
+        load_row<CPL>(cb + row * d, cv[u]);
+        load_row<CPL>(zb + row * d, zv[u]);
+        load_row<CPL>(a.bias + int64_t(slot_first + kk) * d + lane * CPL, bv[u]);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-      float l = (zv[j] + bv[j]) * kLog2e;
-      float nm = fmaxf(mx[j], l);
-      float sc = exp2f(mx[j] - nm);                           // 0 on the first token
-      float e = exp2f(l - nm);
-      sm[j] = sm[j] * sc + e;
-      acc[j] = acc[j] * sc + e * cv[j];
+      float l[U], gm = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        l[u] = k + u < k1 ? (zv[u][j] + bv[u][j]) * kLog2e : -INFINITY;
+        gm = fmaxf(gm, l[u]);
+      }
+      const float nm = fmaxf(mx[j], gm);                      // finite: token k is real
+      const float sc = exp2f(mx[j] - nm);                     // 0 on the first group
+      float es = 0.f, ea = 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float e = exp2f(l[u] - nm);
+        es += e;
+        ea += e * cv[u][j];
+      }
+      sm[j] = sm[j] * sc + es;
+      acc[j] = acc[j] * sc + ea;
       mx[j] = nm;
     }
-    if (a.win_rows && k >= own_first) {                       // per-token window row
-      const int64_t tok = i * m + (k - own_first);           // index among the new tokens
-      norm_rope<CPL>(cv, a.norm_w, d, a.rope_dim, a.pos0 + tok, a.log2_base, a.eps, lane);
-      store_row<CPL>(a.win_rows + (int64_t(b) * a.n_new + tok) * d + lane * CPL, cv);
+    if (a.win_rows) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kk = k + u;
+        if (kk < k1 && kk >= own_first) {                      // per-token window row
+          const int64_t tok = i * m + (kk - own_first);       // index among the new tokens
+          norm_rope<CPL>(cv[u], a.norm_w, d, a.rope_dim, a.pos0 + tok, a.log2_base, a.eps, lane);
+          store_row<CPL>(a.win_rows + (int64_t(b) * a.n_new + tok) * d + lane * CPL, cv[u]);
+        }
+      }
     }
   }
 
@@ -169,21 +232,28 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
   store_row<CPL>(a.entries + (int64_t(b) * (a.n_new / m) + i) * d + lane * CPL, p);
 }
 
+template <int CPL>
+hipError_t launch_compress_cpl(const CompressArgs &a, dim3 grid, hipStream_t stream) {
+  // Tokens per wave: 2m with the previous group (every entry but the sequence's first), else m.
+  const int per = ((a.overlap ? 2 * a.m : a.m) + 3) / 4;
+  const dim3 block(256);
+  if (per >= 4) return launch("compress", compress_kernel<CPL, 4>, grid, block, stream, a);
+  if (per >= 2) return launch("compress", compress_kernel<CPL, 2>, grid, block, stream, a);
+  return launch("compress", compress_kernel<CPL, 1>, grid, block, stream, a);
+}
+
 }  // namespace
 
 hipError_t launch_compress(const CompressArgs &a, hipStream_t stream) {
-  hipError_t e = hipSuccess;
-  dim3 grid(unsigned(a.n_new / a.m), unsigned(a.B));
-  dim3 block(256);
+  const dim3 grid(unsigned(a.n_new / a.m), unsigned(a.B));
   switch (a.d / 64) {
-    case 1: e = launch("compress", compress_kernel<1>, grid, block, stream, a); break;
-    case 2: e = launch("compress", compress_kernel<2>, grid, block, stream, a); break;
-    case 4: e = launch("compress", compress_kernel<4>, grid, block, stream, a); break;
-    case 8: e = launch("compress", compress_kernel<8>, grid, block, stream, a); break;
-    case 16: e = launch("compress", compress_kernel<16>, grid, block, stream, a); break;
+    case 1: return launch_compress_cpl<1>(a, grid, stream);
+    case 2: return launch_compress_cpl<2>(a, grid, stream);
+    case 4: return launch_compress_cpl<4>(a, grid, stream);
+    case 8: return launch_compress_cpl<8>(a, grid, stream);
+    case 16: return launch_compress_cpl<16>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
-  return e;
 }
 
 }  // namespace csa
