@@ -19,37 +19,20 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int CPL>
-__device__ __forceinline__ void load_row(const uint16_t *p, float (&v)[CPL]) {
-  if constexpr (CPL == 1) {
-    v[0] = bf16_to_f32(*p);
-  } else if constexpr (CPL == 2) {
-    uint32_t w = *reinterpret_cast<const uint32_t *>(p);
-    v[0] = bf16lo(w); v[1] = bf16hi(w);
-  } else if constexpr (CPL == 4) {
-    uint2 w = *reinterpret_cast<const uint2 *>(p);
-    v[0] = bf16lo(w.x); v[1] = bf16hi(w.x); v[2] = bf16lo(w.y); v[3] = bf16hi(w.y);
-  } else {
-#pragma unroll
-    for (int q = 0; q < CPL / 8; ++q) {
-      uint4 w = reinterpret_cast<const uint4 *>(p)[q];
-      v[8 * q + 0] = bf16lo(w.x); v[8 * q + 1] = bf16hi(w.x);
-      v[8 * q + 2] = bf16lo(w.y); v[8 * q + 3] = bf16hi(w.y);
-      v[8 * q + 4] = bf16lo(w.z); v[8 * q + 5] = bf16hi(w.z);
-      v[8 * q + 6] = bf16lo(w.w); v[8 * q + 7] = bf16hi(w.w);
-    }
-  }
-}
-
-// A token row's CPL bf16 values as loaded (CPL >= 2), unpacked at use.
+// A token row's CPL bf16 values as loaded, unpacked at use.
 template <int CPL>
 struct RawRow {
-  uint32_t w[CPL / 2];
-  __device__ __forceinline__ float at(int j) const { return (j & 1) ? bf16hi(w[j >> 1]) : bf16lo(w[j >> 1]); }
+  uint32_t w[(CPL + 1) / 2];
+  __device__ __forceinline__ float at(int j) const {
+    if constexpr (CPL == 1) return bf16lo(w[0]);
+    return (j & 1) ? bf16hi(w[j >> 1]) : bf16lo(w[j >> 1]);
+  }
 };
 template <int CPL>
 __device__ __forceinline__ void load_raw(const uint16_t *p, RawRow<CPL> &r) {
-  if constexpr (CPL == 2) {
+  if constexpr (CPL == 1) {
+    r.w[0] = *p;
+  } else if constexpr (CPL == 2) {
     r.w[0] = *reinterpret_cast<const uint32_t *>(p);
   } else if constexpr (CPL == 4) {
     const uint2 x = *reinterpret_cast<const uint2 *>(p);
@@ -118,7 +101,7 @@ __device__ __forceinline__ void norm_rope(float (&v)[CPL], const uint16_t *g, in
   }
 }
 
-template <int CPL, int U>
+template <int CPL, int U, bool WIN>
 __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
   const int d = a.d, m = a.m;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -145,37 +128,21 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
   // tokens).  Past the wave's last token the loads repeat that token (in bounds) and its logit
   // is -inf.
   for (int k = k0; k < k1; k += U) {
-    float cv[U][CPL], zv[U][CPL], bv[U][CPL];
-    if constexpr (CPL >= 2) {
-      RawRow<CPL> rc[U], rz[U], rb[U];                        // as loaded: unpacked per channel below
+    RawRow<CPL> rc[U], rz[U], rb[U];                          // as loaded; unpacked at use
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kk = min(k + u, k1 - 1);
-        const int64_t row = row_first + kk;
-        load_raw<CPL>(cb + row * d, rc[u]);
-        load_raw<CPL>(zb + row * d, rz[u]);
-        load_raw<CPL>(a.bias + int64_t(slot_first + kk) * d + lane * CPL, rb[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) { cv[u][j] = rc[u].at(j); zv[u][j] = rz[u].at(j); bv[u][j] = rb[u].at(j); }
-    } else {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kk = min(k + u, k1 - 1);
-        const int64_t row = row_first + kk;
-        load_row<CPL>(cb + row * d, cv[u]);
-        load_row<CPL>(zb + row * d, zv[u]);
-        load_row<CPL>(a.bias + int64_t(slot_first + kk) * d + lane * CPL, bv[u]);
-      }
+    for (int u = 0; u < U; ++u) {
+      const int kk = min(k + u, k1 - 1);
+      const int64_t row = row_first + kk;
+      load_raw<CPL>(cb + row * d, rc[u]);
+      load_raw<CPL>(zb + row * d, rz[u]);
+      load_raw<CPL>(a.bias + int64_t(slot_first + kk) * d + lane * CPL, rb[u]);
     }
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       float l[U], gm = -INFINITY;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        l[u] = k + u < k1 ? (zv[u][j] + bv[u][j]) * kLog2e : -INFINITY;
+        l[u] = k + u < k1 ? (rz[u].at(j) + rb[u].at(j)) * kLog2e : -INFINITY;
         gm = fmaxf(gm, l[u]);
       }
       const float nm = fmaxf(mx[j], gm);                      // finite: token k is real
@@ -185,20 +152,23 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
       for (int u = 0; u < U; ++u) {
         const float e = exp2f(l[u] - nm);
         es += e;
-        ea += e * cv[u][j];
+        ea += e * rc[u].at(j);
       }
       sm[j] = sm[j] * sc + es;
       acc[j] = acc[j] * sc + ea;
       mx[j] = nm;
     }
-    if (a.win_rows) {
+    if constexpr (WIN) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int kk = k + u;
         if (kk < k1 && kk >= own_first) {                      // per-token window row
           const int64_t tok = i * m + (kk - own_first);       // index among the new tokens
-          norm_rope<CPL>(cv[u], a.norm_w, d, a.rope_dim, a.pos0 + tok, a.log2_base, a.eps, lane);
-          store_row<CPL>(a.win_rows + (int64_t(b) * a.n_new + tok) * d + lane * CPL, cv[u]);
+          float cv[CPL];
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) cv[j] = rc[u].at(j);
+          norm_rope<CPL>(cv, a.norm_w, d, a.rope_dim, a.pos0 + tok, a.log2_base, a.eps, lane);
+          store_row<CPL>(a.win_rows + (int64_t(b) * a.n_new + tok) * d + lane * CPL, cv);
         }
       }
     }
@@ -232,14 +202,22 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
   store_row<CPL>(a.entries + (int64_t(b) * (a.n_new / m) + i) * d + lane * CPL, p);
 }
 
-template <int CPL>
-hipError_t launch_compress_cpl(const CompressArgs &a, dim3 grid, hipStream_t stream) {
+template <int CPL, bool WIN>
+hipError_t launch_compress_win(const CompressArgs &a, dim3 grid, hipStream_t stream) {
   // Tokens per wave: 2m with the previous group (every entry but the sequence's first), else m.
   const int per = ((a.overlap ? 2 * a.m : a.m) + 3) / 4;
   const dim3 block(256);
-  if (per >= 4) return launch("compress", compress_kernel<CPL, 4>, grid, block, stream, a);
-  if (per >= 2) return launch("compress", compress_kernel<CPL, 2>, grid, block, stream, a);
-  return launch("compress", compress_kernel<CPL, 1>, grid, block, stream, a);
+  if (per >= 4) return launch("compress", compress_kernel<CPL, 4, WIN>, grid, block, stream, a);
+  if (per >= 2) return launch("compress", compress_kernel<CPL, 2, WIN>, grid, block, stream, a);
+  return launch("compress", compress_kernel<CPL, 1, WIN>, grid, block, stream, a);
+}
+
+// The per-token window rows (normalised and rotated token rows) are a separate instantiation:
+// their code holds many registers even when not taken, which would cost the pooling occupancy.
+template <int CPL>
+hipError_t launch_compress_cpl(const CompressArgs &a, dim3 grid, hipStream_t stream) {
+  return a.win_rows ? launch_compress_win<CPL, true>(a, grid, stream)
+                    : launch_compress_win<CPL, false>(a, grid, stream);
 }
 
 }  // namespace
