@@ -207,6 +207,7 @@ hipError_t launch_compress_win(const CompressArgs &a, dim3 grid, hipStream_t str
   // Tokens per wave: 2m with the previous group (every entry but the sequence's first), else m.
   const int per = ((a.overlap ? 2 * a.m : a.m) + 3) / 4;
   const dim3 block(256);
+  if (per >= 8) return launch("compress", compress_kernel<CPL, 8, WIN>, grid, block, stream, a);
   if (per >= 4) return launch("compress", compress_kernel<CPL, 4, WIN>, grid, block, stream, a);
   if (per >= 2) return launch("compress", compress_kernel<CPL, 2, WIN>, grid, block, stream, a);
   return launch("compress", compress_kernel<CPL, 1, WIN>, grid, block, stream, a);
