@@ -8,17 +8,18 @@
 // section 2.3: shared-KV multi-query attention; RMSNorm on the query heads before core attention.
 // dev.to "Two Compression Strategies": partial RoPE.
 //
-// Work split (split-K decode): workgroup = (query, block of 16 heads, slice of the row list),
-// 4 waves.  A wave takes 16 rows at a time:
-//   S^T[16 rows x 16 heads] = K[16 x D] * Q^T      v_mfma_f32_16x16x32_bf16, rows as A operand
-//                                                   (one 16-byte load per lane per 32 channels)
-//   V^T fragments                                  v_mfma_f32_16x16x16_bf16 against an identity
-//                                                   fragment (exact: bf16 * 1 in fp32)
-//   O[16 heads x D] += P * V                       v_mfma_f32_16x16x16_bf16, P straight from the
-//                                                   S^T accumulator layout
-// with an online softmax in the exp2 domain (the softmax scale and log2(e) are folded into q).
-// The four waves' (max, sum, O) states merge through LDS; the slice writes a normalised fp32
-// partial and its log2-sum-exp, and a combine kernel merges the slices in a fixed order.
+// Work split (split-K decode): workgroup = (query, block of 16 heads, slice of the row list).  Its
+// NW = D / 128 waves split the channels (wave w owns 128 of them in q, in every row and in O) and
+// take the slice's 16-row chunks together:
+//   S^T partial [16 rows x 16 heads] = K_w Q_w^T    v_mfma_f32_16x16x32_bf16, the rows' channel
+//                                                   slice as A operand (16-byte loads per lane)
+//   S^T = sum over the waves                        through LDS, one barrier per pair of chunks
+//   online softmax in the exp2 domain               every wave alike (the softmax scale and
+//                                                   log2(e) are folded into q)
+//   O_w^T [128 ch x 16 heads] += V_w^T P^T          v_mfma_f32_16x16x16_bf16, V^T fragments from a
+//                                                   transposing LDS read of the staged rows
+// Each wave writes its channels of the slice's normalised fp32 partial; wave 0 writes the slice's
+// log2-sum-exp, and a combine kernel merges the slices in a fixed order.
 #include "common.h"
 #include "internal.h"
 
@@ -48,8 +49,13 @@ __device__ __forceinline__ v4s pack4(float a, float b, float c, float d) {
   return p.s;
 }
 
+// Element e (0..7) of eight packed bf16.
+__device__ __forceinline__ float elem8(const uint4 &w, int e) {
+  const uint32_t x = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
+  return (e & 1) ? bf16hi(x) : bf16lo(x);
+}
+
 constexpr int kMaxRowsPerSplit = 2048;
-constexpr float kRescaleSlack = 8.0f;     // log2 units: the running max may lag the true max by 2^8
 
 // Row code of slot `ri` of the query's row list: an entry index (< N_cap), N_cap + window row, or
 // -1 when the slot is empty.
@@ -111,32 +117,38 @@ __device__ __forceinline__ float group4_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-constexpr int kWaves = 4;                  // waves per workgroup; each takes whole 16-row chunks
+// Channel split: a workgroup has NW = D / C waves and wave w owns the channels [C w, C w + C) of
+// q, of every row and of O.  All waves take every chunk of the workgroup's slice together.
 template <int D>
-constexpr int ring_of() { return D == 512 ? 2 : 4; }   // chunks in flight per wave (registers)
+constexpr int slice_of() { return D >= 128 ? 128 : D; }
+template <int D>
+constexpr int waves_of() { return D / slice_of<D>(); }
+// The launch bound asks for two workgroups per CU (at D = 512: 178 VGPRs, no spills); the split
+// planner counts on that.
+constexpr int kRing = 4;                   // chunks in flight per wave; chunks go in pairs
 
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 template <int D>
-__global__ void __launch_bounds__(64 * kWaves) attend_split_kernel(AttendArgs a, int64_t n_queries) {
-  constexpr int NT = 64 * kWaves;
-  constexpr int NS = D / 32;          // 32-channel steps of a row (QK^T)
-  constexpr int NB = D / 16;          // 16-channel blocks of O (PV)
+__global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(AttendArgs a, int64_t n_queries) {
+  constexpr int C = slice_of<D>(), NW = waves_of<D>(), NT = 64 * NW;
+  constexpr int NS = C / 32;          // 32-channel steps of the wave's slice (QK^T)
+  constexpr int NB = C / 16;          // 16-channel blocks of the wave's O^T (PV)
   constexpr int QCH = D / 32;         // prologue: threads per head (32 channels each)
-  constexpr int RING = ring_of<D>();
-  constexpr int RS = 2 * D + 16;      // staging row stride in bytes: 16 B of padding per row, so
+  constexpr int RING = kRing;
+  constexpr int RS = 2 * C + 16;      // staging row stride in bytes: 16 B of padding per row, so
                                       // the rows one wide LDS access touches fall in different banks
   constexpr int QS = D + 8;           // q^ row stride (bf16), padded likewise
-  constexpr int HD = D / 2;           // the merge runs over two halves of the channels
-  constexpr int OS = HD + 4;          // merge row stride (fp32)
-  // LDS: per-wave staging of the current chunk (for the transposing V reads), q^, row codes.
-  // After the row loop the staging area holds the four waves' scaled O, half the channels at a time.
-  __shared__ __align__(16) unsigned char s_stage[kWaves * 16 * RS];
-  __shared__ __align__(16) uint16_t s_q[16 * QS];
+  constexpr int BUF = (16 * QS * 2 > NW * 32 * RS) ? 16 * QS * 2 : NW * 32 * RS;
+  static_assert(QCH * 16 <= NT, "the q prologue needs one thread per 32 channels of a head");
+  // LDS: q^ during the prologue, then (same bytes) every wave's staging of its current pair of
+  // chunks (their row slices) for the transposing V reads; the waves' S partials (two pairs of chunks, double-buffered); row
+  // codes; rotary angles.
+  __shared__ __align__(16) unsigned char s_buf[BUF];
+  __shared__ __align__(16) float4 s_part[2][2][NW][64];
   __shared__ int s_row[kMaxRowsPerSplit];
   __shared__ float s_cs[256], s_sn[256];
-  __shared__ float s_m[kWaves][16], s_l[kWaves][16];
-  static_assert(kWaves * 16 * OS * 4 <= kWaves * 16 * RS, "merge buffers must fit in the staging area");
+  uint16_t *s_q = reinterpret_cast<uint16_t *>(s_buf);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
@@ -151,7 +163,6 @@ __global__ void __launch_bounds__(64 * kWaves) attend_split_kernel(AttendArgs a,
   const int64_t r1 = min(int64_t(a.plan.n_rows), r0 + a.plan.rows_per_split);
   const int nr = int(r1 - r0);
   const int n_chunks = (nr + 15) >> 4;
-  const int my_chunks = n_chunks > wave ? (n_chunks - wave + kWaves - 1) / kWaves : 0;   // chunks wave, wave+4, ...
 
   // ---- prologue.  The raw q chunk (and norm weights) of this thread are loaded first: loads
   // complete in issue order, so anything issued later (the row prefetch) does not delay them.
@@ -171,19 +182,19 @@ __global__ void __launch_bounds__(64 * kWaves) attend_split_kernel(AttendArgs a,
   for (int i = tid; i < nr; i += NT) s_row[i] = row_code(a, qi, b, t, n_vis, r0 + i);
   const int npairs = a.rope_dim / 2;
   for (int u = tid; u < npairs; u += NT) rope_cos_sin(t, u, a.rope_dim, a.log2_base, &s_cs[u], &s_sn[u]);
-  const uint16_t *ent_b = a.entries + int64_t(b) * a.N_cap * D;
-  const uint16_t *win_b = a.win_rows + int64_t(b) * a.W_cap * D;
-  __syncthreads();
+  const uint16_t *ent_b = a.entries + int64_t(b) * a.N_cap * D + C * wave;
+  const uint16_t *win_b = a.win_rows + int64_t(b) * a.W_cap * D + C * wave;
+  lds_barrier();
 
-  // ring of row fragments: lane (r, g) holds row r of the chunk, channels 32s + 8g .. +7 for every s
+  // ring of row-slice fragments: lane (r, g) holds row r of the chunk, channels C w + 32 s + 8 g .. +7
   Frag8 ring[RING][NS];
   int codes[RING];
   // Loads are unconditional (an empty slot reads entry row 0, which exists and is finite; its
-  // softmax weight is exactly 0): branch-free code lets the compiler wait only for the chunk in use
-  // instead of every outstanding load.
-  auto issue = [&](int j, int slot) {            // this wave's j-th chunk
-    const int i = (wave + kWaves * j) * 16 + r;
-    const int code = (j < my_chunks && i < nr) ? s_row[i] : -1;
+  // softmax weight is exactly 0): every path through the loop issues the same loads in the same
+  // order, so the wait before a chunk covers that chunk's slot only.
+  auto issue = [&](int j, int slot) {            // the slice's j-th chunk
+    const int i = j * 16 + r;
+    const int code = (j < n_chunks && i < nr) ? s_row[i] : -1;
     codes[slot] = code;
     const uint16_t *rp = code < 0 ? ent_b
                                   : (code < a.N_cap ? ent_b + int64_t(code) * D : win_b + (int64_t(code) - a.N_cap) * D);
@@ -193,206 +204,182 @@ __global__ void __launch_bounds__(64 * kWaves) attend_split_kernel(AttendArgs a,
 #pragma unroll
   for (int j = 0; j < RING; ++j) issue(j, j);
 
-  // q^ = RoPE(RMSNorm(q)) * scale * log2(e) for the 16 heads, into LDS
+  // q^ = RoPE(RMSNorm(q)) * scale * log2(e) for the 16 heads, into LDS, 8 channels at a time
+  // (few registers: the row loads above are in flight meanwhile)
   if (qthread) {
-    const int h = qh, c = qc;
-    float v[32];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint4 w = qraw[k];
-      v[8 * k + 0] = bf16lo(w.x); v[8 * k + 1] = bf16hi(w.x); v[8 * k + 2] = bf16lo(w.y);
-      v[8 * k + 3] = bf16hi(w.y); v[8 * k + 4] = bf16lo(w.z); v[8 * k + 5] = bf16hi(w.z);
-      v[8 * k + 6] = bf16lo(w.w); v[8 * k + 7] = bf16hi(w.w);
-    }
-    if (qhead >= a.H) {
-#pragma unroll
-      for (int k = 0; k < 32; ++k) v[k] = 0.f;
-    }
     float ss = 0.f;
 #pragma unroll
-    for (int k = 0; k < 32; ++k) ss += v[k] * v[k];
-#pragma unroll
-    for (int o = 1; o < QCH; o <<= 1) ss += __shfl_xor(ss, o, 64);   // the head's QCH threads
-    const float inv = rsqrtf(ss / float(D) + a.eps) * a.scale_log2;
-    float gw[32];
-    const bool has_w = a.q_norm_w != nullptr;
-#pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint4 w = wraw[k];
-      gw[8 * k + 0] = bf16lo(w.x); gw[8 * k + 1] = bf16hi(w.x); gw[8 * k + 2] = bf16lo(w.y);
-      gw[8 * k + 3] = bf16hi(w.y); gw[8 * k + 4] = bf16lo(w.z); gw[8 * k + 5] = bf16hi(w.z);
-      gw[8 * k + 6] = bf16lo(w.w); gw[8 * k + 7] = bf16hi(w.w);
-    }
-    if (!has_w) {
 #pragma unroll
-      for (int k = 0; k < 32; ++k) gw[k] = 1.0f;
-    }
-#pragma unroll
-    for (int k = 0; k < 32; ++k) v[k] *= inv * gw[k];
-    const int rope0 = D - a.rope_dim;
-    if (32 * c + 32 > rope0) {
-#pragma unroll
-      for (int k = 0; k < 32; k += 2) {
-        const int ch = 32 * c + k;
-        if (ch >= rope0) {
-          const int u = (ch - rope0) >> 1;
-          const float cs = s_cs[u], sn = s_sn[u], x0 = v[k], x1 = v[k + 1];
-          v[k] = x0 * cs - x1 * sn;
-          v[k + 1] = x0 * sn + x1 * cs;
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float x = elem8(qraw[k], e);
+        ss += x * x;
       }
     }
-    uint4 *dst = reinterpret_cast<uint4 *>(s_q + h * QS + 32 * c);
+#pragma unroll
+    for (int o = 1; o < QCH; o <<= 1) ss += __shfl_xor(ss, o, 64);   // the head's QCH threads
+    const float inv = qhead < a.H ? rsqrtf(ss / float(D) + a.eps) * a.scale_log2 : 0.f;
+    const bool has_w = a.q_norm_w != nullptr;
+    const int rope0 = D - a.rope_dim;
+    uint4 *dst = reinterpret_cast<uint4 *>(s_q + qh * QS + 32 * qc);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = elem8(qraw[k], e) * inv * (has_w ? elem8(wraw[k], e) : 1.0f);
+      const int ch0 = 32 * qc + 8 * k;
+      if (ch0 + 8 > rope0) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int ch = ch0 + e;
+          if (ch >= rope0) {
+            const int u = (ch - rope0) >> 1;
+            const float cs = s_cs[u], sn = s_sn[u], x0 = v[e], x1 = v[e + 1];
+            v[e] = x0 * cs - x1 * sn;
+            v[e + 1] = x0 * sn + x1 * cs;
+          }
+        }
+      }
       Pack4 lo, hi;
-      lo.s = pack4(v[8 * k], v[8 * k + 1], v[8 * k + 2], v[8 * k + 3]);
-      hi.s = pack4(v[8 * k + 4], v[8 * k + 5], v[8 * k + 6], v[8 * k + 7]);
+      lo.s = pack4(v[0], v[1], v[2], v[3]);
+      hi.s = pack4(v[4], v[5], v[6], v[7]);
       dst[k] = make_uint4(uint32_t(uint16_t(lo.s[0])) | (uint32_t(uint16_t(lo.s[1])) << 16),
                           uint32_t(uint16_t(lo.s[2])) | (uint32_t(uint16_t(lo.s[3])) << 16),
                           uint32_t(uint16_t(hi.s[0])) | (uint32_t(uint16_t(hi.s[1])) << 16),
                           uint32_t(uint16_t(hi.s[2])) | (uint32_t(uint16_t(hi.s[3])) << 16));
     }
   }
-  __syncthreads();
+  lds_barrier();
+  // this wave's q^ slice as B operands (lane (r, g): head r, channels C w + 32 s + 8 g .. +7).  The
+  // staging area reuses these bytes: every wave's reads complete before any wave stages rows.
+  Frag8 qf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) qf[s].u = *reinterpret_cast<const uint4 *>(s_q + r * QS + C * wave + 32 * s + 8 * g);
+  lds_barrier();
 
-  // O^T block nb (O^T = V^T P^T): lane (r, g) element v = head r, channel 16 nb + 4g + v, so a
-  // lane owns one head: the rescale is lane-local and the merge writes 16 B per block
+  // O^T block nb (O^T = V^T P^T): lane (r, g) element v = head r, channel C w + 16 nb + 4 g + v
   v4f o[NB];
 #pragma unroll
   for (int k = 0; k < NB; ++k) o[k] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;           // of head r (same in the four lanes of head r)
-  unsigned char *stage = s_stage + wave * 16 * RS;
+  float m_run = -INFINITY, l_run = 0.f;           // of head r; the same in every wave
+  unsigned char *stage = s_buf + wave * 32 * RS;
 
-  // One chunk of 16 rows: S^T = K q^T over all D channels (K from registers, q^ from LDS), online
-  // softmax, then the rows go to the wave's staging area once and O += P V takes V^T fragments
-  // from it with the transposing LDS read.  `slot` is a compile-time ring position.
-  auto chunk = [&](int slot) {
-    const uint64_t vmask = __ballot(codes[slot] >= 0);
-    // four independent accumulation chains over the channel steps, summed at the end
-    constexpr int NCH = NS < 4 ? NS : 4;
-    v4f sp[NCH];
+  // Two chunks (32 rows) per step, straight-line code.  Row order within the step: k = 8g + v is
+  // row 4g + v of the first chunk for v < 4 and row 4g + v - 4 of the second for v >= 4, so the
+  // S^T accumulator layout (lane (r, g): rows 4g..4g+3 of head r) gives the P^T operand directly.
+  //   S^T partial = K_slice q^_slice^T over the wave's channels (rows as A operand, q^ as B),
+  //   summed over the waves through LDS in wave order; then one running-max update and rescale
+  //   for the 32 rows (every wave runs the same arithmetic on the same logits, so m and l agree
+  //   across the waves); the rows go to the wave's staging area and two transposing LDS reads give
+  //   the A operand V^T[16 channels x 32 rows] of O^T += V^T P^T.
+  auto pair = [&](int slot0, int parity) __attribute__((always_inline)) {
+    // The V^T fragments do not depend on P: the rows are staged and read back first, so the LDS
+    // round trip overlaps the S^T products, the exchange and the softmax.
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) sp[c] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 2; ++c) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      Frag8 qf;
-      qf.u = *reinterpret_cast<const uint4 *>(s_q + r * QS + 32 * s + 8 * g);
-      sp[s % NCH] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[slot][s].b, qf.b, sp[s % NCH], 0, 0, 0);
+      for (int s = 0; s < NS; ++s)
+        *reinterpret_cast<uint4 *>(stage + (16 * c + r) * RS + (32 * s + 8 * g) * 2) = ring[slot0 + c][s].u;
     }
-    v4f st = sp[0];
-#pragma unroll
-    for (int c = 1; c < NCH; ++c) { st[0] += sp[c][0]; st[1] += sp[c][1]; st[2] += sp[c][2]; st[3] += sp[c][3]; }
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-      *reinterpret_cast<uint4 *>(stage + r * RS + (32 * s + 8 * g) * 2) = ring[slot][s].u;
-    // st[v] = logit of row 4g+v for head r
-    float sv[4], cmax = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      sv[v] = ((vmask >> (4 * g + v)) & 1) ? st[v] : -INFINITY;
-      cmax = fmaxf(cmax, sv[v]);
-    }
-    cmax = group4_max(cmax);
-    // lazy running max: rescale only when some head's max grew past the slack
-    const bool grow = cmax > m_run + kRescaleSlack || (m_run == -INFINITY && cmax != -INFINITY);
-    if (__any(grow)) {
-      const bool empty = __all(m_run == -INFINITY);        // nothing accumulated yet: O is zero
-      const float m_new = fmaxf(m_run, cmax);
-      const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-      l_run *= alpha;
-      m_run = m_new;
-      if (!empty) {
-#pragma unroll
-        for (int k = 0; k < NB; ++k) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) o[k][v] *= alpha;
-        }
-      }
-    }
-    float p[4], psum = 0.f;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      p[v] = (sv[v] == -INFINITY) ? 0.f : exp2f(sv[v] - m_run);
-      psum += p[v];
-    }
-    l_run += group4_sum(psum);
-    const v4s pf = pack4(p[0], p[1], p[2], p[3]);
     // V^T fragment of block nb: lane (n, g) reads row 4g + n/4, channels 16 nb + 4(n%4) .. +3;
-    // the transposing read hands lane (n, g) rows 4g .. 4g+3 of channel 16 nb + n -- the A
-    // operand (channel n, rows 4g..) of O^T += V^T P^T, with P^T as B (lane (r, g): head r, rows 4g..)
+    // the transposing read hands lane (n, g) rows 4g .. 4g+3 of channel 16 nb + n
     const unsigned char *vbase = stage + (4 * g + (r >> 2)) * RS + 8 * (r & 3);
+    Frag8 vt[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const v4s vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vbase + 32 * nb));
-      o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pf, o[nb], 0, 0, 0);
+      vt[nb].h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vbase + 32 * nb));
+      vt[nb].h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vbase + 16 * RS + 32 * nb));
     }
-  };
-  for (int j0 = 0; j0 < my_chunks; j0 += RING) {
+    v4f sp[2];
 #pragma unroll
-    for (int k = 0; k < RING; ++k) {
-      if (j0 + k < my_chunks) {
-        chunk(k);
-        issue(j0 + k + RING, k);     // refill the slot
+    for (int c = 0; c < 2; ++c) {
+      sp[c] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        sp[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[slot0 + c][s].b, qf[s].b, sp[c], 0, 0, 0);
+    }
+    if constexpr (NW > 1) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) s_part[parity][c][wave][lane] = make_float4(sp[c][0], sp[c][1], sp[c][2], sp[c][3]);
+      lds_barrier();
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float4 x = s_part[parity][c][0][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+          const float4 y = s_part[parity][c][w][lane];
+          x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+        }
+        sp[c] = v4f{x.x, x.y, x.z, x.w};
       }
+    }
+    const uint64_t vm0 = __ballot(codes[slot0] >= 0), vm1 = __ballot(codes[slot0 + 1] >= 0);
+    float sv[8], cmax = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      sv[v] = ((vm0 >> (4 * g + v)) & 1) ? sp[0][v] : -INFINITY;
+      sv[4 + v] = ((vm1 >> (4 * g + v)) & 1) ? sp[1][v] : -INFINITY;
+    }
+#pragma unroll
+    for (int v = 0; v < 8; ++v) cmax = fmaxf(cmax, sv[v]);
+    cmax = group4_max(cmax);
+    // v_exp_f32 directly: every argument is <= 0, tiny results may flush to zero (they are below
+    // 2^-126 of the head's largest weight), and exp2(-inf) = 0 masks the empty rows
+    const float m_new = fmaxf(m_run, cmax);
+    const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;      // no valid row yet: every sv is -inf
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      p[v] = __builtin_amdgcn_exp2f(sv[v] - m_use);
+      psum += p[v];
+    }
+    l_run = l_run * alpha + group4_sum(psum);
+    m_run = m_new;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[k][v] *= alpha;
+    }
+    Frag8 pf;
+    pf.h[0] = pack4(p[0], p[1], p[2], p[3]);
+    pf.h[1] = pack4(p[4], p[5], p[6], p[7]);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[nb].b, pf.b, o[nb], 0, 0, 0);
+  };
+  // The barrier inside a pair is reached by every wave (n_chunks is the same for all of them); the
+  // S partial buffers alternate between consecutive pairs, so one barrier per pair suffices.  An
+  // empty second chunk (odd chunk count) reads the dummy row and is masked out.
+  for (int j0 = 0; j0 < n_chunks; j0 += RING) {
+#pragma unroll
+    for (int h = 0; h < RING / 2; ++h) {
+      if (j0 + 2 * h < n_chunks) pair(2 * h, h & 1);
+      issue(j0 + 2 * h + RING, 2 * h);           // refill the pair's slots
+      issue(j0 + 2 * h + 1 + RING, 2 * h + 1);
     }
   }
 
-  // ---- merge the four waves' (m, l, O) states, half of the channels at a time -----------------
-  if (g == 0) { s_m[wave][r] = m_run; s_l[wave][r] = l_run; }
-  __syncthreads();                                   // every wave is done with its staging area
-  // head r's merged maximum, sum and this wave's share (every lane of head r computes the same)
-  float M = -INFINITY;
+  // ---- epilogue: this wave's channels of O / l, and the slice's log2-sum-exp ------------------
+  const int gh = hb * 16 + r;
+  if (gh < a.H) {
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+    const int c0 = C * wave + 4 * g;
+    if (a.plan.n_splits == 1) {
+      uint16_t *dst = a.out + (qi * a.H + gh) * D + c0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
-  float L = 0.f;
+      for (int nb = 0; nb < NB; ++nb)
+        *reinterpret_cast<v4s *>(dst + 16 * nb) = pack4(o[nb][0] * inv, o[nb][1] * inv, o[nb][2] * inv, o[nb][3] * inv);
+      if (a.lse && wave == 0 && g == 0)
+        a.lse[qi * a.H + gh] = l_run > 0.f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+    } else {
+      float *po = static_cast<float *>(a.workspace);
+      float *plse = po + n_queries * a.H * a.plan.n_splits * D;
+      float *dst = po + ((qi * a.H + gh) * a.plan.n_splits + split) * int64_t(D) + c0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) L += s_m[w][r] == -INFINITY ? 0.f : s_l[w][r] * exp2f(s_m[w][r] - M);
-  const float share = (s_m[wave][r] == -INFINITY || !(L > 0.f)) ? 0.f : exp2f(s_m[wave][r] - M) / L;
-  const bool direct = a.plan.n_splits == 1;
-  float *po = static_cast<float *>(a.workspace);
-  float *plse = po + n_queries * a.H * a.plan.n_splits * D;
-  float *mb = reinterpret_cast<float *>(s_stage);
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    // each wave writes its O^T blocks of this half, scaled by its share, as [head][channel]
-    float *mine = mb + wave * 16 * OS;
-#pragma unroll
-    for (int k = 0; k < NB / 2; ++k) {
-      const v4f x = o[half * (NB / 2) + k];
-      *reinterpret_cast<float4 *>(mine + r * OS + 16 * k + 4 * g) =
-          make_float4(x[0] * share, x[1] * share, x[2] * share, x[3] * share);
-    }
-    __syncthreads();
-    // every thread sums four consecutive channels of one head over the waves and writes them
-    constexpr int Q4 = HD / 4;
-    for (int e = tid; e < 16 * Q4; e += NT) {
-      const int h = e / Q4, c4 = (e - h * Q4) * 4;
-      const int gh = hb * 16 + h;
-      if (gh >= a.H) continue;
-      float4 acc = *reinterpret_cast<const float4 *>(mb + h * OS + c4);
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) {
-        const float4 x = *reinterpret_cast<const float4 *>(mb + (w * 16 + h) * OS + c4);
-        acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
-      }
-      const int ch = half * HD + c4;
-      if (direct)
-        *reinterpret_cast<v4s *>(a.out + (qi * a.H + gh) * D + ch) = pack4(acc.x, acc.y, acc.z, acc.w);
-      else
-        *reinterpret_cast<float4 *>(po + ((qi * a.H + gh) * a.plan.n_splits + split) * int64_t(D) + ch) = acc;
-    }
-    if (half == 0) __syncthreads();
-  }
-  if (wave == 0 && g == 0) {
-    const int gh = hb * 16 + r;
-    if (gh < a.H) {
-      const float lse2 = L > 0.f ? M + log2f(L) : -INFINITY;
-      if (direct) {
-        if (a.lse) a.lse[qi * a.H + gh] = lse2 * 0.6931471805599453f;
-      } else {
-        plse[(qi * a.H + gh) * a.plan.n_splits + split] = lse2;
-      }
+      for (int nb = 0; nb < NB; ++nb)
+        *reinterpret_cast<float4 *>(dst + 16 * nb) = make_float4(o[nb][0] * inv, o[nb][1] * inv, o[nb][2] * inv, o[nb][3] * inv);
+      if (wave == 0 && g == 0)
+        plse[(qi * a.H + gh) * a.plan.n_splits + split] = l_run > 0.f ? m_run + log2f(l_run) : -INFINITY;
     }
   }
 }
@@ -442,20 +429,21 @@ AttendPlan plan_attend(int64_t n_queries, int H, int64_t n_sel, int window, int 
   AttendPlan p;
   p.n_hb = (H + 15) / 16;
   p.n_rows = int(n_sel + window);
-  // A split is a multiple of 64 rows (four waves x 16-row chunks).  Aim at two chunks per wave,
-  // but no more splits than keep the grid within one round of resident workgroups (one per CU at
-  // D = 512, two below); every split costs a partial [16 x D] fp32 write and read.
+  // A split is a multiple of 32 rows (a pair of 16-row chunks).  Aim at 128 rows per split, but
+  // no more splits than keep the grid within one round of resident workgroups (two per CU); every
+  // split costs a partial [16 x D] fp32 write and read.
   const int64_t units = n_queries * p.n_hb;
-  const int64_t resident = D == 512 ? 256 : 512;
+  const int64_t resident = 2 * 256;
   int64_t splits = (p.n_rows + 127) / 128;
   const int64_t by_grid = resident / units;
   if (splits > by_grid) splits = by_grid;
   if (splits < 1) splits = 1;
   int64_t rps = (p.n_rows + splits - 1) / splits;
-  rps = (rps + 63) / 64 * 64;
+  rps = (rps + 31) / 32 * 32;
   if (rps > kMaxRowsPerSplit) rps = kMaxRowsPerSplit;
   p.rows_per_split = int(rps);
   p.n_splits = int((p.n_rows + rps - 1) / rps);
+  (void)D;
   return p;
 }
 
@@ -471,10 +459,10 @@ hipError_t launch_attend(const AttendArgs &a, hipStream_t stream) {
   const int64_t pairs = nq * a.plan.n_splits;
   dim3 grid(unsigned(((pairs + 7) / 8) * 8 * a.plan.n_hb));
   switch (a.D) {
-    case 64: e = launch("attend_split", attend_split_kernel<64>, grid, dim3(64 * kWaves), stream, a, nq); break;
-    case 128: e = launch("attend_split", attend_split_kernel<128>, grid, dim3(64 * kWaves), stream, a, nq); break;
-    case 256: e = launch("attend_split", attend_split_kernel<256>, grid, dim3(64 * kWaves), stream, a, nq); break;
-    case 512: e = launch("attend_split", attend_split_kernel<512>, grid, dim3(64 * kWaves), stream, a, nq); break;
+    case 64: e = launch("attend_split", attend_split_kernel<64>, grid, dim3(64 * waves_of<64>()), stream, a, nq); break;
+    case 128: e = launch("attend_split", attend_split_kernel<128>, grid, dim3(64 * waves_of<128>()), stream, a, nq); break;
+    case 256: e = launch("attend_split", attend_split_kernel<256>, grid, dim3(64 * waves_of<256>()), stream, a, nq); break;
+    case 512: e = launch("attend_split", attend_split_kernel<512>, grid, dim3(64 * waves_of<512>()), stream, a, nq); break;
     default: return hipErrorInvalidValue;
   }
   return e;

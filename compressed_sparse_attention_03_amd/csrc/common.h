@@ -8,6 +8,17 @@
 
 namespace csa {
 
+// Workgroup barrier that orders LDS only: the LDS accesses of every wave before it are complete
+// and visible to every wave after it.  Outstanding global loads and stores are not waited for
+// (the workgroup-scope fences of __syncthreads wait for them on this target).  Every barrier in
+// these kernels orders LDS traffic only: no workgroup reads global memory another of its waves
+// wrote in the same launch.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---- bf16 storage ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -181,7 +181,7 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
     s_state[1][wave][lane * CPL + j] = sm[j];
     s_state[2][wave][lane * CPL + j] = acc[j];
   }
-  __syncthreads();
+  lds_barrier();
   if (wave != 0) return;
   float p[CPL];
 #pragma unroll

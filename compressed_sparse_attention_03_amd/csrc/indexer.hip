@@ -339,7 +339,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int *s_tmp, int &total) {
   constexpr int NW = NT / 64;
   int incl = wave_incl_scan(v, lane);
   if (lane == 63) s_tmp[wave] = incl;
-  __syncthreads();
+  lds_barrier();
   int base = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -347,7 +347,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int *s_tmp, int &total) {
     base += (w < wave) ? x : 0;
     tot += x;
   }
-  __syncthreads();
+  lds_barrier();
   total = tot;
   return base + incl - v;
 }
@@ -380,11 +380,11 @@ __device__ uint64_t block_cut(const uint64_t (&keys)[KPT], int need, int keep_mi
   mn = wave_minmax_u64<true>(mn);
   mx = wave_minmax_u64<false>(mx);
   if (lane == 0) { sl.u64[wave] = mn; sl.u64[8 + wave] = mx; }
-  __syncthreads();
+  lds_barrier();
   mn = ~uint64_t(0); mx = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) { mn = umin64(mn, sl.u64[w]); mx = umax64(mx, sl.u64[8 + w]); }
-  if (mn == mx) { __syncthreads(); return mn; }
+  if (mn == mx) { lds_barrier(); return mn; }
   int hi = 63 - __clzll(mn ^ mx);                 // highest bit where keys differ
   uint64_t mask = hi == 63 ? 0 : ~((uint64_t(2) << hi) - 1);
   uint64_t prefix = mn & mask;
@@ -397,7 +397,7 @@ __device__ uint64_t block_cut(const uint64_t (&keys)[KPT], int need, int keep_mi
 #pragma unroll
     for (int k = 0; k < KPT; ++k)
       if (keys[k] != 0 && (keys[k] & mask) == prefix) atomicAdd(&H[(keys[k] >> shift) & dmask], 1u);
-    __syncthreads();
+    lds_barrier();
     // every wave finds the digit holding rank `need`, scanning bins from the top
     const uint4 c4 = *reinterpret_cast<const uint4 *>(&H[252 - 4 * lane]);
     const int c[4] = {int(c4.w), int(c4.z), int(c4.y), int(c4.x)};   // bins 255-4l .. 252-4l
@@ -418,7 +418,7 @@ __device__ uint64_t block_cut(const uint64_t (&keys)[KPT], int need, int keep_mi
     for (int i = tid; i < 256; i += NT) Hn[i] = 0;
     if (bucket != need - above && got + above >= keep_min) {
       // enough keys lie in the bins above d_sel: cut at that bin's upper edge
-      __syncthreads();
+      lds_barrier();
       return (prefix | (uint64_t(d_sel) << shift)) + (uint64_t(1) << shift);
     }
     got += above;
@@ -433,11 +433,11 @@ __device__ uint64_t block_cut(const uint64_t (&keys)[KPT], int need, int keep_mi
         if (keys[k] != 0 && (keys[k] & mask) == prefix) m2 = umin64(m2, keys[k]);
       m2 = wave_minmax_u64<true>(m2);
       if (lane == 0) sl.u64[wave] = m2;
-      __syncthreads();
+      lds_barrier();
       uint64_t res = ~uint64_t(0);
 #pragma unroll
       for (int w = 0; w < NW; ++w) res = umin64(res, sl.u64[w]);
-      __syncthreads();
+      lds_barrier();
       return res;
     }
     hi = shift - 1;
@@ -501,17 +501,17 @@ __global__ void __launch_bounds__(NT) index_score_kernel(IndexArgs a) {
     const float *qsrc = static_cast<const float *>(a.q_idx) + qi * a.H_I * a.D_I;
     for (int i = threadIdx.x; i < a.H_I * a.D_I; i += NT) q_lds[i] = qsrc[i];
     if (threadIdx.x < a.H_I) sh.ql.f[threadIdx.x] = a.w_idx[qi * a.H_I + threadIdx.x];
-    __syncthreads();
+    lds_barrier();
     score_tile_f32(q_lds, sh.ql.f, a.H_I, a.D_I, static_cast<const float *>(a.k_codes), row0, tile, vis,
                    sh.scores);
   } else {
     prep_query_lds<FMT>(raw, a.H_I, sh.ql);
-    __syncthreads();
+    lds_barrier();
     QueryFrag<NHB> qf;
     load_query_frag<FMT, NHB>(sh.ql, threadIdx.x & 63, qf);
     score_tile_mfma<FMT, NHB>(qf, ka, kb, tk, tile, vis, sh.scores);
   }
-  __syncthreads();
+  lds_barrier();
   if (a.scores) {
     float *dst = a.scores + qi * a.N_cap;
     for (int i = threadIdx.x; i < tile; i += NT)
@@ -569,7 +569,7 @@ __device__ void bitonic_sort_u32(uint32_t *v, int P) {
           if ((x > y) == up) { v[i] = y; v[ixj] = x; }
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
 }
@@ -593,19 +593,19 @@ __device__ void merge_fallback(const IndexArgs &a, MergeShared &sh, const uint64
     for (int k = 0; k < KPT; ++k)
       if (keys[k] != 0 && keys[k] >= tau) sh.work[pos++] = keys[k];
   }
-  __syncthreads();
+  lds_barrier();
   QueryFrag<4> qf;
   float *q_lds = reinterpret_cast<float *>(sh.ql.codes);
   if (FMT == 0) {
     const float *qsrc = static_cast<const float *>(a.q_idx) + qi * a.H_I * a.D_I;
     for (int i = tid; i < a.H_I * a.D_I; i += NT) q_lds[i] = qsrc[i];
     if (tid < a.H_I) sh.ql.f[tid] = a.w_idx[qi * a.H_I + tid];
-    __syncthreads();
+    lds_barrier();
   } else {
     QueryRaw raw;
     load_query_raw(static_cast<const uint16_t *>(a.q_idx) + qi * a.H_I * 128, a.w_idx + qi * a.H_I, a.H_I, raw);
     prep_query_lds<FMT>(raw, a.H_I, sh.ql);
-    __syncthreads();
+    lds_barrier();
     load_query_frag<FMT, 4>(sh.ql, tid & 63, qf);
   }
   constexpr int KW = (kMaxK + kMaxTile) / NT;
@@ -627,7 +627,7 @@ __device__ void merge_fallback(const IndexArgs &a, MergeShared &sh, const uint64
       load_batch<FMT>(tk, g_first + (NT / 64) * batch_of<FMT>(), tid & 63, kb);
       score_tile_mfma<FMT, 4>(qf, ka, kb, tk, tile, vis, sh.scores);
     }
-    __syncthreads();
+    lds_barrier();
     // append the tile's entries below its bound (the ones not already candidates) and above tau
     int mine = 0;
     for (int i = tid; i < vis; i += NT) {
@@ -641,7 +641,7 @@ __device__ void merge_fallback(const IndexArgs &a, MergeShared &sh, const uint64
       if (key < bt && key > tau) sh.work[pos++] = key;
     }
     wn += total;
-    __syncthreads();
+    lds_barrier();
     if (wn >= k_eff) {                                          // shrink W back to the k_eff best
       uint64_t wk[KW];
 #pragma unroll
@@ -649,7 +649,7 @@ __device__ void merge_fallback(const IndexArgs &a, MergeShared &sh, const uint64
         const int i = tid * KW + k;
         wk[k] = i < wn ? sh.work[i] : 0;
       }
-      __syncthreads();
+      lds_barrier();
       tau = block_select<NT, KW>(wk, k_eff, sh.sel);
       int m2 = 0;
 #pragma unroll
@@ -660,7 +660,7 @@ __device__ void merge_fallback(const IndexArgs &a, MergeShared &sh, const uint64
       for (int k = 0; k < KW; ++k)
         if (wk[k] != 0 && wk[k] >= tau) sh.work[p2++] = wk[k];
       wn = tot2;
-      __syncthreads();
+      lds_barrier();
     }
   }
   // ascending indices
@@ -673,13 +673,13 @@ __device__ void merge_fallback(const IndexArgs &a, MergeShared &sh, const uint64
     const int i = tid * KW + k;
     tmpv[k] = i < wn ? key_index(sh.work[i]) : 0xffffffffu;
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int k = 0; k < KW; ++k) {
     const int i = tid * KW + k;
     if (i < P) idx[i] = tmpv[k];
   }
-  __syncthreads();
+  lds_barrier();
   bitonic_sort_u32(idx, P);
   for (int i = tid; i < a.topk; i += NT) out[i] = i < wn ? int32_t(idx[i]) : -1;
 }
@@ -724,7 +724,7 @@ __global__ void __launch_bounds__(kMergeThreads) index_merge_kernel(IndexArgs a)
     sh.bounds[i] = cand_bound[qi * n_tiles + i];
   }
   if (tid == 0) sh.flag = 0;
-  __syncthreads();
+  lds_barrier();
   int nvalid_local = 0;
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
@@ -744,7 +744,7 @@ __global__ void __launch_bounds__(kMergeThreads) index_merge_kernel(IndexArgs a)
   // a truncated tile whose smallest kept key beats tau may hold further winners
   for (int i = tid; i < n_tiles; i += NT)
     if (sh.bounds[i] != 0 && sh.bounds[i] > tau) sh.flag = 1;
-  __syncthreads();
+  lds_barrier();
   if (sh.flag) {
     merge_fallback<FMT, KPT>(a, sh, keys, tau, qi, b, n_vis, k_eff, out);
     return;
