@@ -153,6 +153,45 @@ csa_status csa_compress(const uint16_t *c, const uint16_t *z, const uint16_t *bi
   return launched(e, "compress launch");
 }
 
+csa_status csa_decode_append(const uint16_t *c_new, const uint16_t *z_new, const uint16_t *k_new,
+                             const int64_t *pos, const uint16_t *bias, const uint16_t *norm_w, int B,
+                             int d, int m, int overlap, int rope_dim, float rope_base, float eps,
+                             uint16_t *tok_c, uint16_t *tok_z, uint16_t *win_ring, int64_t W_cap,
+                             uint16_t *entries, int64_t N_cap, int key_format, int D_I, void *k_codes,
+                             void *k_scales, int64_t *n_entries, void *stream) {
+  REQUIRE(B >= 0 && B <= 65535, "B must be in [0, 65535]");
+  REQUIRE(d == 64 || d == 128 || d == 256 || d == 512 || d == 1024, "d must be one of 64, 128, 256, 512, 1024");
+  REQUIRE(m >= 1 && m <= 1024, "m must be in [1, 1024]");
+  REQUIRE(overlap == 0 || overlap == 1, "overlap must be 0 or 1");
+  REQUIRE(rope_dim >= 0 && rope_dim <= d && rope_dim % 4 == 0, "rope_dim must be a multiple of 4 in [0, d]");
+  REQUIRE(eps > 0.f && std::isfinite(eps), "eps must be positive");
+  REQUIRE(rope_base > 1.f && std::isfinite(rope_base), "rope_base must be > 1");
+  REQUIRE(W_cap >= 1 && W_cap < (int64_t(1) << 31), "W_cap must be in [1, 2^31)");
+  REQUIRE(N_cap >= 1 && N_cap < (int64_t(1) << 31), "N_cap must be in [1, 2^31)");
+  if (k_new) {
+    REQUIRE(key_format == CSA_KEY_F32 || key_format == CSA_KEY_FP8_E4M3 || key_format == CSA_KEY_MXFP4,
+            "unknown key_format %d", key_format);
+    REQUIRE(D_I >= 1 && D_I <= 1024, "D_I must be in [1, 1024]");
+    REQUIRE(key_format != CSA_KEY_MXFP4 || D_I % 32 == 0, "MXFP4 keys need D_I % 32 == 0");
+  }
+  if (B == 0) return CSA_OK;
+  REQUIRE_PTR(c_new); REQUIRE_PTR(z_new); REQUIRE_PTR(pos); REQUIRE_PTR(bias); REQUIRE_PTR_OR_NULL(norm_w);
+  REQUIRE_PTR(tok_c); REQUIRE_PTR(tok_z); REQUIRE_PTR(win_ring); REQUIRE_PTR(entries); REQUIRE_PTR(n_entries);
+  REQUIRE_PTR_OR_NULL(k_new);
+  if (k_new) {
+    REQUIRE_PTR(k_codes);
+    if (key_format != CSA_KEY_F32) REQUIRE_PTR(k_scales);
+  }
+  csa::AppendArgs a{};
+  a.c_new = c_new; a.z_new = z_new; a.k_new = k_new; a.bias = bias; a.norm_w = norm_w; a.pos = pos;
+  a.tok_c = tok_c; a.tok_z = tok_z; a.win_ring = win_ring; a.entries = entries;
+  a.k_codes = k_codes; a.k_scales = k_scales; a.n_entries = n_entries; a.W_cap = W_cap; a.N_cap = N_cap;
+  a.B = B; a.d = d; a.m = m; a.overlap = overlap; a.rope_dim = rope_dim; a.key_format = key_format;
+  a.D_I = D_I; a.log2_base = std::log2(double(rope_base)); a.eps = eps;
+  hipError_t e = csa::launch_append(a, static_cast<hipStream_t>(stream));
+  return launched(e, "decode_append launch");
+}
+
 csa_status csa_quantize_keys(const uint16_t *x, int64_t rows, int dim, int format, void *codes,
                              void *scales, void *stream) {
   REQUIRE(format == CSA_KEY_FP8_E4M3 || format == CSA_KEY_MXFP4, "format must be CSA_KEY_FP8_E4M3 or CSA_KEY_MXFP4");
@@ -231,8 +270,10 @@ static csa_status check_attend_common(const uint16_t *q, const uint16_t *q_norm_
   REQUIRE(rope_base > 1.f && std::isfinite(rope_base), "rope_base must be > 1");
   REQUIRE(int64_t(B) * Sq <= 65535, "B * Sq must be <= 65535");
   if (B == 0 || Sq == 0) return CSA_OK;
-  REQUIRE_PTR(q); REQUIRE_PTR(entries); REQUIRE_PTR(win_rows); REQUIRE_PTR(win_pos0);
+  REQUIRE_PTR(q); REQUIRE_PTR(entries); REQUIRE_PTR(win_rows); REQUIRE_PTR_OR_NULL(win_pos0);
   REQUIRE_PTR(q_pos0); REQUIRE_PTR(out); REQUIRE_PTR_OR_NULL(q_norm_w); REQUIRE_PTR_OR_NULL(lse);
+  // win_pos0 NULL: win_rows is a ring holding position p at row p mod W_cap (csa_decode_append)
+  REQUIRE(win_pos0 != nullptr || W_cap >= window, "a window ring (win_pos0 NULL) needs W_cap >= window");
   return CSA_OK;
 }
 

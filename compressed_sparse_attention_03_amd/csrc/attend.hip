@@ -76,6 +76,7 @@ __device__ __forceinline__ int row_code(const AttendArgs &a, int64_t qi, int b, 
   if (w >= a.window) return -1;
   const int64_t p = t - a.window + 1 + w;                  // window position
   if (p < 0) return -1;
+  if (a.win_pos0 == nullptr) return int(a.N_cap + p % a.W_cap);   // ring: row of p at p mod W_cap
   const int64_t wr = p - a.win_pos0[b];
   if (wr < 0 || wr >= a.W_cap) return -1;
   return int(a.N_cap + wr);

@@ -47,6 +47,21 @@ __device__ __forceinline__ void load_raw(const uint16_t *p, RawRow<CPL> &r) {
 }
 
 template <int CPL>
+__device__ __forceinline__ void store_raw(uint16_t *p, const RawRow<CPL> &r) {
+  if constexpr (CPL == 1) {
+    *p = uint16_t(r.w[0]);
+  } else if constexpr (CPL == 2) {
+    *reinterpret_cast<uint32_t *>(p) = r.w[0];
+  } else if constexpr (CPL == 4) {
+    *reinterpret_cast<uint2 *>(p) = make_uint2(r.w[0], r.w[1]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < CPL / 8; ++q)
+      reinterpret_cast<uint4 *>(p)[q] = make_uint4(r.w[4 * q], r.w[4 * q + 1], r.w[4 * q + 2], r.w[4 * q + 3]);
+  }
+}
+
+template <int CPL>
 __device__ __forceinline__ void store_row(uint16_t *p, const float (&v)[CPL]) {
   if constexpr (CPL == 1) {
     *p = f32_to_bf16(v[0]);
@@ -202,6 +217,136 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
   store_row<CPL>(a.entries + (int64_t(b) * (a.n_new / m) + i) * d + lane * CPL, p);
 }
 
+// ---- decode-time cache maintenance --------------------------------------------------------
+// "DeepSeek-V4: Million-Token Context" (codexsims explainer), CSA walk-through: the compressed
+// store gains one entry per m tokens; "Follow the white rabbit" (sambatista.com), sliding-window
+// paragraph: the newest tokens are kept as separate rows, and a group becomes an entry once it is
+// complete; indexer paragraph: the indexer keys are stored in low precision.
+//
+// One workgroup per sequence.  The token's raw c, z rows go into the sequence's ring of the last
+// (1+overlap) m tokens (slot = position mod ring size); its window row (RMSNorm, RoPE at its own
+// position) into the window ring (slot = position mod W_cap).  When the token closes a group the
+// entry is pooled exactly as the batch compressor pools it -- from the ring, with the new token
+// taken from registers -- normalised, rotated at i m and written; the entry's indexer key is
+// quantised into the key cache (the encoders of csa_quantize_keys) and n_entries is advanced.
+
+// Quantise-on-write of one indexer key row (one wave): fp32 copy, fp8 e4m3 with a power-of-two
+// row scale, or MXFP4 (one lane per block of 32 values).
+__device__ void store_key_row(const AppendArgs &a, const uint16_t *x, int64_t row, int lane) {
+  const int D = a.D_I;
+  if (a.key_format == 0) {
+    float *dst = static_cast<float *>(a.k_codes) + row * D;
+    for (int c = lane; c < D; c += 64) dst[c] = bf16_to_f32(x[c]);
+  } else if (a.key_format == 1) {
+    float amax = 0.f;
+    for (int c = lane; c < D; c += 64) amax = fmaxf(amax, fabsf(bf16_to_f32(x[c])));
+    amax = wave_max(amax);
+    const int e = e4m3_row_exp(amax);
+    const float inv = ldexpf(1.0f, -e);
+    uint8_t *dst = static_cast<uint8_t *>(a.k_codes) + row * D;
+    for (int c = lane; c < D; c += 64) dst[c] = uint8_t(f32_to_e4m3(bf16_to_f32(x[c]) * inv));
+    if (lane == 0) static_cast<float *>(a.k_scales)[row] = ldexpf(1.0f, e);
+  } else {
+    const int nb = D / 32;
+    for (int blk = lane; blk < nb; blk += 64) {
+      const uint16_t *xb = x + 32 * blk;
+      float amax = 0.f;
+      for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(bf16_to_f32(xb[q])));
+      const uint32_t sb = mx_scale_byte(amax);
+      const float inv = ldexpf(1.0f, 127 - int(sb));
+      uint8_t *dst = static_cast<uint8_t *>(a.k_codes) + row * (D / 2) + 16 * blk;
+      for (int q = 0; q < 16; ++q)
+        dst[q] = uint8_t(f32_to_e2m1(bf16_to_f32(xb[2 * q]) * inv) | (f32_to_e2m1(bf16_to_f32(xb[2 * q + 1]) * inv) << 4));
+      static_cast<uint8_t *>(a.k_scales)[row * nb + blk] = uint8_t(sb);
+    }
+  }
+}
+
+template <int CPL>
+__global__ void __launch_bounds__(256) decode_append_kernel(AppendArgs a) {
+  const int d = a.d, m = a.m;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.x;
+  const int64_t t = a.pos[b];
+  if (t < 0) return;
+  const int R = (1 + a.overlap) * m;                           // ring rows per sequence
+  const int64_t ring0 = int64_t(b) * R;
+  RawRow<CPL> rc, rz;
+  load_raw<CPL>(a.c_new + int64_t(b) * d + lane * CPL, rc);
+  load_raw<CPL>(a.z_new + int64_t(b) * d + lane * CPL, rz);
+  if (wave == 0) {
+    store_raw<CPL>(a.tok_c + (ring0 + t % R) * d + lane * CPL, rc);
+    store_raw<CPL>(a.tok_z + (ring0 + t % R) * d + lane * CPL, rz);
+  } else if (wave == 1) {
+    float v[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) v[j] = rc.at(j);
+    norm_rope<CPL>(v, a.norm_w, d, a.rope_dim, t, a.log2_base, a.eps, lane);
+    store_row<CPL>(a.win_ring + (int64_t(b) * a.W_cap + t % a.W_cap) * d + lane * CPL, v);
+  }
+  if ((t + 1) % m != 0) return;                                // no group closes at this token
+  const int64_t i = (t + 1) / m - 1;                           // the entry it closes
+  if (i >= a.N_cap) return;
+  const bool has_prev = a.overlap && i > 0;
+  const int nt = has_prev ? 2 * m : m;
+  const int64_t p_first = has_prev ? (i - 1) * m : i * m;
+  const int slot_first = has_prev ? 0 : (a.overlap ? m : 0);   // bias row of the first token
+
+  float mx[CPL], sm[CPL], acc[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) { mx[j] = -INFINITY; sm[j] = 0.f; acc[j] = 0.f; }
+  const int per = (nt + 3) >> 2;
+  const int k0 = wave * per, k1 = min(nt, k0 + per);
+  for (int k = k0; k < k1; ++k) {
+    const int64_t p = p_first + k;
+    RawRow<CPL> xc = rc, xz = rz, xb;
+    if (p != t) {                                              // older tokens come from the ring
+      load_raw<CPL>(a.tok_c + (ring0 + p % R) * d + lane * CPL, xc);
+      load_raw<CPL>(a.tok_z + (ring0 + p % R) * d + lane * CPL, xz);
+    }
+    load_raw<CPL>(a.bias + int64_t(slot_first + k) * d + lane * CPL, xb);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const float l = (xz.at(j) + xb.at(j)) * kLog2e;
+      const float nm = fmaxf(mx[j], l);
+      const float sc = exp2f(mx[j] - nm), e = exp2f(l - nm);
+      sm[j] = sm[j] * sc + e;
+      acc[j] = acc[j] * sc + e * xc.at(j);
+      mx[j] = nm;
+    }
+  }
+  __shared__ float s_state[3][4][64 * CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    s_state[0][wave][lane * CPL + j] = mx[j];
+    s_state[1][wave][lane * CPL + j] = sm[j];
+    s_state[2][wave][lane * CPL + j] = acc[j];
+  }
+  lds_barrier();
+  if (wave == 0) {
+    float pv[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int ch = lane * CPL + j;
+      float M = fmaxf(fmaxf(s_state[0][0][ch], s_state[0][1][ch]), fmaxf(s_state[0][2][ch], s_state[0][3][ch]));
+      float S = 0.f, A = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = s_state[0][w][ch];
+        const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+        S += s_state[1][w][ch] * f;
+        A += s_state[2][w][ch] * f;
+      }
+      pv[j] = A / S;
+    }
+    norm_rope<CPL>(pv, a.norm_w, d, a.rope_dim, i * m, a.log2_base, a.eps, lane);
+    store_row<CPL>(a.entries + (int64_t(b) * a.N_cap + i) * d + lane * CPL, pv);
+    if (lane == 0) a.n_entries[b] = i + 1;
+  } else if (wave == 1 && a.k_new) {
+    store_key_row(a, a.k_new + int64_t(b) * a.D_I, int64_t(b) * a.N_cap + i, lane);
+  }
+}
+
 template <int CPL, bool WIN>
 hipError_t launch_compress_win(const CompressArgs &a, dim3 grid, hipStream_t stream) {
   // Tokens per wave: 2m with the previous group (every entry but the sequence's first), else m.
@@ -222,6 +367,18 @@ hipError_t launch_compress_cpl(const CompressArgs &a, dim3 grid, hipStream_t str
 }
 
 }  // namespace
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t stream) {
+  const dim3 grid(unsigned(a.B)), block(256);
+  switch (a.d / 64) {
+    case 1: return launch("decode_append", decode_append_kernel<1>, grid, block, stream, a);
+    case 2: return launch("decode_append", decode_append_kernel<2>, grid, block, stream, a);
+    case 4: return launch("decode_append", decode_append_kernel<4>, grid, block, stream, a);
+    case 8: return launch("decode_append", decode_append_kernel<8>, grid, block, stream, a);
+    case 16: return launch("decode_append", decode_append_kernel<16>, grid, block, stream, a);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_compress(const CompressArgs &a, hipStream_t stream) {
   const dim3 grid(unsigned(a.n_new / a.m), unsigned(a.B));

@@ -18,6 +18,20 @@ struct CompressArgs {
 };
 hipError_t launch_compress(const CompressArgs &a, hipStream_t stream);
 
+// Decode-time cache maintenance: one new token per sequence (see csa_decode_append).
+struct AppendArgs {
+  const uint16_t *c_new, *z_new, *k_new, *bias, *norm_w;
+  const int64_t *pos;
+  uint16_t *tok_c, *tok_z, *win_ring, *entries;
+  void *k_codes, *k_scales;
+  int64_t *n_entries;
+  int64_t W_cap, N_cap;
+  int B, d, m, overlap, rope_dim, key_format, D_I;
+  double log2_base;
+  float eps;
+};
+hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
+
 struct QuantizeArgs {
   const uint16_t *x;
   void *codes, *scales;

@@ -27,6 +27,8 @@ I32, I64, F32, SZ = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_
 _SIGS = {
     "csa_compress": (I32, [P, P, P, P, I32, I64, I32, I32, I32, I32, I32, I64, F32, F32, P, P, P]),
     "csa_quantize_keys": (I32, [P, I64, I32, I32, P, P, P]),
+    "csa_decode_append": (I32, [P, P, P, P, P, P, I32, I32, I32, I32, I32, F32, F32, P, P, P, I64, P, I64,
+                                I32, I32, P, P, P, P]),
     "csa_index_topk": (I32, [P, P, P, P, I32, I32, I32, I32, I32, I64, P, P, I32, I32, P, P, P, SZ, P]),
     "csa_index_topk_workspace_bytes": (SZ, [I32, I32, I64, I32]),
     "csa_attend": (I32, [P, P, P, I64, P, I32, P, I64, P, P, I32, I32, I32, I32, I32, I32, F32, F32,
@@ -142,6 +144,58 @@ def csa_quantize_keys(x, fmt, codes_out=None, scales_out=None):
     return codes, scales
 
 
+def csa_decode_append(c_new, z_new, pos, bias, *, m, overlap, rope_dim, tok_c, tok_z, win_ring, entries,
+                      n_entries, k_new=None, key_format="fp8", k_codes=None, k_scales=None, norm_w=None,
+                      rope_base=10000.0, eps=1e-6):
+    """Decode-time cache maintenance for one new token per sequence, in place on the caches:
+    token ring ``tok_c``/``tok_z`` [B, (1+overlap)*m, d], window ring ``win_ring`` [B, W_cap, d],
+    ``entries`` [B, N_cap, d], indexer keys ``k_codes``/``k_scales`` and ``n_entries`` [B]."""
+    _dev(c_new, "c_new", torch.bfloat16, 2)
+    _dev(z_new, "z_new", torch.bfloat16, 2)
+    B, d = c_new.shape
+    if tuple(z_new.shape) != (B, d):
+        raise ValueError("z_new must have the shape of c_new")
+    _i64(pos, "pos", B)
+    _i64(n_entries, "n_entries", B)
+    _dev(bias, "bias", torch.bfloat16, 2)
+    R = (1 + overlap) * m
+    for name, t in (("tok_c", tok_c), ("tok_z", tok_z)):
+        _dev(t, name, torch.bfloat16, 3)
+        if tuple(t.shape) != (B, R, d):
+            raise ValueError(f"{name} must be [{B}, {R}, {d}]")
+    _dev(win_ring, "win_ring", torch.bfloat16, 3)
+    _dev(entries, "entries", torch.bfloat16, 3)
+    if win_ring.shape[0] != B or win_ring.shape[2] != d or entries.shape[0] != B or entries.shape[2] != d:
+        raise ValueError("win_ring / entries must be [B, rows, d]")
+    if norm_w is not None:
+        _dev(norm_w, "norm_w", torch.bfloat16, 1)
+    N_cap = entries.shape[1]
+    f, D_I = KEY_FORMATS[key_format], 0
+    if k_new is not None:
+        _dev(k_new, "k_new", torch.bfloat16, 2)
+        D_I = k_new.shape[1]
+        if k_new.shape[0] != B:
+            raise ValueError("k_new must be [B, D_I]")
+        if f == KEY_F32:
+            shapes = {"k_codes": ((B, N_cap, D_I), torch.float32)}
+        elif f == KEY_FP8_E4M3:
+            shapes = {"k_codes": ((B, N_cap, D_I), torch.uint8), "k_scales": ((B, N_cap), torch.float32)}
+        else:
+            shapes = {"k_codes": ((B, N_cap, D_I // 2), torch.uint8),
+                      "k_scales": ((B, N_cap, D_I // 32), torch.uint8)}
+        for name, t in (("k_codes", k_codes), ("k_scales", k_scales)):
+            if name in shapes:
+                shp, dt = shapes[name]
+                _dev(t, name, dt)
+                if tuple(t.shape) != shp:
+                    raise ValueError(f"{name} must have shape {shp}")
+    st = lib().csa_decode_append(_ptr(c_new), _ptr(z_new), _ptr(k_new), _ptr(pos), _ptr(bias), _ptr(norm_w), B, d,
+                                 m, overlap, rope_dim, rope_base, eps, _ptr(tok_c), _ptr(tok_z), _ptr(win_ring),
+                                 win_ring.shape[1], _ptr(entries), N_cap, f, D_I, _ptr(k_codes), _ptr(k_scales),
+                                 _ptr(n_entries), _stream())
+    _check(st, "csa_decode_append")
+
+
 def index_topk_workspace(B, Sq, N_cap, topk, device="cuda"):
     n = lib().csa_index_topk_workspace_bytes(B, Sq, N_cap, topk)
     return torch.empty(n, dtype=torch.uint8, device=device)
@@ -191,7 +245,8 @@ def _attend_common(q, entries, win_rows, win_pos0, q_pos0, q_norm_w):
     _dev(win_rows, "win_rows", torch.bfloat16, 3)
     if entries.shape[0] != B or entries.shape[2] != D or win_rows.shape[0] != B or win_rows.shape[2] != D:
         raise ValueError("entries/win_rows must be [B, rows, D]")
-    _i64(win_pos0, "win_pos0", B)
+    if win_pos0 is not None:                     # None: win_rows is a ring (row p mod W_cap)
+        _i64(win_pos0, "win_pos0", B)
     _i64(q_pos0, "q_pos0", B)
     if q_norm_w is not None:
         _dev(q_norm_w, "q_norm_w", torch.bfloat16, 1)

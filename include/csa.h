@@ -87,6 +87,43 @@ csa_status csa_compress(const uint16_t *c, const uint16_t *z, const uint16_t *bi
                         uint16_t *entries, uint16_t *win_rows, void *stream);
 
 /*
+ * csa_decode_append -- decode-time cache maintenance: one new token per sequence.
+ * [EXPLAINER] CSA walk-through: the compressed store gains one entry per m tokens (HCA
+ * walk-through: per m' = 128 tokens); [RABBIT] sliding-window paragraph: the newest tokens are
+ * also kept as separate rows, and tokens of an unfinished group belong to no entry yet; [RABBIT]
+ * indexer paragraph, [DEVTO] "Two Compression Strategies": the indexer keys are kept in low
+ * precision (quantised when written).
+ *
+ * For sequence b with its new token at position t = pos[b] (tokens arrive in position order):
+ *   - the token's c, z rows are kept in the compressor's token ring: rows t mod R of
+ *     tok_c / tok_z [B, R, d], R = (1 + overlap) * m;
+ *   - its window row (RMSNorm with norm_w, RoPE at t; as csa_compress's win_rows) is written to
+ *     win_ring [B, W_cap, d] at row t mod W_cap -- the ring csa_attend / hca_attend read when
+ *     given win_pos0 = NULL;
+ *   - when t + 1 is a multiple of m, entry i = (t+1)/m - 1 is complete: it is pooled from the
+ *     ring exactly as csa_compress defines it (bias slots, overlap, entry 0 alone), normalised,
+ *     rotated at i*m and written to entries[b, i]; k_new[b] (its indexer key, bf16 [B, D_I]) is
+ *     quantised by csa_quantize_keys's rule for key_format (CSA_KEY_F32: copied as fp32) into
+ *     k_codes / k_scales row (b, i); n_entries[b] becomes i + 1.  Entries at i >= N_cap are
+ *     dropped.  k_new NULL keeps no indexer keys (HCA).
+ *   c_new, z_new  bf16 [B, d] the new token's compressor inputs.
+ *   pos           device int64 [B]; a negative position leaves that sequence untouched.
+ *   k_codes       [B, N_cap, D_I] fp32 | [B, N_cap, D_I] e4m3 | [B, N_cap, D_I/2] e2m1 pairs;
+ *   k_scales      NULL | fp32 [B, N_cap] | e8m0 [B, N_cap, D_I/32].
+ *   n_entries     device int64 [B], written when an entry completes.
+ * The caches are device memory owned by the caller; the ring rows of positions before the first
+ * appended token are never read when the sequence starts at position 0.
+ * Limits: d in {64, 128, 256, 512, 1024}; 1 <= m <= 1024; rope_dim % 4 == 0; 1 <= D_I <= 1024
+ * (MXFP4: D_I % 32 == 0); W_cap, N_cap in [1, 2^31).
+ */
+csa_status csa_decode_append(const uint16_t *c_new, const uint16_t *z_new, const uint16_t *k_new,
+                             const int64_t *pos, const uint16_t *bias, const uint16_t *norm_w, int B,
+                             int d, int m, int overlap, int rope_dim, float rope_base, float eps,
+                             uint16_t *tok_c, uint16_t *tok_z, uint16_t *win_ring, int64_t W_cap,
+                             uint16_t *entries, int64_t N_cap, int key_format, int D_I, void *k_codes,
+                             void *k_scales, int64_t *n_entries, void *stream);
+
+/*
  * csa_quantize_keys -- quantise lightning-indexer keys to their storage format (quantise on write).
  * [DEVTO] "Two Compression Strategies": the indexer runs in FP4; [RABBIT] indexer paragraph:
  * smaller representations and lower-precision numbers.
@@ -154,7 +191,9 @@ size_t csa_index_topk_workspace_bytes(int B, int Sq, int64_t N_cap, int topk);
  *   entries    bf16 [B, N_cap, D] compressed entries (as written by csa_compress).
  *   topk_idx   int32 [B, Sq, topk]; -1 marks an empty slot.
  *   win_rows   bf16 [B, W_cap, D] prepared rows; the caller guarantees the window's positions are
- *              inside [win_pos0[b], win_pos0[b] + W_cap).
+ *              inside [win_pos0[b], win_pos0[b] + W_cap).  With win_pos0 NULL, win_rows is a ring
+ *              (as csa_decode_append keeps it): the row of position p is row p mod W_cap, and
+ *              W_cap >= window is required.
  *   out        bf16 [B, Sq, H, D]; lse fp32 [B, Sq, H] or NULL.
  * Limits: D in {64, 128, 256, 512}; H >= 1 (heads are processed in blocks of 16);
  *         rope_dim % 4 == 0, rope_dim <= D; 1 <= window <= 4096; 1 <= topk <= 2048.

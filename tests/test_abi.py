@@ -23,7 +23,8 @@ def declared_functions():
 
 def test_header_declares_the_four_operations():
     names = declared_functions()
-    for n in ("csa_compress", "csa_index_topk", "csa_attend", "hca_attend", "csa_quantize_keys"):
+    for n in ("csa_compress", "csa_index_topk", "csa_attend", "hca_attend", "csa_quantize_keys",
+              "csa_decode_append"):
         assert n in names
 
 
@@ -129,6 +130,38 @@ def _attend(fn="csa_attend", **kw):
 ])
 def test_attend_rejects_bad_arguments(fn, kw, status):
     assert _attend(fn, **kw) == status
+
+
+def test_attend_window_ring_needs_room_for_the_window():
+    # win_pos0 NULL selects the ring layout, which must hold a whole window
+    assert _attend("csa_attend", win_pos0=None, W_cap=64, window=128) == 1
+    assert _attend("hca_attend", win_pos0=None, W_cap=64, window=128) == 1
+
+
+def _append(**kw):
+    L = ops.lib()
+    a = dict(c_new=16, z_new=16, k_new=16, pos=16, bias=16, norm_w=None, B=4, d=512, m=4, overlap=1,
+             rope_dim=64, base=10000.0, eps=1e-6, tok_c=16, tok_z=16, win_ring=16, W_cap=128, entries=16,
+             N_cap=1024, key_format=2, D_I=128, k_codes=16, k_scales=16, n_entries=16, stream=None)
+    a.update(kw)
+    ptrs = ("c_new", "z_new", "k_new", "pos", "bias", "norm_w", "tok_c", "tok_z", "win_ring", "entries",
+            "k_codes", "k_scales", "n_entries", "stream")
+    return L.csa_decode_append(*[ctypes.c_void_p(v) if k in ptrs and v is not None else v for k, v in a.items()])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(d=96), dict(m=0), dict(overlap=2), dict(rope_dim=66), dict(W_cap=0), dict(N_cap=0),
+    dict(key_format=7), dict(key_format=2, D_I=40), dict(D_I=0), dict(eps=0.0), dict(pos=None),
+    dict(tok_c=None), dict(k_scales=None), dict(c_new=8),
+])
+def test_append_rejects_bad_arguments(kw):
+    assert _append(**kw) == 1
+
+
+def test_append_zero_batch_and_keyless_calls_validate_on_the_host():
+    assert _append(B=0) == 0
+    # without k_new the key arguments are not examined
+    assert _append(B=0, k_new=None, key_format=9, D_I=0, k_codes=None, k_scales=None) == 0
 
 
 def test_quantize_rejects_bad_arguments():
