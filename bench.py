@@ -68,8 +68,9 @@ def index_score_bytes(w):
 
 # ---- one workload leg --------------------------------------------------------------------------
 class Leg:
-    def __init__(self, w: gen.Workload):
+    def __init__(self, w: gen.Workload, append: bool = False):
         self.w = w
+        self.append = append
         self.step_bytes = w.B * (hca_query_bytes(w) if w.kind == "hca_decode" else csa_query_bytes(w))
         self.ncopies = max(2, math.ceil(4 * MALL_BYTES / self.step_bytes))
         log(f"[{w.name}] generating inputs; {self.ncopies} copies of {self.step_bytes / 1e6:.1f} MB/step")
@@ -93,6 +94,20 @@ class Leg:
             self.sel = [torch.empty((w.B, 1, w.topk), dtype=torch.int32, device="cuda") for _ in range(self.ncopies)]
             self.ws_i = ops.index_topk_workspace(w.B, 1, w.N, w.topk)
             self.ws_a = ops.attend_workspace(w.B, 1, w.H, w.d, w.topk, w.window)
+            if append:
+                # cache maintenance in front of the step: the new token at t = T-1 closes a group
+                # (entry N-1 is rewritten and its key quantised every step); the window rows are
+                # read as a ring of W_cap = window rows
+                g = torch.Generator(device="cuda").manual_seed(w.cfg)
+                bf = lambda *shape, std=1.0: (std * torch.randn(shape, generator=g, device="cuda")).to(torch.bfloat16)
+                R = (1 + w.overlap) * w.m
+                self.tok_c = [bf(w.B, R, w.d) for _ in range(self.ncopies)]
+                self.tok_z = [bf(w.B, R, w.d) for _ in range(self.ncopies)]
+                self.c_new = [bf(w.B, w.d) for _ in range(self.ncopies)]
+                self.z_new = [bf(w.B, w.d) for _ in range(self.ncopies)]
+                self.k_new = [bf(w.B, w.D_I) for _ in range(self.ncopies)]
+                self.bias = bf(R, w.d, std=0.1)
+                self.n_app = self.n_ent.clone()
         else:
             self.ws_a = ops.hca_workspace(w.B, 1, w.H, w.d, w.N, w.window)
         del x
@@ -101,7 +116,17 @@ class Leg:
 
     def step(self, i):
         w, c = self.w, i % self.ncopies
-        if w.kind == "csa_decode":
+        if w.kind == "csa_decode" and self.append:
+            ops.csa_decode_append(self.c_new[c], self.z_new[c], self.t, self.bias, m=w.m, overlap=w.overlap,
+                                  rope_dim=w.rope_dim, tok_c=self.tok_c[c], tok_z=self.tok_z[c], win_ring=self.win[c],
+                                  entries=self.ent[c], n_entries=self.n_app, k_new=self.k_new[c],
+                                  key_format=w.key_format, k_codes=self.codes[c], k_scales=self.scales[c])
+            ops.csa_index_topk(self.q_idx[c], self.w_idx[c], self.codes[c], self.scales[c], key_format=w.key_format,
+                               n_entries=self.n_app, q_pos0=self.t, m=w.m, topk=w.topk, workspace=self.ws_i,
+                               topk_out=self.sel[c])
+            ops.csa_attend(self.q[c], self.ent[c], self.sel[c], self.win[c], None, self.t,
+                           rope_dim=w.rope_dim, window=w.window, workspace=self.ws_a, out=self.out[c])
+        elif w.kind == "csa_decode":
             ops.csa_index_topk(self.q_idx[c], self.w_idx[c], self.codes[c], self.scales[c], key_format=w.key_format,
                                n_entries=self.n_ent, q_pos0=self.t, m=w.m, topk=w.topk, workspace=self.ws_i,
                                topk_out=self.sel[c])
@@ -122,7 +147,7 @@ class Leg:
             self.step(i)
         torch.cuda.synchronize()
         res = {}
-        for k in ("index_score", "index_merge", "attend_split", "attend_combine"):
+        for k in ("decode_append", "index_score", "index_merge", "attend_split", "attend_combine"):
             ms, cnt = ops.timing_read(k)
             if cnt:
                 res[k] = 1000.0 * ms / cnt
@@ -427,7 +452,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--legs", default="main,d128,c32k,hca,prefill,compress")
+    ap.add_argument("--legs", default="main,d128,c32k,hca,append,prefill,compress")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy", "summarize-trace", "summarize-traffic"])
     ap.add_argument("--db", nargs="*", default=[], help="rocprofv3 databases for the summarize modes: one "
                     "kernel-trace db; or FETCH, WRITE, copy-FETCH, copy-WRITE dbs")
@@ -450,7 +475,7 @@ def main():
         return
     legs = args.legs.split(",")
     table = {"main": gen.CSA_DECODE_1M, "d128": gen.CSA_DECODE_128K, "c32k": gen.CSA_DECODE_32K,
-             "hca": gen.HCA_DECODE_1M}
+             "hca": gen.HCA_DECODE_1M, "append": gen.CSA_DECODE_1M}
     results = {}
     for name in legs:
         if name == "prefill":
@@ -465,13 +490,14 @@ def main():
             log(json.dumps(results[name]))
             continue
         w = table[name]
-        leg = Leg(w)
+        leg = Leg(w, append=(name == "append"))
         kt = leg.kernel_times()
         sec = leg.run(args.steps, args.warmup, graph=True)
         sec_eager = leg.run(min(args.steps, 200), min(args.warmup, 20), graph=False)
         ms = 1000 * sec / args.steps
         tok_s = w.B * args.steps / sec
-        r = {"workload": w.name, "value": tok_s, "unit": "query-tokens/s", "ms_per_step": ms,
+        r = {"workload": w.name + ("+decode_append" if name == "append" else ""), "value": tok_s,
+             "unit": "query-tokens/s", "ms_per_step": ms,
              "hbm_frac_step": leg.step_bytes * args.steps / sec / (PEAK_HBM_GBS * 1e9),
              "bytes_per_step": leg.step_bytes, "copies": leg.ncopies,
              "eager_ms_per_step": 1000 * sec_eager / min(args.steps, 200), "kernel_us": kt}
@@ -492,7 +518,7 @@ def main():
         log(json.dumps(r))
         leg.free()
         del leg
-    table_legs = [k for k in legs if k in table]
+    table_legs = [k for k in legs if k in table and k != "append"]
     if not table_legs:                                           # only side legs were asked for
         return
     main_name = table_legs[0]

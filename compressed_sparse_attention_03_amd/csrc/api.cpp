@@ -171,8 +171,7 @@ csa_status csa_decode_append(const uint16_t *c_new, const uint16_t *z_new, const
   if (k_new) {
     REQUIRE(key_format == CSA_KEY_F32 || key_format == CSA_KEY_FP8_E4M3 || key_format == CSA_KEY_MXFP4,
             "unknown key_format %d", key_format);
-    REQUIRE(D_I >= 1 && D_I <= 1024, "D_I must be in [1, 1024]");
-    REQUIRE(key_format != CSA_KEY_MXFP4 || D_I % 32 == 0, "MXFP4 keys need D_I % 32 == 0");
+    REQUIRE(D_I >= 32 && D_I <= 1024 && D_I % 32 == 0, "D_I must be a multiple of 32 in [32, 1024]");
   }
   if (B == 0) return CSA_OK;
   REQUIRE_PTR(c_new); REQUIRE_PTR(z_new); REQUIRE_PTR(pos); REQUIRE_PTR(bias); REQUIRE_PTR_OR_NULL(norm_w);

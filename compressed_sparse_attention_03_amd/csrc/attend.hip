@@ -182,7 +182,8 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
   // row codes and rotary angles; the first chunks' loads go out before q^ is built
   for (int i = tid; i < nr; i += NT) s_row[i] = row_code(a, qi, b, t, n_vis, r0 + i);
   const int npairs = a.rope_dim / 2;
-  for (int u = tid; u < npairs; u += NT) rope_cos_sin(t, u, a.rope_dim, a.log2_base, &s_cs[u], &s_sn[u]);
+  const double rate = rope_rate(a.rope_dim, a.log2_base);
+  for (int u = tid; u < npairs; u += NT) rope_cos_sin(t, u, rate, &s_cs[u], &s_sn[u]);
   const uint16_t *ent_b = a.entries + int64_t(b) * a.N_cap * D + C * wave;
   const uint16_t *win_b = a.win_rows + int64_t(b) * a.W_cap * D + C * wave;
   lds_barrier();

@@ -112,16 +112,18 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // ---- rotary angles ---------------------------------------------------------------------------
-// cos/sin of pos * base^(-2u/r).  The angle is formed and reduced modulo 2*pi in double so that
-// positions near 2^20 keep full fp32 accuracy; the final sin/cos are fp32.
-__device__ __forceinline__ void rope_cos_sin(int64_t pos, int u, int r, double log2_base,
-                                             float *c, float *s) {
-  double inv = exp2(-(2.0 * double(u) / double(r)) * log2_base);
-  double phi = double(pos) * inv;
-  const double two_pi = 6.283185307179586476925286766559;
-  phi -= two_pi * rint(phi / two_pi);
-  float p = float(phi);
-  sincosf(p, s, c);
+// Pair u of an r-dim rotation at position pos turns by pos * base^(-2u/r) radians.  rope_rate
+// gives -2 log2(base) / r once per call site; rope_cos_sin forms the angle in double, measured in
+// turns, and keeps its fractional part there (so positions near 2^21 keep full fp32 accuracy of
+// the reduced angle); the hardware sine and cosine (v_sin_f32 / v_cos_f32, whose argument is in
+// turns) take the fp32 fraction.
+__device__ __forceinline__ double rope_rate(int r, double log2_base) { return -2.0 * log2_base / double(r); }
+__device__ __forceinline__ void rope_cos_sin(int64_t pos, int u, double rate, float *c, float *s) {
+  constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
+  const double turns = double(pos) * (exp2(double(u) * rate) * kInvTwoPi);
+  const float f = float(turns - rint(turns));                   // in [-1/2, 1/2]
+  *s = __builtin_amdgcn_sinf(f);
+  *c = __builtin_amdgcn_cosf(f);
 }
 
 }  // namespace csa

@@ -78,10 +78,26 @@ __device__ __forceinline__ void store_row(uint16_t *p, const float (&v)[CPL]) {
   }
 }
 
-// RMSNorm (weight g, or ones) then rotation of the channels >= d - r at position pos.
+// The RMSNorm weights of a lane's channels, loaded once per workgroup with one vector load.
+// Without weights (g NULL) the load reads `any` (a valid row of at least d values) and the
+// weights are ones.
+template <int CPL>
+struct NormWeights {
+  RawRow<CPL> w;
+  bool has;
+};
+template <int CPL>
+__device__ __forceinline__ NormWeights<CPL> load_norm_weights(const uint16_t *g, const uint16_t *any, int lane) {
+  NormWeights<CPL> n;
+  n.has = g != nullptr;
+  load_raw<CPL>((g ? g : any) + lane * CPL, n.w);
+  return n;
+}
+
+// RMSNorm (weights gw) then rotation of the channels >= d - r at position pos.
 // Every lane of the wave must call this (it reduces across the wave).
 template <int CPL>
-__device__ __forceinline__ void norm_rope(float (&v)[CPL], const uint16_t *g, int d, int r,
+__device__ __forceinline__ void norm_rope(float (&v)[CPL], const NormWeights<CPL> &gw, int d, int r,
                                           int64_t pos, double log2_base, float eps, int lane) {
   float ss = 0.f;
 #pragma unroll
@@ -90,16 +106,17 @@ __device__ __forceinline__ void norm_rope(float (&v)[CPL], const uint16_t *g, in
   float inv = rsqrtf(ss / float(d) + eps);
   const int c0 = lane * CPL;
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) v[j] *= inv * (g ? bf16_to_f32(g[c0 + j]) : 1.0f);
+  for (int j = 0; j < CPL; ++j) v[j] *= inv * (gw.has ? gw.w.at(j) : 1.0f);
   const int rope0 = d - r;
   if constexpr (CPL >= 2) {
     if (c0 + CPL > rope0) {
+      const double rate = rope_rate(r, log2_base);
 #pragma unroll
       for (int j = 0; j < CPL; j += 2) {
         int ch = c0 + j;
         if (ch >= rope0) {
           float cs, sn;
-          rope_cos_sin(pos, (ch - rope0) >> 1, r, log2_base, &cs, &sn);
+          rope_cos_sin(pos, (ch - rope0) >> 1, rate, &cs, &sn);
           float a = v[j], b = v[j + 1];
           v[j] = a * cs - b * sn;
           v[j + 1] = a * sn + b * cs;
@@ -110,7 +127,7 @@ __device__ __forceinline__ void norm_rope(float (&v)[CPL], const uint16_t *g, in
     float partner = __shfl_xor(v[0], 1, 64);
     if (c0 >= rope0) {
       float cs, sn;
-      rope_cos_sin(pos, (c0 - rope0) >> 1, r, log2_base, &cs, &sn);
+      rope_cos_sin(pos, (c0 - rope0) >> 1, rope_rate(r, log2_base), &cs, &sn);
       v[0] = (c0 & 1) ? (partner * sn + v[0] * cs) : (v[0] * cs - partner * sn);
     }
   }
@@ -131,6 +148,7 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
   const int64_t rows = a.halo + a.n_new;
   const uint16_t *cb = a.c + (int64_t(b) * rows) * d + lane * CPL;
   const uint16_t *zb = a.z + (int64_t(b) * rows) * d + lane * CPL;
+  const NormWeights<CPL> gw = load_norm_weights<CPL>(a.norm_w, a.bias, lane);
 
   float mx[CPL], sm[CPL], acc[CPL];
 #pragma unroll
@@ -182,7 +200,7 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
           float cv[CPL];
 #pragma unroll
           for (int j = 0; j < CPL; ++j) cv[j] = rc[u].at(j);
-          norm_rope<CPL>(cv, a.norm_w, d, a.rope_dim, a.pos0 + tok, a.log2_base, a.eps, lane);
+          norm_rope<CPL>(cv, gw, d, a.rope_dim, a.pos0 + tok, a.log2_base, a.eps, lane);
           store_row<CPL>(a.win_rows + (int64_t(b) * a.n_new + tok) * d + lane * CPL, cv);
         }
       }
@@ -213,7 +231,7 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
     }
     p[j] = A / S;
   }
-  norm_rope<CPL>(p, a.norm_w, d, a.rope_dim, gi * m, a.log2_base, a.eps, lane);
+  norm_rope<CPL>(p, gw, d, a.rope_dim, gi * m, a.log2_base, a.eps, lane);
   store_row<CPL>(a.entries + (int64_t(b) * (a.n_new / m) + i) * d + lane * CPL, p);
 }
 
@@ -230,34 +248,51 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
 // taken from registers -- normalised, rotated at i m and written; the entry's indexer key is
 // quantised into the key cache (the encoders of csa_quantize_keys) and n_entries is advanced.
 
-// Quantise-on-write of one indexer key row (one wave): fp32 copy, fp8 e4m3 with a power-of-two
-// row scale, or MXFP4 (one lane per block of 32 values).
+// Quantise-on-write of one indexer key row (one wave; D_I % 32 == 0, <= 1024): lane l holds the
+// value pairs l, l + 64, ... (all loaded before any store).  fp32 copy, fp8 e4m3 with a
+// power-of-two row scale, or MXFP4 (a block of 32 values is the pairs of 16 lanes).
 __device__ void store_key_row(const AppendArgs &a, const uint16_t *x, int64_t row, int lane) {
-  const int D = a.D_I;
+  const int np = a.D_I / 2;
+  uint32_t w[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int q = lane + 64 * k;
+    w[k] = q < np ? reinterpret_cast<const uint32_t *>(x)[q] : 0u;
+  }
   if (a.key_format == 0) {
-    float *dst = static_cast<float *>(a.k_codes) + row * D;
-    for (int c = lane; c < D; c += 64) dst[c] = bf16_to_f32(x[c]);
+    float2 *dst = reinterpret_cast<float2 *>(static_cast<float *>(a.k_codes) + row * a.D_I);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (lane + 64 * k < np) dst[lane + 64 * k] = make_float2(bf16lo(w[k]), bf16hi(w[k]));
   } else if (a.key_format == 1) {
     float amax = 0.f;
-    for (int c = lane; c < D; c += 64) amax = fmaxf(amax, fabsf(bf16_to_f32(x[c])));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fmaxf(fabsf(bf16lo(w[k])), fabsf(bf16hi(w[k]))));
     amax = wave_max(amax);
     const int e = e4m3_row_exp(amax);
     const float inv = ldexpf(1.0f, -e);
-    uint8_t *dst = static_cast<uint8_t *>(a.k_codes) + row * D;
-    for (int c = lane; c < D; c += 64) dst[c] = uint8_t(f32_to_e4m3(bf16_to_f32(x[c]) * inv));
+    uint16_t *dst = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(a.k_codes) + row * a.D_I);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (lane + 64 * k < np)
+        dst[lane + 64 * k] = uint16_t(f32_to_e4m3(bf16lo(w[k]) * inv) | (f32_to_e4m3(bf16hi(w[k]) * inv) << 8));
     if (lane == 0) static_cast<float *>(a.k_scales)[row] = ldexpf(1.0f, e);
   } else {
-    const int nb = D / 32;
-    for (int blk = lane; blk < nb; blk += 64) {
-      const uint16_t *xb = x + 32 * blk;
-      float amax = 0.f;
-      for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(bf16_to_f32(xb[q])));
+    uint8_t *dst = static_cast<uint8_t *>(a.k_codes) + row * np;
+    uint8_t *sdst = static_cast<uint8_t *>(a.k_scales) + row * (a.D_I / 32);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (64 * k >= np) break;                                  // uniform
+      float amax = fmaxf(fabsf(bf16lo(w[k])), fabsf(bf16hi(w[k])));
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));   // the block's 16 lanes
       const uint32_t sb = mx_scale_byte(amax);
       const float inv = ldexpf(1.0f, 127 - int(sb));
-      uint8_t *dst = static_cast<uint8_t *>(a.k_codes) + row * (D / 2) + 16 * blk;
-      for (int q = 0; q < 16; ++q)
-        dst[q] = uint8_t(f32_to_e2m1(bf16_to_f32(xb[2 * q]) * inv) | (f32_to_e2m1(bf16_to_f32(xb[2 * q + 1]) * inv) << 4));
-      static_cast<uint8_t *>(a.k_scales)[row * nb + blk] = uint8_t(sb);
+      const int q = lane + 64 * k;
+      if (q < np) {
+        dst[q] = uint8_t(f32_to_e2m1(bf16lo(w[k]) * inv) | (f32_to_e2m1(bf16hi(w[k]) * inv) << 4));
+        if ((q & 15) == 0) sdst[q >> 4] = uint8_t(sb);
+      }
     }
   }
 }
@@ -274,56 +309,71 @@ __global__ void __launch_bounds__(256) decode_append_kernel(AppendArgs a) {
   RawRow<CPL> rc, rz;
   load_raw<CPL>(a.c_new + int64_t(b) * d + lane * CPL, rc);
   load_raw<CPL>(a.z_new + int64_t(b) * d + lane * CPL, rz);
-  if (wave == 0) {
-    store_raw<CPL>(a.tok_c + (ring0 + t % R) * d + lane * CPL, rc);
-    store_raw<CPL>(a.tok_z + (ring0 + t % R) * d + lane * CPL, rz);
-  } else if (wave == 1) {
-    float v[CPL];
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) v[j] = rc.at(j);
-    norm_rope<CPL>(v, a.norm_w, d, a.rope_dim, t, a.log2_base, a.eps, lane);
-    store_row<CPL>(a.win_ring + (int64_t(b) * a.W_cap + t % a.W_cap) * d + lane * CPL, v);
-  }
-  if ((t + 1) % m != 0) return;                                // no group closes at this token
-  const int64_t i = (t + 1) / m - 1;                           // the entry it closes
-  if (i >= a.N_cap) return;
-  const bool has_prev = a.overlap && i > 0;
-  const int nt = has_prev ? 2 * m : m;
-  const int64_t p_first = has_prev ? (i - 1) * m : i * m;
-  const int slot_first = has_prev ? 0 : (a.overlap ? m : 0);   // bias row of the first token
+  const NormWeights<CPL> gw = load_norm_weights<CPL>(a.norm_w, a.bias, lane);
+  const int64_t i = (t + 1) / m - 1;                           // the entry this token closes, if any
+  const bool closes = (t + 1) % m == 0 && i < a.N_cap;         // uniform over the workgroup
 
-  float mx[CPL], sm[CPL], acc[CPL];
+  __shared__ float s_state[3][4][64 * CPL];
+  if (closes) {
+    // pooling first (its loads are the longest chain); the four waves split the entry's tokens
+    const bool has_prev = a.overlap && i > 0;
+    const int nt = has_prev ? 2 * m : m;
+    const int64_t p_first = has_prev ? (i - 1) * m : i * m;
+    const int slot_first = has_prev ? 0 : (a.overlap ? m : 0); // bias row of the first token
+    float mx[CPL], sm[CPL], acc[CPL];
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) { mx[j] = -INFINITY; sm[j] = 0.f; acc[j] = 0.f; }
-  const int per = (nt + 3) >> 2;
-  const int k0 = wave * per, k1 = min(nt, k0 + per);
-  for (int k = k0; k < k1; ++k) {
-    const int64_t p = p_first + k;
-    RawRow<CPL> xc = rc, xz = rz, xb;
-    if (p != t) {                                              // older tokens come from the ring
-      load_raw<CPL>(a.tok_c + (ring0 + p % R) * d + lane * CPL, xc);
-      load_raw<CPL>(a.tok_z + (ring0 + p % R) * d + lane * CPL, xz);
+    for (int j = 0; j < CPL; ++j) { mx[j] = -INFINITY; sm[j] = 0.f; acc[j] = 0.f; }
+    const int per = (nt + 3) >> 2;
+    const int k0 = wave * per, k1 = min(nt, k0 + per);
+    const int ring_first = int(p_first % R);                   // ring slot of the entry's first token
+    // groups of 4 tokens, their loads in flight together; the token at t comes from registers
+    // (its ring row is written by this launch), and past the wave's last token the loads repeat
+    // that token (in bounds) with logit -inf
+    constexpr int U = 4;
+    for (int k = k0; k < k1; k += U) {
+      RawRow<CPL> xc[U], xz[U], xb[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kk = min(k + u, k1 - 1);
+        const int slot = (ring_first + kk) % R;
+        load_raw<CPL>(a.tok_c + (ring0 + slot) * d + lane * CPL, xc[u]);
+        load_raw<CPL>(a.tok_z + (ring0 + slot) * d + lane * CPL, xz[u]);
+        load_raw<CPL>(a.bias + int64_t(slot_first + kk) * d + lane * CPL, xb[u]);
+        if (p_first + kk == t) { xc[u] = rc; xz[u] = rz; }
+      }
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        float l[U], gm = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          l[u] = k + u < k1 ? (xz[u].at(j) + xb[u].at(j)) * kLog2e : -INFINITY;
+          gm = fmaxf(gm, l[u]);
+        }
+        const float nm = fmaxf(mx[j], gm);
+        const float sc = exp2f(mx[j] - nm);
+        float es = 0.f, ea = 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float e = exp2f(l[u] - nm);
+          es += e;
+          ea += e * xc[u].at(j);
+        }
+        sm[j] = sm[j] * sc + es;
+        acc[j] = acc[j] * sc + ea;
+        mx[j] = nm;
+      }
     }
-    load_raw<CPL>(a.bias + int64_t(slot_first + k) * d + lane * CPL, xb);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-      const float l = (xz.at(j) + xb.at(j)) * kLog2e;
-      const float nm = fmaxf(mx[j], l);
-      const float sc = exp2f(mx[j] - nm), e = exp2f(l - nm);
-      sm[j] = sm[j] * sc + e;
-      acc[j] = acc[j] * sc + e * xc.at(j);
-      mx[j] = nm;
+      s_state[0][wave][lane * CPL + j] = mx[j];
+      s_state[1][wave][lane * CPL + j] = sm[j];
+      s_state[2][wave][lane * CPL + j] = acc[j];
     }
+    lds_barrier();
   }
-  __shared__ float s_state[3][4][64 * CPL];
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    s_state[0][wave][lane * CPL + j] = mx[j];
-    s_state[1][wave][lane * CPL + j] = sm[j];
-    s_state[2][wave][lane * CPL + j] = acc[j];
-  }
-  lds_barrier();
+  // then one job per wave: the entry, its key, the token's window row, the token's ring rows
   if (wave == 0) {
+    if (!closes) return;
     float pv[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
@@ -339,11 +389,20 @@ __global__ void __launch_bounds__(256) decode_append_kernel(AppendArgs a) {
       }
       pv[j] = A / S;
     }
-    norm_rope<CPL>(pv, a.norm_w, d, a.rope_dim, i * m, a.log2_base, a.eps, lane);
+    norm_rope<CPL>(pv, gw, d, a.rope_dim, i * m, a.log2_base, a.eps, lane);
     store_row<CPL>(a.entries + (int64_t(b) * a.N_cap + i) * d + lane * CPL, pv);
     if (lane == 0) a.n_entries[b] = i + 1;
-  } else if (wave == 1 && a.k_new) {
-    store_key_row(a, a.k_new + int64_t(b) * a.D_I, int64_t(b) * a.N_cap + i, lane);
+  } else if (wave == 1) {
+    if (closes && a.k_new) store_key_row(a, a.k_new + int64_t(b) * a.D_I, int64_t(b) * a.N_cap + i, lane);
+  } else if (wave == 2) {
+    float v[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) v[j] = rc.at(j);
+    norm_rope<CPL>(v, gw, d, a.rope_dim, t, a.log2_base, a.eps, lane);
+    store_row<CPL>(a.win_ring + (int64_t(b) * a.W_cap + t % a.W_cap) * d + lane * CPL, v);
+  } else {
+    store_raw<CPL>(a.tok_c + (ring0 + t % R) * d + lane * CPL, rc);
+    store_raw<CPL>(a.tok_z + (ring0 + t % R) * d + lane * CPL, rz);
   }
 }
 

@@ -113,8 +113,8 @@ csa_status csa_compress(const uint16_t *c, const uint16_t *z, const uint16_t *bi
  *   n_entries     device int64 [B], written when an entry completes.
  * The caches are device memory owned by the caller; the ring rows of positions before the first
  * appended token are never read when the sequence starts at position 0.
- * Limits: d in {64, 128, 256, 512, 1024}; 1 <= m <= 1024; rope_dim % 4 == 0; 1 <= D_I <= 1024
- * (MXFP4: D_I % 32 == 0); W_cap, N_cap in [1, 2^31).
+ * Limits: d in {64, 128, 256, 512, 1024}; 1 <= m <= 1024; rope_dim % 4 == 0; D_I a multiple of
+ * 32 in [32, 1024]; W_cap, N_cap in [1, 2^31).
  */
 csa_status csa_decode_append(const uint16_t *c_new, const uint16_t *z_new, const uint16_t *k_new,
                              const int64_t *pos, const uint16_t *bias, const uint16_t *norm_w, int B,
