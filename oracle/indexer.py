@@ -46,6 +46,26 @@ def quantize_keys(k: np.ndarray, fmt: str):
     return np.asarray(k, dtype=np.float64), None
 
 
+def compress_keys(c_i, z_i, bias_i, m: int, overlap: int, pos_first: int = 0):
+    """Indexer keys of the compressed entries, produced by compression of a per-token stream.
+
+    [EXPLAINER] CSA walk-through: the lightning indexer scores compressed blocks, so each entry
+    carries its own indexer key; the compressor makes every entry from its group of tokens by a
+    learned softmax weighting.  [RABBIT] indexer paragraph: the indexer works on smaller
+    representations (a narrower key than the attention rows).
+
+    Reading: a per-token indexer stream c_i [T, D_I] with logits z_i and position bias bias_i
+    [(1+overlap) m, D_I] is pooled exactly as the KV compressor pools (same token groups, same
+    per-channel softmax), with no RMSNorm and no rotation (the keys are used as they are).
+    Returns (keys [n, D_I] float64, first entry index).
+    """
+    from .compress import entry_range, pool_entry
+    lo, hi = entry_range(pos_first, c_i.shape[0], m, overlap)
+    keys = np.stack([pool_entry(c_i, z_i, bias_i, i, m, overlap, pos_first)[0] for i in range(lo, hi)]) \
+        if hi > lo else np.zeros((0, c_i.shape[1]))
+    return keys, lo
+
+
 def dequantize_keys(codes, scales, fmt: str) -> np.ndarray:
     if fmt == "fp8":
         return quant.dequantize_fp8_rows(codes, scales)

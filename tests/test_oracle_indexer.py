@@ -94,3 +94,39 @@ def test_topk_ties_go_to_lower_index_and_padding():
     np.testing.assert_array_equal(oi.topk_fast(s, 3, 6), [1, 2, 4])
     s2 = np.zeros(50)
     np.testing.assert_array_equal(oi.topk_fast(s2, 5, 50), [0, 1, 2, 3, 4])
+
+
+# ---- indexer keys produced by compression ----------------------------------------------------
+def test_compressed_keys_pool_like_the_kv_compressor():
+    # Special case -> library: zero logits and bias make every weight equal, so each key is the
+    # plain mean of its tokens (torch's avg_pool1d, independently); without overlap the groups
+    # are the pooling windows.
+    import torch
+    rng = np.random.default_rng(5)
+    T, D, m = 48, 32, 4
+    x = rng.standard_normal((T, D))
+    keys, lo = oi.compress_keys(x, np.zeros((T, D)), np.zeros((m, D)), m, 0)
+    ref = torch.nn.functional.avg_pool1d(torch.from_numpy(x.T[None]), m).numpy()[0].T
+    assert lo == 0 and keys.shape == (T // m, D)
+    np.testing.assert_allclose(keys, ref, rtol=0, atol=1e-12)
+
+
+def test_compressed_keys_of_a_constant_stream_are_the_constant():
+    # the pooling weights sum to one in every channel, whatever the logits: a constant token row
+    # compresses to itself (with overlap too, including entry 0 with no previous group)
+    rng = np.random.default_rng(6)
+    T, D, m = 40, 16, 4
+    v = rng.standard_normal(D)
+    keys, _ = oi.compress_keys(np.tile(v, (T, 1)), rng.standard_normal((T, D)),
+                               0.3 * rng.standard_normal((2 * m, D)), m, 1)
+    np.testing.assert_allclose(keys, np.tile(v, (T // m, 1)), rtol=0, atol=1e-12)
+
+
+def test_compressed_keys_are_not_normalised():
+    # scaling the stream scales the keys (an RMSNorm would undo it)
+    rng = np.random.default_rng(8)
+    T, D, m = 32, 16, 4
+    x, z, b = rng.standard_normal((T, D)), rng.standard_normal((T, D)), rng.standard_normal((2 * m, D))
+    k1, _ = oi.compress_keys(x, z, b, m, 1)
+    k3, _ = oi.compress_keys(3.0 * x, z, b, m, 1)
+    np.testing.assert_allclose(k3, 3.0 * k1, rtol=1e-12, atol=1e-12)
