@@ -105,9 +105,15 @@ class Leg:
                 self.tok_z = [bf(w.B, R, w.d) for _ in range(self.ncopies)]
                 self.c_new = [bf(w.B, w.d) for _ in range(self.ncopies)]
                 self.z_new = [bf(w.B, w.d) for _ in range(self.ncopies)]
-                self.k_new = [bf(w.B, w.D_I) for _ in range(self.ncopies)]
                 self.bias = bf(R, w.d, std=0.1)
                 self.n_app = self.n_ent.clone()
+                # the indexer stream: its ring, the new token's row and logits, its bias; the
+                # closed entry's key is produced by compression and quantised on write
+                self.tok_ci = [bf(w.B, R, w.D_I) for _ in range(self.ncopies)]
+                self.tok_zi = [bf(w.B, R, w.D_I) for _ in range(self.ncopies)]
+                self.c_i_new = [bf(w.B, w.D_I) for _ in range(self.ncopies)]
+                self.z_i_new = [bf(w.B, w.D_I) for _ in range(self.ncopies)]
+                self.bias_i = bf(R, w.D_I, std=0.1)
         else:
             self.ws_a = ops.hca_workspace(w.B, 1, w.H, w.d, w.N, w.window)
         del x
@@ -119,8 +125,10 @@ class Leg:
         if w.kind == "csa_decode" and self.append:
             ops.csa_decode_append(self.c_new[c], self.z_new[c], self.t, self.bias, m=w.m, overlap=w.overlap,
                                   rope_dim=w.rope_dim, tok_c=self.tok_c[c], tok_z=self.tok_z[c], win_ring=self.win[c],
-                                  entries=self.ent[c], n_entries=self.n_app, k_new=self.k_new[c],
-                                  key_format=w.key_format, k_codes=self.codes[c], k_scales=self.scales[c])
+                                  entries=self.ent[c], n_entries=self.n_app)
+            ops.csa_decode_append_index(self.c_i_new[c], self.z_i_new[c], self.t, self.bias_i, m=w.m,
+                                        overlap=w.overlap, tok_c=self.tok_ci[c], tok_z=self.tok_zi[c],
+                                        key_format=w.key_format, k_codes=self.codes[c], k_scales=self.scales[c])
             ops.csa_index_topk(self.q_idx[c], self.w_idx[c], self.codes[c], self.scales[c], key_format=w.key_format,
                                n_entries=self.n_app, q_pos0=self.t, m=w.m, topk=w.topk, workspace=self.ws_i,
                                topk_out=self.sel[c])
@@ -147,7 +155,8 @@ class Leg:
             self.step(i)
         torch.cuda.synchronize()
         res = {}
-        for k in ("decode_append", "index_score", "index_merge", "attend_split", "attend_combine"):
+        for k in ("decode_append", "decode_append_keys", "index_score", "index_merge", "attend_split",
+                  "attend_combine"):
             ms, cnt = ops.timing_read(k)
             if cnt:
                 res[k] = 1000.0 * ms / cnt
@@ -271,8 +280,9 @@ def copy_calibration():
 # ---- prefill chunk and compressor legs ------------------------------------------------------------
 class PrefillLeg:
     """One prefill chunk: compress 4,096 new tokens (plus the m-token halo) into 1,024 entries
-    appended after the 32,768 existing ones (and their prepared window rows), quantise the new
-    entries' indexer keys, then csa_index_topk and csa_attend for all 4,096 query tokens."""
+    appended after the 32,768 existing ones (and their prepared window rows), produce the new
+    entries' indexer keys by compressing the chunk's per-token indexer stream (quantised on
+    write), then csa_index_topk and csa_attend for all 4,096 query tokens."""
 
     def __init__(self, w: gen.Workload):
         self.w = w
@@ -293,6 +303,11 @@ class PrefillLeg:
         self.win = torch.empty((1, self.W_cap, d), dtype=torch.bfloat16, device="cuda")
         self.win[:, :self.Wp] = dev_bf16(gen.normal_bf16(w.cfg, gen.T_WIN, (self.Wp, d))).view(1, self.Wp, d)
         self.codes, self.scales = ops.csa_quantize_keys(self.k_idx, w.key_format)   # existing keys
+        # the chunk's per-token indexer stream (plus the halo), its logits and position bias
+        self.c_i = dev_bf16(gen.normal_bf16(w.cfg, gen.T_KIDX, (n + m, w.D_I), row0=self.N_cap,
+                                            nrows=n + m)).view(1, n + m, w.D_I)
+        self.z_i = dev_bf16(gen.normal_bf16(w.cfg, gen.T_Z, (n + m, w.D_I))).view(1, n + m, w.D_I)
+        self.bias_i = dev_bf16(gen.normal_bf16(w.cfg, gen.T_BIAS, (2 * m, w.D_I), std=0.1))
         self.n_ent = torch.tensor([self.N_cap], dtype=torch.int64, device="cuda")
         self.t = torch.tensor([w.T], dtype=torch.int64, device="cuda")
         self.win_pos0 = torch.tensor([w.T - self.Wp], dtype=torch.int64, device="cuda")
@@ -311,8 +326,9 @@ class PrefillLeg:
         w = self.w
         ops.csa_compress(self.c, self.z, self.bias, m=w.m, overlap=w.overlap, rope_dim=w.rope_dim, pos0=w.T,
                          win_rows=True, entries_out=self.entries[:, self.N0:], win_rows_out=self.win[:, self.Wp:])
-        ops.csa_quantize_keys(self.k_idx[:, self.N0:], w.key_format, codes_out=self.codes[:, self.N0:],
-                              scales_out=self.scales[:, self.N0:])
+        ops.csa_compress_index_keys(self.c_i, self.z_i, self.bias_i, m=w.m, overlap=w.overlap,
+                                    key_format=w.key_format, pos0=w.T, k_codes=self.codes[:, self.N0:],
+                                    k_scales=self.scales[:, self.N0:])
         ops.csa_index_topk(self.q_idx, self.w_idx, self.codes, self.scales, key_format=w.key_format,
                            n_entries=self.n_ent, q_pos0=self.t, m=w.m, topk=w.topk, workspace=self.ws_i,
                            topk_out=self.sel)
@@ -328,7 +344,7 @@ class PrefillLeg:
             self.step()
         torch.cuda.synchronize()
         kt = {}
-        for k in ("compress", "quantize", "index_score", "index_merge", "attend_split", "attend_combine"):
+        for k in ("compress", "compress_keys", "index_score", "index_merge", "attend_split", "attend_combine"):
             ms, cnt = ops.timing_read(k)
             if cnt:
                 kt[k] = 1000.0 * ms / cnt

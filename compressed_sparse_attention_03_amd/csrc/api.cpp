@@ -191,6 +191,64 @@ csa_status csa_decode_append(const uint16_t *c_new, const uint16_t *z_new, const
   return launched(e, "decode_append launch");
 }
 
+static csa_status check_key_cache(int D_I, int key_format, void *k_codes, void *k_scales) {
+  if (!(D_I == 128 || D_I == 256 || D_I == 512 || D_I == 1024))
+    return fail(CSA_ERR_UNSUPPORTED, "D_I must be one of 128, 256, 512, 1024 (got %d)", D_I);
+  REQUIRE(key_format == CSA_KEY_F32 || key_format == CSA_KEY_FP8_E4M3 || key_format == CSA_KEY_MXFP4,
+          "unknown key_format %d", key_format);
+  REQUIRE_PTR(k_codes);
+  if (key_format != CSA_KEY_F32) REQUIRE_PTR(k_scales);
+  return CSA_OK;
+}
+
+csa_status csa_compress_index_keys(const uint16_t *c_i, const uint16_t *z_i, const uint16_t *bias_i, int B,
+                                   int64_t n_new, int halo, int D_I, int m, int overlap, int64_t pos0,
+                                   int key_format, uint16_t *keys_out, void *k_codes, void *k_scales,
+                                   void *stream) {
+  REQUIRE(B >= 0 && B <= 65535, "B must be in [0, 65535]");
+  REQUIRE(n_new >= 0, "n_new must be >= 0");
+  REQUIRE(m >= 1 && m <= 1024, "m must be in [1, 1024]");
+  REQUIRE(overlap == 0 || overlap == 1, "overlap must be 0 or 1");
+  REQUIRE(pos0 >= 0 && pos0 % m == 0, "pos0 must be a non-negative multiple of m");
+  REQUIRE(n_new % m == 0, "n_new must be a multiple of m");
+  REQUIRE(halo == ((overlap && pos0 > 0) ? m : 0), "halo must be m when overlap && pos0 > 0, else 0");
+  REQUIRE(n_new / m <= 2147483647LL, "too many entries");
+  if (B == 0 || n_new == 0) return CSA_OK;
+  csa_status s = check_key_cache(D_I, key_format, k_codes, k_scales);
+  if (s != CSA_OK) return s;
+  REQUIRE_PTR(c_i); REQUIRE_PTR(z_i); REQUIRE_PTR(bias_i); REQUIRE_PTR_OR_NULL(keys_out);
+  csa::CompressArgs a{};
+  a.c = c_i; a.z = z_i; a.bias = bias_i; a.norm_w = nullptr; a.entries = keys_out; a.win_rows = nullptr;
+  a.B = B; a.d = D_I; a.m = m; a.overlap = overlap; a.rope_dim = 0; a.halo = halo; a.n_new = n_new;
+  a.pos0 = pos0; a.log2_base = 1.0; a.eps = 1e-6f; a.key_format = key_format; a.k_codes = k_codes;
+  a.k_scales = k_scales;
+  hipError_t e = csa::launch_compress_keys(a, static_cast<hipStream_t>(stream));
+  return launched(e, "compress_index_keys launch");
+}
+
+csa_status csa_decode_append_index(const uint16_t *c_i_new, const uint16_t *z_i_new, const int64_t *pos,
+                                   const uint16_t *bias_i, int B, int D_I, int m, int overlap, uint16_t *tok_c,
+                                   uint16_t *tok_z, int64_t N_cap, int key_format, uint16_t *keys_out,
+                                   void *k_codes, void *k_scales, void *stream) {
+  REQUIRE(B >= 0 && B <= 65535, "B must be in [0, 65535]");
+  REQUIRE(m >= 1 && m <= 1024, "m must be in [1, 1024]");
+  REQUIRE(overlap == 0 || overlap == 1, "overlap must be 0 or 1");
+  REQUIRE(N_cap >= 1 && N_cap < (int64_t(1) << 31), "N_cap must be in [1, 2^31)");
+  if (B == 0) return CSA_OK;
+  csa_status s = check_key_cache(D_I, key_format, k_codes, k_scales);
+  if (s != CSA_OK) return s;
+  REQUIRE_PTR(c_i_new); REQUIRE_PTR(z_i_new); REQUIRE_PTR(pos); REQUIRE_PTR(bias_i);
+  REQUIRE_PTR(tok_c); REQUIRE_PTR(tok_z); REQUIRE_PTR_OR_NULL(keys_out);
+  csa::AppendArgs a{};
+  a.c_new = c_i_new; a.z_new = z_i_new; a.k_new = nullptr; a.bias = bias_i; a.norm_w = nullptr; a.pos = pos;
+  a.tok_c = tok_c; a.tok_z = tok_z; a.win_ring = nullptr; a.entries = keys_out; a.k_codes = k_codes;
+  a.k_scales = k_scales; a.n_entries = nullptr; a.W_cap = 1; a.N_cap = N_cap; a.B = B; a.d = D_I; a.m = m;
+  a.overlap = overlap; a.rope_dim = 0; a.key_format = key_format; a.D_I = D_I; a.log2_base = 1.0;
+  a.eps = 1e-6f;
+  hipError_t e = csa::launch_append_keys(a, static_cast<hipStream_t>(stream));
+  return launched(e, "decode_append_index launch");
+}
+
 csa_status csa_quantize_keys(const uint16_t *x, int64_t rows, int dim, int format, void *codes,
                              void *scales, void *stream) {
   REQUIRE(format == CSA_KEY_FP8_E4M3 || format == CSA_KEY_MXFP4, "format must be CSA_KEY_FP8_E4M3 or CSA_KEY_MXFP4");

@@ -94,6 +94,46 @@ __device__ __forceinline__ NormWeights<CPL> load_norm_weights(const uint16_t *g,
   return n;
 }
 
+// Quantise-on-write of a key row held as CPL consecutive channels per lane (one wave, d = 64 CPL,
+// CPL >= 2), the values already rounded to bf16: fp32 copy (format 0), fp8 e4m3 with a
+// power-of-two row scale (1), MXFP4 with 32/CPL lanes per block of 32 (2) -- the encoders and
+// rules of csa_quantize_keys.
+template <int CPL>
+__device__ __forceinline__ void encode_key_lanes(const float (&v)[CPL], int fmt, int d, void *codes, void *scales,
+                                                 int64_t row, int lane) {
+  static_assert(CPL >= 2 && CPL <= 16, "two to sixteen channels per lane");
+  if (fmt == 0) {
+    float *dst = static_cast<float *>(codes) + row * d + lane * CPL;
+#pragma unroll
+    for (int j = 0; j < CPL; j += 2) *reinterpret_cast<float2 *>(dst + j) = make_float2(v[j], v[j + 1]);
+  } else if (fmt == 1) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = wave_max(amax);
+    const int e = e4m3_row_exp(amax);
+    const float inv = ldexpf(1.0f, -e);
+    uint8_t *dst = static_cast<uint8_t *>(codes) + row * d + lane * CPL;
+#pragma unroll
+    for (int j = 0; j < CPL; j += 2)
+      *reinterpret_cast<uint16_t *>(dst + j) = uint16_t(f32_to_e4m3(v[j] * inv) | (f32_to_e4m3(v[j + 1] * inv) << 8));
+    if (lane == 0) static_cast<float *>(scales)[row] = ldexpf(1.0f, e);
+  } else {
+    constexpr int LB = 32 / CPL;                    // lanes per block of 32 values
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) amax = fmaxf(amax, fabsf(v[j]));
+#pragma unroll
+    for (int o = 1; o < LB; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const uint32_t sb = mx_scale_byte(amax);
+    const float inv = ldexpf(1.0f, 127 - int(sb));
+    uint8_t *dst = static_cast<uint8_t *>(codes) + row * (d / 2) + lane * (CPL / 2);
+#pragma unroll
+    for (int j = 0; j < CPL; j += 2) dst[j / 2] = uint8_t(f32_to_e2m1(v[j] * inv) | (f32_to_e2m1(v[j + 1] * inv) << 4));
+    if (lane % LB == 0) static_cast<uint8_t *>(scales)[row * (d / 32) + lane / LB] = uint8_t(sb);
+  }
+}
+
 // RMSNorm (weights gw) then rotation of the channels >= d - r at position pos.
 // Every lane of the wave must call this (it reduces across the wave).
 template <int CPL>
@@ -133,7 +173,7 @@ __device__ __forceinline__ void norm_rope(float (&v)[CPL], const NormWeights<CPL
   }
 }
 
-template <int CPL, int U, bool WIN>
+template <int CPL, int U, bool WIN, bool KEYS>
 __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
   const int d = a.d, m = a.m;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -231,8 +271,17 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
     }
     p[j] = A / S;
   }
-  norm_rope<CPL>(p, gw, d, a.rope_dim, gi * m, a.log2_base, a.eps, lane);
-  store_row<CPL>(a.entries + (int64_t(b) * (a.n_new / m) + i) * d + lane * CPL, p);
+  const int64_t row = int64_t(b) * (a.n_new / m) + i;
+  if constexpr (KEYS) {
+    // an indexer key: pooled only, rounded to bf16 as a stored key would be, then quantised
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) p[j] = bf16_to_f32(f32_to_bf16(p[j]));
+    if (a.entries) store_row<CPL>(a.entries + row * d + lane * CPL, p);
+    encode_key_lanes<CPL>(p, a.key_format, d, a.k_codes, a.k_scales, row, lane);
+  } else {
+    norm_rope<CPL>(p, gw, d, a.rope_dim, gi * m, a.log2_base, a.eps, lane);
+    store_row<CPL>(a.entries + row * d + lane * CPL, p);
+  }
 }
 
 // ---- decode-time cache maintenance --------------------------------------------------------
@@ -297,7 +346,7 @@ __device__ void store_key_row(const AppendArgs &a, const uint16_t *x, int64_t ro
   }
 }
 
-template <int CPL>
+template <int CPL, bool KEYS>
 __global__ void __launch_bounds__(256) decode_append_kernel(AppendArgs a) {
   const int d = a.d, m = a.m;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -374,6 +423,28 @@ __global__ void __launch_bounds__(256) decode_append_kernel(AppendArgs a) {
   // then one job per wave: the entry, its key, the token's window row, the token's ring rows
   if (wave == 0) {
     if (!closes) return;
+    if constexpr (KEYS) {
+      // the indexer stream: the pooled key, rounded to bf16 and quantised into the key cache
+      float kv[CPL];
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int ch = lane * CPL + j;
+        float M = fmaxf(fmaxf(s_state[0][0][ch], s_state[0][1][ch]), fmaxf(s_state[0][2][ch], s_state[0][3][ch]));
+        float S = 0.f, A = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float mw = s_state[0][w][ch];
+          const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+          S += s_state[1][w][ch] * f;
+          A += s_state[2][w][ch] * f;
+        }
+        kv[j] = bf16_to_f32(f32_to_bf16(A / S));
+      }
+      const int64_t row = int64_t(b) * a.N_cap + i;
+      if (a.entries) store_row<CPL>(a.entries + row * d + lane * CPL, kv);
+      encode_key_lanes<CPL>(kv, a.key_format, d, a.k_codes, a.k_scales, row, lane);
+      return;
+    }
     float pv[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
@@ -393,8 +464,9 @@ __global__ void __launch_bounds__(256) decode_append_kernel(AppendArgs a) {
     store_row<CPL>(a.entries + (int64_t(b) * a.N_cap + i) * d + lane * CPL, pv);
     if (lane == 0) a.n_entries[b] = i + 1;
   } else if (wave == 1) {
-    if (closes && a.k_new) store_key_row(a, a.k_new + int64_t(b) * a.D_I, int64_t(b) * a.N_cap + i, lane);
+    if (!KEYS && closes && a.k_new) store_key_row(a, a.k_new + int64_t(b) * a.D_I, int64_t(b) * a.N_cap + i, lane);
   } else if (wave == 2) {
+    if (KEYS) return;
     float v[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) v[j] = rc.at(j);
@@ -411,10 +483,20 @@ hipError_t launch_compress_win(const CompressArgs &a, dim3 grid, hipStream_t str
   // Tokens per wave: 2m with the previous group (every entry but the sequence's first), else m.
   const int per = ((a.overlap ? 2 * a.m : a.m) + 3) / 4;
   const dim3 block(256);
-  if (per >= 8) return launch("compress", compress_kernel<CPL, 8, WIN>, grid, block, stream, a);
-  if (per >= 4) return launch("compress", compress_kernel<CPL, 4, WIN>, grid, block, stream, a);
-  if (per >= 2) return launch("compress", compress_kernel<CPL, 2, WIN>, grid, block, stream, a);
-  return launch("compress", compress_kernel<CPL, 1, WIN>, grid, block, stream, a);
+  if (per >= 8) return launch("compress", compress_kernel<CPL, 8, WIN, false>, grid, block, stream, a);
+  if (per >= 4) return launch("compress", compress_kernel<CPL, 4, WIN, false>, grid, block, stream, a);
+  if (per >= 2) return launch("compress", compress_kernel<CPL, 2, WIN, false>, grid, block, stream, a);
+  return launch("compress", compress_kernel<CPL, 1, WIN, false>, grid, block, stream, a);
+}
+
+template <int CPL>
+hipError_t launch_compress_keys_cpl(const CompressArgs &a, dim3 grid, hipStream_t stream) {
+  const int per = ((a.overlap ? 2 * a.m : a.m) + 3) / 4;
+  const dim3 block(256);
+  if (per >= 8) return launch("compress_keys", compress_kernel<CPL, 8, false, true>, grid, block, stream, a);
+  if (per >= 4) return launch("compress_keys", compress_kernel<CPL, 4, false, true>, grid, block, stream, a);
+  if (per >= 2) return launch("compress_keys", compress_kernel<CPL, 2, false, true>, grid, block, stream, a);
+  return launch("compress_keys", compress_kernel<CPL, 1, false, true>, grid, block, stream, a);
 }
 
 // The per-token window rows (normalised and rotated token rows) are a separate instantiation:
@@ -430,11 +512,33 @@ hipError_t launch_compress_cpl(const CompressArgs &a, dim3 grid, hipStream_t str
 hipError_t launch_append(const AppendArgs &a, hipStream_t stream) {
   const dim3 grid(unsigned(a.B)), block(256);
   switch (a.d / 64) {
-    case 1: return launch("decode_append", decode_append_kernel<1>, grid, block, stream, a);
-    case 2: return launch("decode_append", decode_append_kernel<2>, grid, block, stream, a);
-    case 4: return launch("decode_append", decode_append_kernel<4>, grid, block, stream, a);
-    case 8: return launch("decode_append", decode_append_kernel<8>, grid, block, stream, a);
-    case 16: return launch("decode_append", decode_append_kernel<16>, grid, block, stream, a);
+    case 1: return launch("decode_append", decode_append_kernel<1, false>, grid, block, stream, a);
+    case 2: return launch("decode_append", decode_append_kernel<2, false>, grid, block, stream, a);
+    case 4: return launch("decode_append", decode_append_kernel<4, false>, grid, block, stream, a);
+    case 8: return launch("decode_append", decode_append_kernel<8, false>, grid, block, stream, a);
+    case 16: return launch("decode_append", decode_append_kernel<16, false>, grid, block, stream, a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_append_keys(const AppendArgs &a, hipStream_t stream) {
+  const dim3 grid(unsigned(a.B)), block(256);
+  switch (a.d / 64) {
+    case 2: return launch("decode_append_keys", decode_append_kernel<2, true>, grid, block, stream, a);
+    case 4: return launch("decode_append_keys", decode_append_kernel<4, true>, grid, block, stream, a);
+    case 8: return launch("decode_append_keys", decode_append_kernel<8, true>, grid, block, stream, a);
+    case 16: return launch("decode_append_keys", decode_append_kernel<16, true>, grid, block, stream, a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_compress_keys(const CompressArgs &a, hipStream_t stream) {
+  const dim3 grid(unsigned(a.n_new / a.m), unsigned(a.B));
+  switch (a.d / 64) {
+    case 2: return launch_compress_keys_cpl<2>(a, grid, stream);
+    case 4: return launch_compress_keys_cpl<4>(a, grid, stream);
+    case 8: return launch_compress_keys_cpl<8>(a, grid, stream);
+    case 16: return launch_compress_keys_cpl<16>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -15,8 +15,13 @@ struct CompressArgs {
   int64_t n_new, pos0;
   double log2_base;
   float eps;
+  // indexer keys (launch_compress_keys): pooled only, rounded to bf16 (entries: optional bf16
+  // copy) and quantised into k_codes / k_scales in key_format
+  int key_format;
+  void *k_codes, *k_scales;
 };
 hipError_t launch_compress(const CompressArgs &a, hipStream_t stream);
+hipError_t launch_compress_keys(const CompressArgs &a, hipStream_t stream);
 
 // Decode-time cache maintenance: one new token per sequence (see csa_decode_append).
 struct AppendArgs {
@@ -31,6 +36,8 @@ struct AppendArgs {
   float eps;
 };
 hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
+// the indexer stream's ring and keys (d = D_I; entries: optional bf16 keys [B, N_cap, D_I])
+hipError_t launch_append_keys(const AppendArgs &a, hipStream_t stream);
 
 struct QuantizeArgs {
   const uint16_t *x;

@@ -27,6 +27,8 @@ I32, I64, F32, SZ = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_
 _SIGS = {
     "csa_compress": (I32, [P, P, P, P, I32, I64, I32, I32, I32, I32, I32, I64, F32, F32, P, P, P]),
     "csa_quantize_keys": (I32, [P, I64, I32, I32, P, P, P]),
+    "csa_compress_index_keys": (I32, [P, P, P, I32, I64, I32, I32, I32, I32, I64, I32, P, P, P, P]),
+    "csa_decode_append_index": (I32, [P, P, P, P, I32, I32, I32, I32, P, P, I64, I32, P, P, P, P]),
     "csa_decode_append": (I32, [P, P, P, P, P, P, I32, I32, I32, I32, I32, F32, F32, P, P, P, I64, P, I64,
                                 I32, I32, P, P, P, P]),
     "csa_index_topk": (I32, [P, P, P, P, I32, I32, I32, I32, I32, I64, P, P, I32, I32, P, P, P, SZ, P]),
@@ -142,6 +144,81 @@ def csa_quantize_keys(x, fmt, codes_out=None, scales_out=None):
     st = lib().csa_quantize_keys(_ptr(x), rows, dim, f, _ptr(codes), _ptr(scales), _stream())
     _check(st, "csa_quantize_keys")
     return codes, scales
+
+
+def _key_cache_shapes(lead, D_I, f):
+    if f == KEY_F32:
+        return (lead + (D_I,), torch.float32), None
+    if f == KEY_FP8_E4M3:
+        return (lead + (D_I,), torch.uint8), (lead, torch.float32)
+    return (lead + (D_I // 2,), torch.uint8), (lead + (D_I // 32,), torch.uint8)
+
+
+def _check_key_cache(k_codes, k_scales, lead, D_I, f):
+    cs, ss = _key_cache_shapes(lead, D_I, f)
+    _dev(k_codes, "k_codes", cs[1])
+    if tuple(k_codes.shape) != cs[0]:
+        raise ValueError(f"k_codes must have shape {cs[0]}")
+    if ss is not None:
+        _dev(k_scales, "k_scales", ss[1])
+        if tuple(k_scales.shape) != ss[0]:
+            raise ValueError(f"k_scales must have shape {ss[0]}")
+
+
+def csa_compress_index_keys(c_i, z_i, bias_i, *, m, overlap, key_format, pos0=0, keys_out=False,
+                            k_codes=None, k_scales=None):
+    """Indexer keys by compression of the per-token stream c_i/z_i [B, halo+n_new, D_I]:
+    (codes, scales, bf16 keys or None) for entries pos0/m .. in ``key_format``."""
+    _dev(c_i, "c_i", torch.bfloat16, 3)
+    _dev(z_i, "z_i", torch.bfloat16, 3)
+    _dev(bias_i, "bias_i", torch.bfloat16, 2)
+    B, rows, D_I = c_i.shape
+    if z_i.shape != c_i.shape:
+        raise ValueError("z_i must have the shape of c_i")
+    halo = m if (overlap and pos0 > 0) else 0
+    n_new = rows - halo
+    n_out = max(n_new, 0) // m
+    f = KEY_FORMATS[key_format]
+    cs, ss = _key_cache_shapes((B, n_out), D_I, f)
+    codes = k_codes if k_codes is not None else torch.empty(cs[0], dtype=cs[1], device=c_i.device)
+    scales = None
+    if ss is not None:
+        scales = k_scales if k_scales is not None else torch.empty(ss[0], dtype=ss[1], device=c_i.device)
+    _check_key_cache(codes, scales, (B, n_out), D_I, f)
+    ko = torch.empty((B, n_out, D_I), dtype=torch.bfloat16, device=c_i.device) if keys_out else None
+    st = lib().csa_compress_index_keys(_ptr(c_i), _ptr(z_i), _ptr(bias_i), B, n_new, halo, D_I, m, overlap, pos0,
+                                       f, _ptr(ko), _ptr(codes), _ptr(scales), _stream())
+    _check(st, "csa_compress_index_keys")
+    return codes, scales, ko
+
+
+def csa_decode_append_index(c_i_new, z_i_new, pos, bias_i, *, m, overlap, tok_c, tok_z, key_format, k_codes,
+                            k_scales=None, keys_out=None):
+    """The indexer stream's decode-time maintenance, in place: ring ``tok_c``/``tok_z``
+    [B, (1+overlap)*m, D_I] and key cache ``k_codes``/``k_scales`` ([B, N_cap] rows)."""
+    _dev(c_i_new, "c_i_new", torch.bfloat16, 2)
+    _dev(z_i_new, "z_i_new", torch.bfloat16, 2)
+    B, D_I = c_i_new.shape
+    if tuple(z_i_new.shape) != (B, D_I):
+        raise ValueError("z_i_new must have the shape of c_i_new")
+    _i64(pos, "pos", B)
+    _dev(bias_i, "bias_i", torch.bfloat16, 2)
+    R = (1 + overlap) * m
+    for name, t in (("tok_c", tok_c), ("tok_z", tok_z)):
+        _dev(t, name, torch.bfloat16, 3)
+        if tuple(t.shape) != (B, R, D_I):
+            raise ValueError(f"{name} must be [{B}, {R}, {D_I}]")
+    f = KEY_FORMATS[key_format]
+    N_cap = k_codes.shape[1]
+    _check_key_cache(k_codes, k_scales, (B, N_cap), D_I, f)
+    if keys_out is not None:
+        _dev(keys_out, "keys_out", torch.bfloat16, 3)
+        if tuple(keys_out.shape) != (B, N_cap, D_I):
+            raise ValueError(f"keys_out must be [{B}, {N_cap}, {D_I}]")
+    st = lib().csa_decode_append_index(_ptr(c_i_new), _ptr(z_i_new), _ptr(pos), _ptr(bias_i), B, D_I, m, overlap,
+                                       _ptr(tok_c), _ptr(tok_z), N_cap, f, _ptr(keys_out), _ptr(k_codes),
+                                       _ptr(k_scales), _stream())
+    _check(st, "csa_decode_append_index")
 
 
 def csa_decode_append(c_new, z_new, pos, bias, *, m, overlap, rope_dim, tok_c, tok_z, win_ring, entries,

@@ -124,6 +124,42 @@ csa_status csa_decode_append(const uint16_t *c_new, const uint16_t *z_new, const
                              void *k_scales, int64_t *n_entries, void *stream);
 
 /*
+ * csa_compress_index_keys -- lightning-indexer keys produced by compression, quantised on write.
+ * [EXPLAINER] CSA walk-through: the indexer scores compressed blocks, each made from its group of
+ * tokens by a learned softmax weighting; [RABBIT] indexer paragraph: the indexer works on smaller
+ * representations in lower precision.
+ *
+ * A per-token indexer stream c_i with logits z_i and bias bias_i is pooled exactly as
+ * csa_compress pools (same groups, overlap, bias slots, entry 0 alone), with no RMSNorm and no
+ * rotation.  Each pooled key is rounded to bf16 (written to keys_out when given) and quantised by
+ * csa_quantize_keys's rule for key_format (CSA_KEY_F32: stored as fp32).
+ *   c_i, z_i   bf16 [B, halo + n_new, D_I]; bias_i bf16 [(1+overlap)*m, D_I]; halo, pos0, n_new as
+ *              csa_compress.
+ *   keys_out   bf16 [B, n_new/m, D_I] or NULL.
+ *   k_codes, k_scales  the keys of entries pos0/m .. in key_format: rows [B, n_new/m] of the
+ *              layouts of csa_quantize_keys (fp32: codes fp32 [B, n_new/m, D_I], scales unused).
+ * Limits: D_I in {128, 256, 512, 1024}; 1 <= m <= 1024.
+ */
+csa_status csa_compress_index_keys(const uint16_t *c_i, const uint16_t *z_i, const uint16_t *bias_i, int B,
+                                   int64_t n_new, int halo, int D_I, int m, int overlap, int64_t pos0,
+                                   int key_format, uint16_t *keys_out, void *k_codes, void *k_scales,
+                                   void *stream);
+
+/*
+ * csa_decode_append_index -- the indexer stream's part of decode-time cache maintenance.
+ * As csa_decode_append for the per-token indexer stream: the new token's c_i, z_i rows go to
+ * the stream's ring tok_c / tok_z [B, (1+overlap)*m, D_I] at row t mod ring size; when t + 1
+ * completes entry i = (t+1)/m - 1 its key is pooled from the ring as csa_compress_index_keys
+ * pools it, rounded to bf16 (keys_out [B, N_cap, D_I] row (b, i) when given) and quantised into
+ * k_codes / k_scales row (b, i) ([B, N_cap] rows).  n_entries is left to csa_decode_append.
+ * Limits as csa_compress_index_keys; pos < 0 leaves a sequence untouched.
+ */
+csa_status csa_decode_append_index(const uint16_t *c_i_new, const uint16_t *z_i_new, const int64_t *pos,
+                                   const uint16_t *bias_i, int B, int D_I, int m, int overlap, uint16_t *tok_c,
+                                   uint16_t *tok_z, int64_t N_cap, int key_format, uint16_t *keys_out,
+                                   void *k_codes, void *k_scales, void *stream);
+
+/*
  * csa_quantize_keys -- quantise lightning-indexer keys to their storage format (quantise on write).
  * [DEVTO] "Two Compression Strategies": the indexer runs in FP4; [RABBIT] indexer paragraph:
  * smaller representations and lower-precision numbers.

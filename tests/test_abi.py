@@ -164,6 +164,27 @@ def test_append_zero_batch_and_keyless_calls_validate_on_the_host():
     assert _append(B=0, k_new=None, key_format=9, D_I=0, k_codes=None, k_scales=None) == 0
 
 
+def test_index_key_compression_rejects_bad_arguments():
+    L = ops.lib()
+    v = ctypes.c_void_p(16)
+    ok = dict(c=v, z=v, b=v, B=2, n_new=64, halo=0, D_I=128, m=4, overlap=1, pos0=0, fmt=2, ko=None, kc=v, ks=v,
+              st=None)
+
+    def call(**kw):
+        a = dict(ok); a.update(kw)
+        return L.csa_compress_index_keys(*a.values())
+    assert call(D_I=64) == 2                      # not a supported key width
+    assert call(fmt=5) == 1
+    assert call(m=0) == 1
+    assert call(n_new=63) == 1
+    assert call(pos0=8) == 1                      # overlap needs the previous group as halo
+    assert call(ks=None) == 1
+    assert call(fmt=0, ks=None, B=0) == 0
+    assert L.csa_decode_append_index(v, v, v, v, 2, 96, 4, 1, v, v, 100, 1, None, v, v, None) == 2
+    assert L.csa_decode_append_index(v, v, None, v, 2, 128, 4, 1, v, v, 100, 1, None, v, v, None) == 1
+    assert L.csa_decode_append_index(v, v, v, v, 0, 128, 4, 1, v, v, 100, 1, None, v, v, None) == 0
+
+
 def test_quantize_rejects_bad_arguments():
     L = ops.lib()
     v = ctypes.c_void_p(16)
