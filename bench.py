@@ -468,7 +468,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--legs", default="main,d128,c32k,hca,append,prefill,compress")
+    ap.add_argument("--legs", default="main,d128,c32k,hca,flash,append,prefill,compress")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy", "summarize-trace", "summarize-traffic"])
     ap.add_argument("--db", nargs="*", default=[], help="rocprofv3 databases for the summarize modes: one "
                     "kernel-trace db; or FETCH, WRITE, copy-FETCH, copy-WRITE dbs")
@@ -491,7 +491,7 @@ def main():
         return
     legs = args.legs.split(",")
     table = {"main": gen.CSA_DECODE_1M, "d128": gen.CSA_DECODE_128K, "c32k": gen.CSA_DECODE_32K,
-             "hca": gen.HCA_DECODE_1M, "append": gen.CSA_DECODE_1M}
+             "hca": gen.HCA_DECODE_1M, "append": gen.CSA_DECODE_1M, "flash": gen.CSA_DECODE_1M_FLASH}
     results = {}
     for name in legs:
         if name == "prefill":

@@ -338,7 +338,7 @@ static csa_status run_attend(csa::AttendArgs &a, void *stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = csa::launch_attend(a, st);
   if (e != hipSuccess) return launched(e, "attend launch");
-  if (a.plan.n_splits > 1) {
+  if (a.plan.n_splits > 1 && !a.plan.fused) {
       e = csa::launch_combine(a, st);
   }
   return launched(e, "combine launch");

@@ -90,17 +90,39 @@ struct AttendTile {
   int split, hb;
   bool valid;
 };
-__device__ __forceinline__ AttendTile attend_tile(const AttendArgs &a, int64_t n_queries) {
+__device__ __forceinline__ AttendTile attend_tile(const AttendArgs &a, int64_t n_queries, int grid_splits) {
   const int64_t L = blockIdx.x;
   const int64_t x = L & 7, rest = L >> 3;
   const int hb = int(rest % a.plan.n_hb);
   const int64_t pair = (rest / a.plan.n_hb) * 8 + x;
   AttendTile t;
-  t.valid = pair < n_queries * a.plan.n_splits;
-  t.qi = pair / a.plan.n_splits;
-  t.split = int(pair % a.plan.n_splits);
+  t.valid = pair < n_queries * grid_splits;
+  t.qi = pair / grid_splits;
+  t.split = int(pair % grid_splits);
   t.hb = hb;
   return t;
+}
+
+// The merge of slice partials, shared by the combine kernel and the fused path so that both give
+// the same bits: a slice's partial is x = O / l with log2-sum-exp m + log2 l; slices are merged in
+// order with a running maximum M and sum L (explicit roundings: no contraction choices).
+__device__ __forceinline__ float slice_scale(float l) { return l > 0.f ? 1.0f / l : 0.f; }
+__device__ __forceinline__ float slice_value(float o, float inv) { return __fmul_rn(o, inv); }
+__device__ __forceinline__ float slice_lse2(float m, float l) { return l > 0.f ? m + log2f(l) : -INFINITY; }
+struct MergeWeights {
+  float c, w;   // factor of the running sums, weight of the slice
+};
+__device__ __forceinline__ MergeWeights merge_slice(float &M, float &L, float ls) {
+  const float Mn = fmaxf(M, ls);
+  MergeWeights k;
+  k.c = M == -INFINITY ? 0.f : exp2f(M - Mn);
+  k.w = exp2f(ls - Mn);
+  L = __fmaf_rn(L, k.c, k.w);
+  M = Mn;
+  return k;
+}
+__device__ __forceinline__ float merge_value(float acc, const MergeWeights &k, float x) {
+  return __fmaf_rn(k.w, x, __fmul_rn(acc, k.c));
 }
 
 // Sum / maximum over lanes l, l^16, l^32 and l^48 (the four row groups of one head), in every lane,
@@ -130,7 +152,10 @@ constexpr int kRing = 4;                   // chunks in flight per wave; chunks 
 
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-template <int D>
+// FUSED: one workgroup per (query, head block) takes every slice in order and merges them in
+// registers exactly as the combine kernel does (for calls with many queries: no workspace, same
+// bits as the split-K path).
+template <int D, bool FUSED>
 __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(AttendArgs a, int64_t n_queries) {
   constexpr int C = slice_of<D>(), NW = waves_of<D>(), NT = 64 * NW;
   constexpr int NS = C / 32;          // 32-channel steps of the wave's slice (QK^T)
@@ -153,17 +178,15 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
-  const AttendTile tl = attend_tile(a, n_queries);
+  const AttendTile tl = attend_tile(a, n_queries, FUSED ? 1 : a.plan.n_splits);
   if (!tl.valid) return;
-  const int split = tl.split, hb = tl.hb;
+  const int hb = tl.hb;
   const int64_t qi = tl.qi;
   const int b = int(qi / a.Sq), s_idx = int(qi % a.Sq);
   const int64_t t = a.q_pos0[b] + s_idx;
   const int64_t n_vis = a.topk_idx ? 0 : min(a.n_entries[b], (t + 1) / a.m);
-  const int64_t r0 = int64_t(split) * a.plan.rows_per_split;
-  const int64_t r1 = min(int64_t(a.plan.n_rows), r0 + a.plan.rows_per_split);
-  const int nr = int(r1 - r0);
-  const int n_chunks = (nr + 15) >> 4;
+  const int split_first = FUSED ? 0 : tl.split;
+  const int split_end = FUSED ? a.plan.n_splits : tl.split + 1;
 
   // ---- prologue.  The raw q chunk (and norm weights) of this thread are loaded first: loads
   // complete in issue order, so anything issued later (the row prefetch) does not delay them.
@@ -179,16 +202,21 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
 #pragma unroll
     for (int k = 0; k < 4; ++k) { qraw[k] = src[k]; wraw[k] = wsrc[k]; }
   }
-  // row codes and rotary angles; the first chunks' loads go out before q^ is built
-  for (int i = tid; i < nr; i += NT) s_row[i] = row_code(a, qi, b, t, n_vis, r0 + i);
   const int npairs = a.rope_dim / 2;
   const double rate = rope_rate(a.rope_dim, a.log2_base);
   for (int u = tid; u < npairs; u += NT) rope_cos_sin(t, u, rate, &s_cs[u], &s_sn[u]);
   const uint16_t *ent_b = a.entries + int64_t(b) * a.N_cap * D + C * wave;
   const uint16_t *win_b = a.win_rows + int64_t(b) * a.W_cap * D + C * wave;
-  lds_barrier();
+  // the fused path's running merge of the slices (per head r; lane's channels as in O^T below)
+  float fM = -INFINITY, fL = 0.f;
+  v4f facc[FUSED ? NB : 1];
+#pragma unroll
+  for (int k = 0; k < (FUSED ? NB : 1); ++k) facc[k] = v4f{0.f, 0.f, 0.f, 0.f};
+  Frag8 qf[NS];
 
-  // ring of row-slice fragments: lane (r, g) holds row r of the chunk, channels C w + 32 s + 8 g .. +7
+  // slice state: its row count and chunks, the ring of row-slice fragments (lane (r, g) holds row
+  // r of the chunk, channels C w + 32 s + 8 g .. +7) and the row codes in the ring
+  int nr = 0, n_chunks = 0;
   Frag8 ring[RING][NS];
   int codes[RING];
   // Loads are unconditional (an empty slot reads entry row 0, which exists and is finite; its
@@ -203,8 +231,18 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
 #pragma unroll
     for (int s = 0; s < NS; ++s) ring[slot][s].u = *reinterpret_cast<const uint4 *>(rp + 32 * s + 8 * g);
   };
+  // a slice begins with its row codes in LDS and its first chunks' loads in flight
+  auto begin_slice = [&](int split) __attribute__((always_inline)) {
+    const int64_t r0 = int64_t(split) * a.plan.rows_per_split;
+    const int64_t r1 = min(int64_t(a.plan.n_rows), r0 + a.plan.rows_per_split);
+    nr = int(r1 - r0);
+    n_chunks = (nr + 15) >> 4;
+    for (int i = tid; i < nr; i += NT) s_row[i] = row_code(a, qi, b, t, n_vis, r0 + i);
+    lds_barrier();
 #pragma unroll
-  for (int j = 0; j < RING; ++j) issue(j, j);
+    for (int j = 0; j < RING; ++j) issue(j, j);
+  };
+  begin_slice(split_first);                      // its loads go out before q^ is built
 
   // q^ = RoPE(RMSNorm(q)) * scale * log2(e) for the 16 heads, into LDS, 8 channels at a time
   // (few registers: the row loads above are in flight meanwhile)
@@ -254,10 +292,16 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
   lds_barrier();
   // this wave's q^ slice as B operands (lane (r, g): head r, channels C w + 32 s + 8 g .. +7).  The
   // staging area reuses these bytes: every wave's reads complete before any wave stages rows.
-  Frag8 qf[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) qf[s].u = *reinterpret_cast<const uint4 *>(s_q + r * QS + C * wave + 32 * s + 8 * g);
   lds_barrier();
+
+  for (int split = split_first; split < split_end; ++split) {
+  if (split != split_first) {
+    lds_barrier();                               // the previous slice's readers of the row codes are done
+    begin_slice(split);
+  }
+
 
   // O^T block nb (O^T = V^T P^T): lane (r, g) element v = head r, channel C w + 16 nb + 4 g + v
   v4f o[NB];
@@ -361,27 +405,51 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
     }
   }
 
-  // ---- epilogue: this wave's channels of O / l, and the slice's log2-sum-exp ------------------
+  // ---- end of the slice: this wave's channels of O / l and the slice's log2-sum-exp ----------
   const int gh = hb * 16 + r;
-  if (gh < a.H) {
-    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-    const int c0 = C * wave + 4 * g;
+  const float inv = slice_scale(l_run);
+  const float ls = slice_lse2(m_run, l_run);
+  const int c0 = C * wave + 4 * g;
+  if constexpr (FUSED) {
+    if (ls != -INFINITY) {                        // as the combine kernel: empty slices are skipped
+      const MergeWeights k = merge_slice(fM, fL, ls);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) facc[nb][v] = merge_value(facc[nb][v], k, slice_value(o[nb][v], inv));
+    }
+  } else if (gh < a.H) {
     if (a.plan.n_splits == 1) {
       uint16_t *dst = a.out + (qi * a.H + gh) * D + c0;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        *reinterpret_cast<v4s *>(dst + 16 * nb) = pack4(o[nb][0] * inv, o[nb][1] * inv, o[nb][2] * inv, o[nb][3] * inv);
-      if (a.lse && wave == 0 && g == 0)
-        a.lse[qi * a.H + gh] = l_run > 0.f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+        *reinterpret_cast<v4s *>(dst + 16 * nb) = pack4(slice_value(o[nb][0], inv), slice_value(o[nb][1], inv),
+                                                       slice_value(o[nb][2], inv), slice_value(o[nb][3], inv));
+      if (a.lse && wave == 0 && g == 0) a.lse[qi * a.H + gh] = ls * 0.6931471805599453f;
     } else {
       float *po = static_cast<float *>(a.workspace);
       float *plse = po + n_queries * a.H * a.plan.n_splits * D;
       float *dst = po + ((qi * a.H + gh) * a.plan.n_splits + split) * int64_t(D) + c0;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        *reinterpret_cast<float4 *>(dst + 16 * nb) = make_float4(o[nb][0] * inv, o[nb][1] * inv, o[nb][2] * inv, o[nb][3] * inv);
-      if (wave == 0 && g == 0)
-        plse[(qi * a.H + gh) * a.plan.n_splits + split] = l_run > 0.f ? m_run + log2f(l_run) : -INFINITY;
+        *reinterpret_cast<float4 *>(dst + 16 * nb) = make_float4(slice_value(o[nb][0], inv), slice_value(o[nb][1], inv),
+                                                                 slice_value(o[nb][2], inv), slice_value(o[nb][3], inv));
+      if (wave == 0 && g == 0) plse[(qi * a.H + gh) * a.plan.n_splits + split] = ls;
+    }
+  }
+  }  // slices
+
+  if constexpr (FUSED) {
+    const int gh = hb * 16 + r;
+    if (gh < a.H) {
+      const float finv = fL > 0.f ? 1.0f / fL : 0.f;
+      uint16_t *dst = a.out + (qi * a.H + gh) * D + C * wave + 4 * g;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        *reinterpret_cast<v4s *>(dst + 16 * nb) = pack4(__fmul_rn(facc[nb][0], finv), __fmul_rn(facc[nb][1], finv),
+                                                       __fmul_rn(facc[nb][2], finv), __fmul_rn(facc[nb][3], finv));
+      if (a.lse && wave == 0 && g == 0)
+        a.lse[qi * a.H + gh] = fL > 0.f ? (fM + log2f(fL)) * 0.6931471805599453f : -INFINITY;
     }
   }
 }
@@ -411,17 +479,15 @@ __global__ void __launch_bounds__(D / 4) attend_combine_kernel(AttendArgs a, int
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       if (s0 + j >= ns || ls[j] == -INFINITY) continue;
-      const float Mn = fmaxf(M, ls[j]);
-      const float c = M == -INFINITY ? 0.f : exp2f(M - Mn), w = exp2f(ls[j] - Mn);
-      L = L * c + w;
-      acc.x = acc.x * c + w * x[j].x; acc.y = acc.y * c + w * x[j].y;
-      acc.z = acc.z * c + w * x[j].z; acc.w = acc.w * c + w * x[j].w;
-      M = Mn;
+      const MergeWeights k = merge_slice(M, L, ls[j]);
+      acc.x = merge_value(acc.x, k, x[j].x); acc.y = merge_value(acc.y, k, x[j].y);
+      acc.z = merge_value(acc.z, k, x[j].z); acc.w = merge_value(acc.w, k, x[j].w);
     }
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   uint16_t *dst = a.out + qh * D + ch;
-  *reinterpret_cast<v4s *>(dst) = pack4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  *reinterpret_cast<v4s *>(dst) = pack4(__fmul_rn(acc.x, inv), __fmul_rn(acc.y, inv), __fmul_rn(acc.z, inv),
+                                        __fmul_rn(acc.w, inv));
   if (a.lse && threadIdx.x == 0) a.lse[qh] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
 }
 
@@ -431,48 +497,54 @@ AttendPlan plan_attend(int64_t n_queries, int H, int64_t n_sel, int window, int 
   AttendPlan p;
   p.n_hb = (H + 15) / 16;
   p.n_rows = int(n_sel + window);
-  // A split is a multiple of 32 rows (a pair of 16-row chunks).  Aim at 128 rows per split, but
-  // no more splits than keep the grid within one round of resident workgroups (two per CU); every
-  // split costs a partial [16 x D] fp32 write and read.
-  const int64_t units = n_queries * p.n_hb;
-  const int64_t resident = 2 * 256;
-  int64_t splits = (p.n_rows + 127) / 128;
-  const int64_t by_grid = resident / units;
-  if (splits > by_grid) splits = by_grid;
+  // The slices depend on the row count alone -- never on how many queries share the call -- so a
+  // query's output has the same bits in any batch (batch invariance): up to 16 slices of about 144
+  // rows or more, each a multiple of 32 rows (a pair of 16-row chunks).  (k + W = 1,152 rows give 8
+  // slices: 512 workgroups, one round, for 16 queries of 64 heads.)
+  int64_t splits = (p.n_rows + 143) / 144;
+  if (splits > 16) splits = 16;
   if (splits < 1) splits = 1;
   int64_t rps = (p.n_rows + splits - 1) / splits;
   rps = (rps + 31) / 32 * 32;
   if (rps > kMaxRowsPerSplit) rps = kMaxRowsPerSplit;
   p.rows_per_split = int(rps);
   p.n_splits = int((p.n_rows + rps - 1) / rps);
+  // Split-K (a workgroup per slice, partials merged by the combine kernel) while the grid stays
+  // within a few rounds of resident workgroups (two per CU); beyond that one workgroup per
+  // (query, head block) takes the slices in order and merges them itself, with no workspace.
+  p.fused = (p.n_splits > 1 && n_queries * p.n_hb * p.n_splits > 4 * 512) ? 1 : 0;
   (void)D;
   return p;
 }
 
 size_t attend_workspace_bytes(int64_t n_queries, int H, int D, int64_t n_sel, int window) {
   AttendPlan p = plan_attend(n_queries, H, n_sel, window, D);
-  if (p.n_splits == 1) return 256;
+  if (p.n_splits == 1 || p.fused) return 256;
   return size_t(n_queries * H * p.n_splits * (int64_t(D) + 1) * 4 + 256);
 }
 
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream) {
   hipError_t e = hipSuccess;
   const int64_t nq = int64_t(a.B) * a.Sq;
-  const int64_t pairs = nq * a.plan.n_splits;
+  const int64_t pairs = nq * (a.plan.fused ? 1 : a.plan.n_splits);
   dim3 grid(unsigned(((pairs + 7) / 8) * 8 * a.plan.n_hb));
+#define CSA_ATTEND_LAUNCH(DD)                                                                          \
+  e = a.plan.fused ? launch("attend_split", attend_split_kernel<DD, true>, grid, dim3(64 * waves_of<DD>()), stream, a, nq) \
+                   : launch("attend_split", attend_split_kernel<DD, false>, grid, dim3(64 * waves_of<DD>()), stream, a, nq)
   switch (a.D) {
-    case 64: e = launch("attend_split", attend_split_kernel<64>, grid, dim3(64 * waves_of<64>()), stream, a, nq); break;
-    case 128: e = launch("attend_split", attend_split_kernel<128>, grid, dim3(64 * waves_of<128>()), stream, a, nq); break;
-    case 256: e = launch("attend_split", attend_split_kernel<256>, grid, dim3(64 * waves_of<256>()), stream, a, nq); break;
-    case 512: e = launch("attend_split", attend_split_kernel<512>, grid, dim3(64 * waves_of<512>()), stream, a, nq); break;
+    case 64: CSA_ATTEND_LAUNCH(64); break;
+    case 128: CSA_ATTEND_LAUNCH(128); break;
+    case 256: CSA_ATTEND_LAUNCH(256); break;
+    case 512: CSA_ATTEND_LAUNCH(512); break;
     default: return hipErrorInvalidValue;
   }
+#undef CSA_ATTEND_LAUNCH
   return e;
 }
 
 hipError_t launch_combine(const AttendArgs &a, hipStream_t stream) {
   hipError_t e = hipSuccess;
-  if (a.plan.n_splits == 1) return hipSuccess;
+  if (a.plan.n_splits == 1 || a.plan.fused) return hipSuccess;
   const int64_t nq = int64_t(a.B) * a.Sq;
   dim3 grid(unsigned(nq * a.H));
   switch (a.D) {

@@ -77,9 +77,10 @@ hipError_t launch_index_merge(const IndexArgs &a, hipStream_t stream);
 // ---- core attention ------------------------------------------------------------------------
 struct AttendPlan {
   int n_hb;         // head blocks of 16
-  int n_splits;     // row splits per (query, head block)
+  int n_splits;     // row splits per (query, head block); a function of n_rows only
   int rows_per_split;
   int n_rows;       // row-list length per query: n_sel + window
+  int fused;        // one workgroup per (query, head block) merges every split (many queries)
 };
 AttendPlan plan_attend(int64_t n_queries, int H, int64_t n_sel, int window, int D);
 size_t attend_workspace_bytes(int64_t n_queries, int H, int D, int64_t n_sel, int window);

@@ -139,12 +139,16 @@ HCA_DECODE_1M = Workload("hca_decode_1m_b8", 3, "hca_decode", B=8, T=1048576, d=
 CSA_DECODE_1M = Workload("csa_decode_1m_b4_mxfp4", 4, "csa_decode", B=4, T=1048576, d=512, H=64,
                          rope_dim=64, m=4, overlap=1, H_I=64, D_I=128, key_format="mxfp4",
                          topk=1024, n_planted=16)
+# The Flash configuration's attention top-k (512) at the maximum context, else as above.
+CSA_DECODE_1M_FLASH = Workload("csa_decode_1m_b4_mxfp4_k512", 4, "csa_decode", B=4, T=1048576, d=512, H=64,
+                               rope_dim=64, m=4, overlap=1, H_I=64, D_I=128, key_format="mxfp4",
+                               topk=512, n_planted=16)
 # Derived decode point at 128K context with the 32K decode shapes (the metric names 128K decode).
 CSA_DECODE_128K = Workload("csa_decode_128k_b16_fp8", 5, "csa_decode", B=16, T=131072, d=512, H=64,
                            rope_dim=64, m=4, overlap=1, H_I=64, D_I=128, key_format="fp8", topk=1024)
 
 WORKLOADS = {w.name: w for w in (TINY, CSA_DECODE_32K, CSA_PREFILL_128K, HCA_DECODE_1M,
-                                 CSA_DECODE_1M, CSA_DECODE_128K)}
+                                 CSA_DECODE_1M, CSA_DECODE_128K, CSA_DECODE_1M_FLASH)}
 
 
 def decode_inputs(w: Workload, b_lo: int = 0, b_hi: int | None = None, n_rows: int | None = None,

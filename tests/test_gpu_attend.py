@@ -93,6 +93,13 @@ def test_csa_decode_1m_full():
     check_csa(x["q"], x["entries"], sel, x["win_rows"], x["win_pos0"], x["t"], w.window, w.rope_dim, w.name)
 
 
+def test_csa_decode_1m_flash_topk512_full():
+    w = gen.CSA_DECODE_1M_FLASH
+    x = gen.decode_inputs(w, parts=("attend",))
+    sel = _selection(np.random.default_rng(75), w.B, 1, w.N, w.topk)
+    check_csa(x["q"], x["entries"], sel, x["win_rows"], x["win_pos0"], x["t"], w.window, w.rope_dim, w.name)
+
+
 def test_hca_decode_1m_full():
     w = gen.HCA_DECODE_1M
     x = gen.decode_inputs(w, parts=("attend",))

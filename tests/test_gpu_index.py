@@ -133,6 +133,11 @@ def test_csa_decode_1m_mxfp4_planted_full():
     _decode_case(gen.CSA_DECODE_1M)
 
 
+def test_csa_decode_1m_flash_topk512_full():
+    # the Flash configuration: attention top-k 512 at the maximum context
+    _decode_case(gen.CSA_DECODE_1M_FLASH)
+
+
 def test_prefill_chunk_full_size_sampled():
     # 4,096 query tokens at positions 131,072.. over 33,792 entries (the 32,768 existing ones plus
     # the chunk's 1,024), fp8 keys; every query runs, 12 seeded ones (first and last included) are
