@@ -231,10 +231,14 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
 #pragma unroll
     for (int s = 0; s < NS; ++s) ring[slot][s].u = *reinterpret_cast<const uint4 *>(rp + 32 * s + 8 * g);
   };
-  // a slice begins with its row codes in LDS and its first chunks' loads in flight
-  auto begin_slice = [&](int split) __attribute__((always_inline)) {
-    const int64_t r0 = int64_t(split) * a.plan.rows_per_split;
-    const int64_t r1 = min(int64_t(a.plan.n_rows), r0 + a.plan.rows_per_split);
+  // A segment of the row list -- one slice, or in the fused path every slice when the whole list
+  // fits the row-code buffer (one continuous stream of chunks, no restart between slices) --
+  // begins with its row codes in LDS and its first chunks' loads in flight.
+  const bool stream = FUSED && a.plan.n_rows <= kMaxRowsPerSplit;
+  const int n_seg = stream ? 1 : split_end - split_first;
+  auto begin_segment = [&](int seg) __attribute__((always_inline)) {
+    const int64_t r0 = stream ? 0 : int64_t(split_first + seg) * a.plan.rows_per_split;
+    const int64_t r1 = stream ? a.plan.n_rows : min(int64_t(a.plan.n_rows), r0 + a.plan.rows_per_split);
     nr = int(r1 - r0);
     n_chunks = (nr + 15) >> 4;
     for (int i = tid; i < nr; i += NT) s_row[i] = row_code(a, qi, b, t, n_vis, r0 + i);
@@ -242,7 +246,7 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
 #pragma unroll
     for (int j = 0; j < RING; ++j) issue(j, j);
   };
-  begin_slice(split_first);                      // its loads go out before q^ is built
+  begin_segment(0);                              // its loads go out before q^ is built
 
   // q^ = RoPE(RMSNorm(q)) * scale * log2(e) for the 16 heads, into LDS, 8 channels at a time
   // (few registers: the row loads above are in flight meanwhile)
@@ -296,19 +300,18 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
   for (int s = 0; s < NS; ++s) qf[s].u = *reinterpret_cast<const uint4 *>(s_q + r * QS + C * wave + 32 * s + 8 * g);
   lds_barrier();
 
-  for (int split = split_first; split < split_end; ++split) {
-  if (split != split_first) {
-    lds_barrier();                               // the previous slice's readers of the row codes are done
-    begin_slice(split);
-  }
-
-
   // O^T block nb (O^T = V^T P^T): lane (r, g) element v = head r, channel C w + 16 nb + 4 g + v
   v4f o[NB];
+  float m_run, l_run;                             // of head r; the same in every wave
+  auto reset_slice = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int k = 0; k < NB; ++k) o[k] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;           // of head r; the same in every wave
+    for (int k = 0; k < NB; ++k) o[k] = v4f{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
+  };
+  reset_slice();
   unsigned char *stage = s_buf + wave * 32 * RS;
+  int split = split_first;                        // the slice being accumulated
 
   // Two chunks (32 rows) per step, straight-line code.  Row order within the step: k = 8g + v is
   // row 4g + v of the first chunk for v < 4 and row 4g + v - 4 of the second for v >= 4, so the
@@ -393,19 +396,8 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[nb].b, pf.b, o[nb], 0, 0, 0);
   };
-  // The barrier inside a pair is reached by every wave (n_chunks is the same for all of them); the
-  // S partial buffers alternate between consecutive pairs, so one barrier per pair suffices.  An
-  // empty second chunk (odd chunk count) reads the dummy row and is masked out.
-  for (int j0 = 0; j0 < n_chunks; j0 += RING) {
-#pragma unroll
-    for (int h = 0; h < RING / 2; ++h) {
-      if (j0 + 2 * h < n_chunks) pair(2 * h, h & 1);
-      issue(j0 + 2 * h + RING, 2 * h);           // refill the pair's slots
-      issue(j0 + 2 * h + 1 + RING, 2 * h + 1);
-    }
-  }
-
-  // ---- end of the slice: this wave's channels of O / l and the slice's log2-sum-exp ----------
+  // ---- end of a slice: this wave's channels of O / l and the slice's log2-sum-exp ------------
+  auto end_slice = [&]() __attribute__((always_inline)) {
   const int gh = hb * 16 + r;
   const float inv = slice_scale(l_run);
   const float ls = slice_lse2(m_run, l_run);
@@ -437,7 +429,41 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
       if (wave == 0 && g == 0) plse[(qi * a.H + gh) * a.plan.n_splits + split] = ls;
     }
   }
-  }  // slices
+  };
+
+  // The barrier inside a pair is reached by every wave (n_chunks is the same for all of them); the
+  // S partial buffers alternate between consecutive pairs, so one barrier per pair suffices.  An
+  // empty second chunk (odd chunk count) reads the dummy row and is masked out.  Slices are whole
+  // pairs (rows_per_split is a multiple of 32), so in a stream a slice ends between two pairs and
+  // its pairs are exactly the ones the split-K path takes for it.
+  const int cps = a.plan.rows_per_split >> 4;     // chunks per slice (even)
+  for (int seg = 0; seg < n_seg; ++seg) {
+    if (seg != 0) {
+      lds_barrier();                              // the previous segment's readers of the row codes are done
+      begin_segment(seg);
+    }
+    for (int j0 = 0; j0 < n_chunks; j0 += RING) {
+#pragma unroll
+      for (int h = 0; h < RING / 2; ++h) {
+        const int j = j0 + 2 * h;
+        if (j < n_chunks) {
+          pair(2 * h, h & 1);
+          if constexpr (FUSED) {
+            if ((j + 2) % cps == 0 && j + 2 < n_chunks) {   // a slice ends inside the stream
+              end_slice();
+              ++split;
+              reset_slice();
+            }
+          }
+        }
+        issue(j + RING, 2 * h);                  // refill the pair's slots
+        issue(j + 1 + RING, 2 * h + 1);
+      }
+    }
+    end_slice();
+    ++split;
+    reset_slice();
+  }
 
   if constexpr (FUSED) {
     const int gh = hb * 16 + r;
