@@ -31,6 +31,7 @@ from compressed_sparse_attention_03_amd import inputs as gen  # noqa: E402
 from compressed_sparse_attention_03_amd import ops  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0     # dense bf16 MFMA (MI355X, no sparsity)
 METRIC = "CSA decode query-tokens/sec at 128K and 1M ctx; % of peak HBM GB/s"
 KEY_BYTES = {"fp8": 128 + 4, "mxfp4": 64 + 4}
 MALL_BYTES = 256e6
@@ -411,6 +412,49 @@ def compress_leg(steps: int):
             "data": "seeded torch generator on the GPU"}
 
 
+def oproj_leg(steps: int):
+    """The grouped output projection after core attention: 64 heads x 512 in 8 groups, each group
+    projected to 512 of a 4,096-wide hidden state (synthetic shapes and weights: the pages give
+    no sizes).  A decode step of four tokens streams the 32 MiB of weights (HBM roofline); a
+    4,096-token prefill chunk is a 137 GFLOP bf16 contraction (MFMA roofline)."""
+    H, D, G, N_g = 64, 512, 8, 512
+    K_g = H * D // G
+    gpu = torch.Generator(device="cuda")
+    gpu.manual_seed(77)
+    ncopy = max(2, math.ceil(4 * MALL_BYTES / (G * N_g * K_g * 2)))     # weights beyond the cache
+    ws = [(torch.randn((G, N_g, K_g), generator=gpu, device="cuda") / math.sqrt(K_g)).to(torch.bfloat16)
+          for _ in range(ncopy)]
+    res = {"workload": "grouped_output_projection_h64x512_g8_to_4096", "data": "seeded torch generator on the GPU",
+           "kernel_us": {}}
+    for M, tag in ((4, "decode_m4"), (4096, "prefill_m4096")):
+        o = torch.randn((M, H, D), generator=gpu, device="cuda").to(torch.bfloat16)
+        y = torch.empty((M, G * N_g), dtype=torch.bfloat16, device="cuda")
+        for i in range(ncopy):
+            ops.csa_output_projection(o, ws[i], out=y)
+        torch.cuda.synchronize()
+        n = steps if M == 4 else max(3, steps // 20)
+        ops.timing_enable(True)
+        for i in range(n):
+            ops.csa_output_projection(o, ws[i % ncopy], out=y)
+        torch.cuda.synchronize()
+        ms, cnt = ops.timing_read("oproj")
+        ops.timing_enable(False)
+        us = 1000.0 * ms / max(cnt, 1)
+        res["kernel_us"][tag] = us
+        if M == 4:
+            nbytes = G * N_g * K_g * 2 + o.numel() * 2 + y.numel() * 2
+            res[tag] = {"bound": "hbm", "achieved": nbytes / (us * 1e-6) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": nbytes}
+        else:
+            flops = 2.0 * M * K_g * N_g * G
+            res[tag] = {"bound": "mfma", "dtype": "bf16", "flops": flops, "achieved_tflops": flops / (us * 1e-6) / 1e12,
+                        "peak_tflops": PEAK_BF16_TFLOPS, "frac": flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}
+        del o, y
+    del ws
+    torch.cuda.empty_cache()
+    return res
+
+
 # ---- rocprofv3 summaries (text for profiles/) -----------------------------------------------------
 def _short_kernel(name: str) -> str:
     name = name.replace("void ", "").replace("csa::(anonymous namespace)::", "")
@@ -468,7 +512,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--legs", default="main,d128,c32k,hca,flash,append,prefill,compress")
+    ap.add_argument("--legs", default="main,d128,c32k,hca,flash,append,prefill,compress,oproj")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy", "summarize-trace", "summarize-traffic"])
     ap.add_argument("--db", nargs="*", default=[], help="rocprofv3 databases for the summarize modes: one "
                     "kernel-trace db; or FETCH, WRITE, copy-FETCH, copy-WRITE dbs")
@@ -503,6 +547,10 @@ def main():
             continue
         if name == "compress":
             results[name] = compress_leg(max(3, min(args.steps // 200, 10)))
+            log(json.dumps(results[name]))
+            continue
+        if name == "oproj":
+            results[name] = oproj_leg(max(20, min(args.steps, 200)))
             log(json.dumps(results[name]))
             continue
         w = table[name]

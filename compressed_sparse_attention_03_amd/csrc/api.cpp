@@ -249,6 +249,21 @@ csa_status csa_decode_append_index(const uint16_t *c_i_new, const uint16_t *z_i_
   return launched(e, "decode_append_index launch");
 }
 
+csa_status csa_output_projection(const uint16_t *o, const uint16_t *w, int M, int H, int D, int G, int N_g,
+                                 uint16_t *y, void *stream) {
+  REQUIRE(M >= 0 && M <= (1 << 24), "M must be in [0, 2^24]");
+  REQUIRE(H >= 1 && D >= 1 && G >= 1 && H % G == 0, "H must be a positive multiple of G");
+  const int64_t K_g = int64_t(H) * D / G;
+  if (K_g % 256 != 0 || K_g > (1 << 20) || N_g % 128 != 0 || N_g < 128 || int64_t(G) * N_g > (1 << 20))
+    return fail(CSA_ERR_UNSUPPORTED, "need (H*D/G) %% 256 == 0 and N_g %% 128 == 0 (got K_g %lld, N_g %d)",
+                (long long)K_g, N_g);
+  if (M == 0) return CSA_OK;
+  REQUIRE_PTR(o); REQUIRE_PTR(w); REQUIRE_PTR(y);
+  csa::ProjArgs a{o, w, y, M, G, N_g, int(K_g), int64_t(H) * D, int64_t(G) * N_g};
+  hipError_t e = csa::launch_oproj(a, static_cast<hipStream_t>(stream));
+  return launched(e, "output projection launch");
+}
+
 csa_status csa_quantize_keys(const uint16_t *x, int64_t rows, int dim, int format, void *codes,
                              void *scales, void *stream) {
   REQUIRE(format == CSA_KEY_FP8_E4M3 || format == CSA_KEY_MXFP4, "format must be CSA_KEY_FP8_E4M3 or CSA_KEY_MXFP4");

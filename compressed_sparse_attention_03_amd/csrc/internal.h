@@ -74,6 +74,15 @@ struct IndexArgs {
 hipError_t launch_index_score(const IndexArgs &a, hipStream_t stream);
 hipError_t launch_index_merge(const IndexArgs &a, hipStream_t stream);
 
+// ---- grouped output projection --------------------------------------------------------------
+struct ProjArgs {
+  const uint16_t *o, *w;            // [M, ldo] head outputs; [G, N_g, K_g] weights
+  uint16_t *y;                      // [M, ldy]
+  int M, G, N_g, K_g;
+  int64_t ldo, ldy;
+};
+hipError_t launch_oproj(const ProjArgs &a, hipStream_t stream);
+
 // ---- core attention ------------------------------------------------------------------------
 struct AttendPlan {
   int n_hb;         // head blocks of 16

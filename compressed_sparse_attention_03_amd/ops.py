@@ -27,6 +27,7 @@ I32, I64, F32, SZ = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_
 _SIGS = {
     "csa_compress": (I32, [P, P, P, P, I32, I64, I32, I32, I32, I32, I32, I64, F32, F32, P, P, P]),
     "csa_quantize_keys": (I32, [P, I64, I32, I32, P, P, P]),
+    "csa_output_projection": (I32, [P, P, I32, I32, I32, I32, I32, P, P]),
     "csa_compress_index_keys": (I32, [P, P, P, I32, I64, I32, I32, I32, I32, I64, I32, P, P, P, P]),
     "csa_decode_append_index": (I32, [P, P, P, P, I32, I32, I32, I32, P, P, I64, I32, P, P, P, P]),
     "csa_decode_append": (I32, [P, P, P, P, P, P, I32, I32, I32, I32, I32, F32, F32, P, P, P, I64, P, I64,
@@ -363,6 +364,25 @@ def hca_attend(q, entries, n_entries, win_rows, win_pos0, q_pos0, *, m, rope_dim
                           scale, rope_base, eps, _ptr(o), _ptr(ls), _ptr(ws), ws.numel(), _stream())
     _check(st, "hca_attend")
     return o, ls
+
+
+def csa_output_projection(o, w, out=None):
+    """Grouped output projection: o bf16 [..., H, D] (heads last) and w bf16 [G, N_g, H*D/G] ->
+    y bf16 [..., G*N_g]."""
+    _dev(o, "o", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16, 3)
+    H, D = o.shape[-2], o.shape[-1]
+    M = o.numel() // (H * D)
+    G, N_g, K_g = w.shape
+    if G * K_g != H * D:
+        raise ValueError("w must be [G, N_g, H*D/G]")
+    y = out if out is not None else torch.empty(tuple(o.shape[:-2]) + (G * N_g,), dtype=torch.bfloat16, device=o.device)
+    _dev(y, "out", torch.bfloat16)
+    if y.numel() != M * G * N_g:
+        raise ValueError("out must hold [..., G*N_g]")
+    st = lib().csa_output_projection(_ptr(o), _ptr(w), M, H, D, G, N_g, _ptr(y), _stream())
+    _check(st, "csa_output_projection")
+    return y
 
 
 def timing_enable(on: bool):

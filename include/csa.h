@@ -259,6 +259,23 @@ csa_status hca_attend(const uint16_t *q, const uint16_t *q_norm_w, const uint16_
                       size_t workspace_bytes, void *stream);
 size_t hca_attend_workspace_bytes(int B, int Sq, int H, int D, int64_t N_cap, int window);
 
+/*
+ * csa_output_projection -- grouped output projection of the core-attention head outputs.
+ * [SUMMARY] 2.3, shared-KV and output-projection paragraph: CSA and HCA use a grouped output
+ * projection, which makes projecting the many head outputs back to the hidden state cheaper.
+ *
+ * The H heads fall into G equal groups in head order; group g's concatenated head outputs
+ * (K_g = H*D/G values) are projected by its own weight w[g] [N_g, K_g] (a linear layer's
+ * [out, in] layout) to N_g outputs; the groups' outputs are concatenated:
+ *     y[m, g*N_g + n] = sum_k o[m, g*K_g + k] * w[g, n, k]     (fp32 accumulation)
+ *   o  bf16 [M, H*D] (for example csa_attend's output [B, Sq, H, D] with M = B*Sq).
+ *   w  bf16 [G, N_g, K_g].
+ *   y  out bf16 [M, G*N_g].
+ * Limits: H % G == 0; K_g % 256 == 0; N_g % 128 == 0; G*N_g <= 2^20.
+ */
+csa_status csa_output_projection(const uint16_t *o, const uint16_t *w, int M, int H, int D, int G, int N_g,
+                                 uint16_t *y, void *stream);
+
 /* Text for a status code (static storage). */
 const char *csa_status_string(csa_status s);
 /* Thread-local detail of the last failed call on this thread ("" if none). */

@@ -185,6 +185,16 @@ def test_index_key_compression_rejects_bad_arguments():
     assert L.csa_decode_append_index(v, v, v, v, 0, 128, 4, 1, v, v, 100, 1, None, v, v, None) == 0
 
 
+def test_output_projection_rejects_bad_arguments():
+    L = ops.lib()
+    v = ctypes.c_void_p(16)
+    assert L.csa_output_projection(v, v, 4, 64, 512, 7, 512, v, None) == 1     # H % G != 0
+    assert L.csa_output_projection(v, v, 4, 64, 512, 8, 100, v, None) == 2     # N_g % 128 != 0
+    assert L.csa_output_projection(v, v, 4, 4, 40, 2, 128, v, None) == 2       # K_g = 80
+    assert L.csa_output_projection(None, v, 4, 64, 512, 8, 512, v, None) == 1
+    assert L.csa_output_projection(None, None, 0, 64, 512, 8, 512, None, None) == 0
+
+
 def test_quantize_rejects_bad_arguments():
     L = ops.lib()
     v = ctypes.c_void_p(16)

@@ -1,0 +1,48 @@
+"""Grouped output projection (csa_output_projection) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from compressed_sparse_attention_03_amd import inputs as gen
+from compressed_sparse_attention_03_amd import ops
+from oracle import projection as op
+from helpers import assert_close, dev_bf16, f64, host_f64, say
+
+pytestmark = pytest.mark.gpu
+CFG = 43
+
+
+def _case(M, H, D, G, N_g):
+    K_g = H * D // G
+    o = gen.normal_bf16(CFG, gen.T_Q, (M * H, D)).reshape(M, H, D)
+    # weights scaled so every output is O(1): the tolerance then reads as a relative one
+    w = gen.normal_bf16(CFG, gen.T_W, (G * N_g, K_g), std=1.0 / np.sqrt(K_g)).reshape(G, N_g, K_g)
+    return o, w
+
+
+@pytest.mark.parametrize("M,H,D,G,N_g", [
+    (4, 64, 512, 8, 512),        # a decode step of four sequences: weights streamed (small-M path)
+    (1, 16, 128, 2, 128),
+    (16, 64, 512, 8, 512),       # largest small-M call
+    (17, 64, 512, 8, 512),       # smallest tiled call, ragged tile
+    (300, 16, 256, 4, 256),
+    (32, 8, 128, 1, 256),        # one group: a dense projection
+])
+def test_projection(M, H, D, G, N_g):
+    say(f"case: output projection M={M} H={H} D={D} G={G} N_g={N_g}")
+    o, w = _case(M, H, D, G, N_g)
+    y = ops.csa_output_projection(dev_bf16(o), dev_bf16(w))
+    ref = op.grouped_output_projection(f64(o).reshape(M, H * D), f64(w))
+    assert_close(host_f64(y), ref, "y")
+    y2 = ops.csa_output_projection(dev_bf16(o), dev_bf16(w))
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "repeat differs"
+
+
+def test_projection_prefill_size_sampled():
+    M, H, D, G, N_g = 4096, 64, 512, 8, 512
+    say(f"case: output projection prefill M={M} (sampled rows)")
+    o, w = _case(M, H, D, G, N_g)
+    y = host_f64(ops.csa_output_projection(dev_bf16(o), dev_bf16(w)))
+    rows = np.array([0, 1, 127, 128, 1000, 2047, 3333, 4095])
+    ref = op.grouped_output_projection(f64(o[rows]).reshape(len(rows), H * D), f64(w))
+    assert_close(y[rows], ref, "y rows")
