@@ -23,6 +23,7 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));   // converted with v_cvt_pk_bf16_f32 (round to nearest even)
 union F8 {
   uint4 u;
   v8bf b;
@@ -160,12 +161,121 @@ __global__ void __launch_bounds__(256) oproj_tiled_kernel(ProjArgs a) {
       }
 }
 
+// Large M: a 256 x 256 output tile per workgroup (one per CU at 4,096 x 4,096), four waves of
+// 128 x 128 each.  A wave's 8 x 8 accumulator tiles (256 values a lane) stay in accumulation
+// registers until the end -- nothing but the MFMAs touches them -- so per 32-wide K step a wave
+// reads 16 fragments from LDS for 64 MFMAs (twice the reuse of the 128-tile kernel, which is
+// LDS-bound).  The products are taken as Y^T tiles (weight rows as the A operand, token rows as B),
+// so a lane ends with four consecutive output columns of one token: one 8-byte store each.
+// Global -> LDS: load l of thread tid is the 16-byte piece (tid % 8) of tile row 32 l + tid / 8, so
+// one instruction reads eight whole 128-byte row segments.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBig = 256;         // output tile rows and columns per workgroup
+constexpr int kBigStep = 64;      // K per LDS stage
+constexpr int kBigRow = kBigStep + 8;
+
+__global__ void __launch_bounds__(256, 1) oproj_big_kernel(ProjArgs a) {
+  __shared__ __align__(16) uint16_t s_a[2][kBig * kBigRow];   // token rows
+  __shared__ __align__(16) uint16_t s_b[2][kBig * kBigRow];   // weight rows
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, q = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;                     // the wave's 128 x 128 quarter
+  // Workgroup -> tile.  Workgroups go to the 8 XCDs round-robin by linear id; when the groups
+  // divide evenly, XCD x takes every tile of groups x, x + 8, ..., so a group's weights stay in one
+  // L2, and the column tiles that share a token tile get neighbouring ids (same XCD, launched
+  // together: the token tile is fetched once).
+  const int n_sub = a.N_g / kBig, m_tiles = (a.M + kBig - 1) / kBig;
+  const int L = blockIdx.x;
+  int g, sub, mt;
+  if (a.G % 8 == 0) {
+    const int x = L & 7, j = L >> 3;
+    g = x + 8 * (j / (n_sub * m_tiles));
+    const int rest = j % (n_sub * m_tiles);
+    mt = rest / n_sub;
+    sub = rest % n_sub;
+  } else {
+    g = L / (n_sub * m_tiles);
+    const int rest = L % (n_sub * m_tiles);
+    mt = rest / n_sub;
+    sub = rest % n_sub;
+  }
+  const int64_t m0 = int64_t(mt) * kBig;
+  const int n0 = g * a.N_g + sub * kBig;
+  const int K = a.K_g;
+  const int lrow = tid >> 3, lp = tid & 7;
+  const uint16_t *ga0 = a.o + int64_t(g) * K + 8 * lp;
+  const uint16_t *gb0 = a.w + (int64_t(g) * a.N_g + (n0 - g * a.N_g) + lrow) * K + 8 * lp;
+  u32x4 ra[8], rb[8];
+  auto load = [&](int k) __attribute__((always_inline)) {
+#pragma unroll
+    for (int l = 0; l < 8; ++l) {
+      const int64_t m = min(m0 + 32 * l + lrow, int64_t(a.M) - 1);  // rows past M repeat the last (not stored)
+      ra[l] = *reinterpret_cast<const u32x4 *>(ga0 + m * a.ldo + k);
+      rb[l] = *reinterpret_cast<const u32x4 *>(gb0 + int64_t(32 * l) * K + k);
+    }
+  };
+  auto store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int l = 0; l < 8; ++l) {
+      *reinterpret_cast<u32x4 *>(s_a[buf] + (32 * l + lrow) * kBigRow + 8 * lp) = ra[l];
+      *reinterpret_cast<u32x4 *>(s_b[buf] + (32 * l + lrow) * kBigRow + 8 * lp) = rb[l];
+    }
+  };
+  v4f acc[8][8];                                               // [weight tile y][token tile x]
+#pragma unroll
+  for (int y = 0; y < 8; ++y)
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc[y][x] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int steps = K / kBigStep;
+  load(0);
+  store(0);
+  lds_barrier();
+  for (int t = 0; t < steps; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < steps) load(kBigStep * (t + 1));               // in flight while this step computes
+#pragma unroll 1
+    for (int kk = 0; kk < kBigStep; kk += 32) {
+      F8 fa[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x)
+        fa[x].u = *reinterpret_cast<const uint4 *>(s_a[buf] + (wm * 128 + x * 16 + i) * kBigRow + kk + 8 * q);
+#pragma unroll
+      for (int y = 0; y < 8; ++y) {
+        F8 fb;
+        fb.u = *reinterpret_cast<const uint4 *>(s_b[buf] + (wn * 128 + y * 16 + i) * kBigRow + kk + 8 * q);
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+          acc[y][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb.b, fa[x].b, acc[y][x], 0, 0, 0);
+      }
+    }
+    if (t + 1 < steps) store(buf ^ 1);                          // the other buffer: last read a step ago
+    lds_barrier();
+  }
+  // tile (y, x), lane (i, q): token row 16 x + i, output columns 16 y + 4 q .. +3
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    const int64_t m = m0 + wm * 128 + x * 16 + i;
+    if (m < a.M) {
+      uint16_t *dst = a.y + m * a.ldy + n0 + wn * 128 + 4 * q;
+#pragma unroll
+      for (int y = 0; y < 8; ++y) {
+        *reinterpret_cast<v4bf *>(dst + 16 * y) =
+            v4bf{__bf16(acc[y][x][0]), __bf16(acc[y][x][1]), __bf16(acc[y][x][2]), __bf16(acc[y][x][3])};
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_oproj(const ProjArgs &a, hipStream_t stream) {
   const int n_total = a.G * a.N_g;
   if (a.M <= 16)
     return launch("oproj", oproj_small_kernel, dim3(unsigned(n_total / 16)), dim3(64 * kSmallWaves), stream, a);
+  if (a.M >= 512 && a.N_g % kBig == 0) {
+    const dim3 grid(unsigned(int64_t(n_total / kBig) * ((a.M + kBig - 1) / kBig)));
+    return launch("oproj", oproj_big_kernel, grid, dim3(256), stream, a);
+  }
   const dim3 grid(unsigned(n_total / kTile), unsigned((a.M + kTile - 1) / kTile));
   return launch("oproj", oproj_tiled_kernel, grid, dim3(256), stream, a);
 }

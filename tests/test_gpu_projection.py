@@ -27,6 +27,8 @@ def _case(M, H, D, G, N_g):
     (17, 64, 512, 8, 512),       # smallest tiled call, ragged tile
     (300, 16, 256, 4, 256),
     (32, 8, 128, 1, 256),        # one group: a dense projection
+    (700, 16, 256, 8, 256),      # 256-wide tiles, groups spread over the XCDs, ragged last row tile
+    (600, 16, 256, 4, 512),      # 256-wide tiles, groups not a multiple of 8 (plain tile order)
 ])
 def test_projection(M, H, D, G, N_g):
     say(f"case: output projection M={M} H={H} D={D} G={G} N_g={N_g}")
