@@ -337,6 +337,7 @@ static csa_status check_attend_common(const uint16_t *q, const uint16_t *q_norm_
   REQUIRE(window >= 1 && window <= 4096, "window must be in [1, 4096]");
   REQUIRE(N_cap >= 1 && N_cap < (int64_t(1) << 31), "N_cap must be in [1, 2^31)");
   REQUIRE(W_cap >= 1 && N_cap + W_cap < (int64_t(1) << 31), "W_cap must be >= 1 and N_cap + W_cap < 2^31");
+  REQUIRE(N_cap + window < (int64_t(1) << 31), "N_cap + window must be < 2^31");
   REQUIRE(std::isfinite(softmax_scale) && softmax_scale > 0.f, "softmax_scale must be positive");
   REQUIRE(eps > 0.f && std::isfinite(eps), "eps must be positive");
   REQUIRE(rope_base > 1.f && std::isfinite(rope_base), "rope_base must be > 1");

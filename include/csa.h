@@ -232,7 +232,9 @@ size_t csa_index_topk_workspace_bytes(int B, int Sq, int64_t N_cap, int topk);
  *              W_cap >= window is required.
  *   out        bf16 [B, Sq, H, D]; lse fp32 [B, Sq, H] or NULL.
  * Limits: D in {64, 128, 256, 512}; H >= 1 (heads are processed in blocks of 16);
- *         rope_dim % 4 == 0, rope_dim <= D; 1 <= window <= 4096; 1 <= topk <= 2048.
+ *         rope_dim % 4 == 0, rope_dim <= D; 1 <= window <= 4096; 1 <= topk <= 2048;
+ *         N_cap + W_cap and N_cap + window below 2^31 (rows are named by 32-bit codes);
+ *         B * Sq <= 65535.
  */
 csa_status csa_attend(const uint16_t *q, const uint16_t *q_norm_w, const uint16_t *entries,
                       int64_t N_cap, const int32_t *topk_idx, int topk, const uint16_t *win_rows,

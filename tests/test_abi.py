@@ -132,6 +132,13 @@ def test_attend_rejects_bad_arguments(fn, kw, status):
     assert _attend(fn, **kw) == status
 
 
+def test_attend_rejects_row_codes_past_int32():
+    # row codes (entry index, or N_cap + window row) are 32-bit: the row list must fit
+    big = (1 << 31) - 100
+    assert _attend("hca_attend", N_cap=big, W_cap=64, window=128) == 1
+    assert _attend("csa_attend", N_cap=big, W_cap=99, window=128) == 1
+
+
 def test_attend_window_ring_needs_room_for_the_window():
     # win_pos0 NULL selects the ring layout, which must hold a whole window
     assert _attend("csa_attend", win_pos0=None, W_cap=64, window=128) == 1
