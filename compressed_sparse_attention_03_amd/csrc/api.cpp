@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -280,7 +281,10 @@ csa_status csa_quantize_keys(const uint16_t *x, int64_t rows, int dim, int forma
 
 size_t csa_index_topk_workspace_bytes(int B, int Sq, int64_t N_cap, int topk) {
   if (B <= 0 || Sq <= 0 || N_cap <= 0 || topk <= 0) return 256;
-  return csa::index_workspace_bytes(int64_t(B) * Sq, N_cap, topk);
+  // the larger of the two plans (tiles shared by several queries, or one query per workgroup):
+  // the plan depends on the key format and on whether full scores are asked for
+  return std::max(csa::index_workspace_bytes(B, Sq, N_cap, topk, CSA_KEY_F32),
+                  csa::index_workspace_bytes(B, Sq, N_cap, topk, CSA_KEY_FP8_E4M3));
 }
 
 csa_status csa_index_topk(const void *q_idx, const float *w_idx, const void *k_codes,
@@ -308,7 +312,9 @@ csa_status csa_index_topk(const void *q_idx, const float *w_idx, const void *k_c
   REQUIRE_PTR(q_pos0); REQUIRE_PTR(topk_idx);
   if (key_format != CSA_KEY_F32) REQUIRE_PTR(k_scales);
   REQUIRE_PTR_OR_NULL(scores);
-  const size_t need = csa::index_workspace_bytes(int64_t(B) * Sq, N_cap, topk);
+  // full scores are written by the one-query-per-workgroup kernel only
+  const int plan_format = scores ? CSA_KEY_F32 : key_format;
+  const size_t need = csa::index_workspace_bytes(B, Sq, N_cap, topk, plan_format);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(CSA_ERR_WORKSPACE, "index_topk needs %zu workspace bytes, got %zu", need, workspace_bytes);
   REQUIRE_PTR(workspace);
@@ -317,7 +323,7 @@ csa_status csa_index_topk(const void *q_idx, const float *w_idx, const void *k_c
   a.n_entries = n_entries; a.q_pos0 = q_pos0; a.topk_idx = topk_idx; a.scores = scores;
   a.workspace = workspace; a.format = key_format; a.B = B; a.Sq = Sq; a.H_I = H_I; a.D_I = D_I;
   a.m = m; a.topk = topk; a.N_cap = N_cap;
-  a.plan = csa::plan_index(int64_t(B) * Sq, N_cap, topk);
+  a.plan = csa::plan_index(B, Sq, N_cap, topk, plan_format);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = csa::launch_index_score(a, st);
   if (e != hipSuccess) return launched(e, "index_score launch");

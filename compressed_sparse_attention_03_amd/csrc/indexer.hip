@@ -78,8 +78,8 @@ struct QueryRaw {
   uint32_t wv[16];
   float w;
 };
-__device__ __forceinline__ void load_query_raw(const uint16_t *q, const float *w, int H_I, QueryRaw &raw) {
-  const int t = threadIdx.x & 255;
+__device__ __forceinline__ void load_query_raw(const uint16_t *q, const float *w, int H_I, QueryRaw &raw,
+                                               int t = int(threadIdx.x & 255)) {
   const int h = min(t >> 2, H_I - 1), c = t & 3;
   const uint4 *src = reinterpret_cast<const uint4 *>(q + h * 128 + c * 32);
 #pragma unroll
@@ -92,10 +92,11 @@ __device__ __forceinline__ void load_query_raw(const uint16_t *q, const float *w
 
 // Quantise one query's [H_I x 128] bf16 heads into LDS.  Thread t < 256 owns head t/4, values
 // 32*(t%4) .. +31; heads >= H_I are written as zeros (factor 0) so 4 head blocks are always valid.
+// Slot t (< 256) of the quantised query: head t/4, values 32*(t%4) .. +31; the 4 slots of a head
+// are 4 consecutive lanes (the head's maximum is reduced over them).
 template <int FMT>
-__device__ void prep_query_lds(const QueryRaw &raw, int H_I, QueryLds &ql) {
-  const int t = threadIdx.x;
-  if (t < 256) {
+__device__ __forceinline__ void prep_query_slot(const QueryRaw &raw, int t, int H_I, QueryLds &ql) {
+  {
     const bool act = t < 4 * H_I;
     const int h = t >> 2, c = t & 3;
     uint32_t wv[16];
@@ -140,6 +141,11 @@ __device__ void prep_query_lds(const QueryRaw &raw, int H_I, QueryLds &ql) {
       if (c == 0) ql.f[h] = act ? wh : 0.f;
     }
   }
+}
+
+template <int FMT>
+__device__ void prep_query_lds(const QueryRaw &raw, int H_I, QueryLds &ql) {
+  if (threadIdx.x < 256) prep_query_slot<FMT>(raw, int(threadIdx.x), H_I, ql);
 }
 
 // Per-lane MFMA operands of the quantised query (NHB head blocks of 16).
@@ -545,6 +551,204 @@ __global__ void __launch_bounds__(NT) index_score_kernel(IndexArgs a) {
   (void)nvalid_local;
 }
 
+// ---- kernel 1b (prefill): one key tile, eight queries of one sequence ------------------------
+// For calls with many queries per sequence (a prefill chunk) the same keys are scored against
+// consecutive queries.  Workgroup = (tile of 512 entries, 8 consecutive queries, sequence): the
+// tile's quantised keys are loaded into LDS once and every wave scores them against its own query
+// (quantised straight into MFMA operands, no LDS), then selects its candidates with a wave-local
+// radix select -- no workgroup barrier after the tile is loaded.  Scores are bit-identical to
+// index_score_kernel's (the same MFMA operands and epilogue order), so the selection is too.
+constexpr int kMultiQ = 8;              // queries per workgroup, one per wave
+constexpr int kMultiTile = 512;         // entries per tile
+
+// Keep the wave's largest keys (8 per lane, distinct, 0 = absent): the same cut as block_cut --
+// exactly `need` keys, or between keep_min and need - 1 when one histogram pass separates them --
+// on one wave, with the wave's own 256-bin histogram in LDS and no workgroup barrier (a wave's
+// LDS accesses complete in order; the fences keep the compiler from reordering them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+__device__ uint64_t wave_cut(const uint64_t (&keys)[8], int need, int keep_min, uint32_t *H) {
+  const int lane = threadIdx.x & 63;
+  uint64_t mn = ~uint64_t(0), mx = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (keys[k] != 0) { mn = umin64(mn, keys[k]); mx = umax64(mx, keys[k]); }
+  mn = wave_minmax_u64<true>(mn);
+  mx = wave_minmax_u64<false>(mx);
+  if (mn == mx) return mn;
+  int hi = 63 - __clzll(mn ^ mx);
+  uint64_t mask = hi == 63 ? 0 : ~((uint64_t(2) << hi) - 1);
+  uint64_t prefix = mn & mask;
+  int got = 0;
+  *reinterpret_cast<uint4 *>(&H[4 * lane]) = make_uint4(0, 0, 0, 0);
+  wave_lds_sync();
+  for (;;) {
+    const int width = hi + 1 < 8 ? hi + 1 : 8;
+    const int shift = hi - width + 1;
+    const uint64_t dmask = (uint64_t(1) << width) - 1;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (keys[k] != 0 && (keys[k] & mask) == prefix) atomicAdd(&H[(keys[k] >> shift) & dmask], 1u);
+    wave_lds_sync();
+    const uint4 c4 = *reinterpret_cast<const uint4 *>(&H[252 - 4 * lane]);
+    const int c[4] = {int(c4.w), int(c4.z), int(c4.y), int(c4.x)};   // bins 255-4l .. 252-4l
+    const int sum = c[0] + c[1] + c[2] + c[3];
+    int cum = wave_incl_scan(sum, lane) - sum;
+    int hit = 0, d_sel = 0, above = 0, bucket = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (!hit && cum < need && need <= cum + c[j]) { hit = 1; d_sel = 255 - 4 * lane - j; above = cum; bucket = c[j]; }
+      cum += c[j];
+    }
+    const int src = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)__ballot(hit)) - 1);
+    d_sel = __builtin_amdgcn_readlane(d_sel, src);
+    above = __builtin_amdgcn_readlane(above, src);
+    bucket = __builtin_amdgcn_readlane(bucket, src);
+    *reinterpret_cast<uint4 *>(&H[252 - 4 * lane]) = make_uint4(0, 0, 0, 0);   // for the next pass
+    wave_lds_sync();
+    if (bucket != need - above && got + above >= keep_min)
+      return (prefix | (uint64_t(d_sel) << shift)) + (uint64_t(1) << shift);
+    got += above;
+    need -= above;
+    prefix |= uint64_t(d_sel) << shift;
+    mask |= dmask << shift;
+    if (bucket == need || shift == 0) {
+      uint64_t m2 = ~uint64_t(0);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (keys[k] != 0 && (keys[k] & mask) == prefix) m2 = umin64(m2, keys[k]);
+      return wave_minmax_u64<true>(m2);
+    }
+    hi = shift - 1;
+  }
+}
+
+struct alignas(16) MultiShared {
+  union {
+    struct {
+      uint8_t codes[kMultiTile * 128];    // fp8 [entry][128]; MXFP4 [entry][64]
+      uint32_t scales[kMultiTile];        // fp8: row scale bits; MXFP4: the row's four e8m0 bytes
+    } tile;
+    QueryLds q[kMultiQ];                  // before the tile arrives: each wave's quantised query
+  };
+  uint32_t hist[kMultiQ][256];            // each wave's select histogram
+};
+
+template <int FMT, int NHB>
+__global__ void __launch_bounds__(64 * kMultiQ, 2) index_score_multi_kernel(IndexArgs a) {
+  __shared__ MultiShared sh;
+  constexpr int NT = 64 * kMultiQ;
+  constexpr int RB = FMT == 1 ? 128 : 64;                      // code bytes per entry
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile_id = blockIdx.x, b = blockIdx.z;
+  const int s0 = blockIdx.y * kMultiQ;
+  const int tile = a.plan.tile, cand = a.plan.cand;
+  const int64_t e_begin = int64_t(tile_id) * tile;
+  const int64_t row0 = int64_t(b) * a.N_cap + e_begin;
+  const int rows = int(min(int64_t(tile), a.N_cap - e_begin));
+  // the tile's keys, through range-checked buffer loads (rows past N_cap read zeros), go to
+  // registers first; the LDS they land in holds the waves' quantised queries until then
+  constexpr int LPT = kMultiTile * RB / 16 / NT;               // 16-byte loads per thread
+  uint4 v[LPT];
+  uint32_t sc;
+  {
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(static_cast<const uint8_t *>(a.k_codes) + row0 * RB), short(0), rows * RB, kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(static_cast<const uint8_t *>(a.k_scales) + row0 * 4), short(0), rows * 4, kRawBufferWord3);
+#pragma unroll
+    for (int l = 0; l < LPT; ++l)
+      v[l] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, uint32_t((l * NT + tid) * 16), 0, 0));
+    sc = __builtin_amdgcn_raw_buffer_load_b32(rs, uint32_t(tid * 4), 0, 0);
+  }
+  // this wave's query, quantised into its LDS slot four (head, quarter) slots per lane at a time
+  // (the encoders of the one-query kernel), then read back as MFMA operands
+  const int s = s0 + wave;
+  const bool live = s < a.Sq;
+  const int64_t qi = int64_t(b) * a.Sq + (live ? s : a.Sq - 1);
+  {
+    const uint16_t *qsrc = static_cast<const uint16_t *>(a.q_idx) + qi * a.H_I * 128;
+    const float *wsrc = a.w_idx + qi * a.H_I;
+#pragma unroll 1
+    for (int it = 0; it < 4; ++it) {
+      QueryRaw raw;
+      load_query_raw(qsrc, wsrc, a.H_I, raw, it * 64 + lane);
+      prep_query_slot<FMT>(raw, it * 64 + lane, a.H_I, sh.q[wave]);
+    }
+  }
+  wave_lds_sync();
+  QueryFrag<NHB> qf;
+  load_query_frag<FMT, NHB>(sh.q[wave], lane, qf);
+  const int64_t t = a.q_pos0[b] + s;
+  const int64_t n_vis = min(a.n_entries[b], (t + 1) / a.m);
+  const int vis = int(max(int64_t(0), min(int64_t(tile), n_vis - e_begin)));
+  lds_barrier();                                                // every wave has its query
+#pragma unroll
+  for (int l = 0; l < LPT; ++l) *reinterpret_cast<uint4 *>(sh.tile.codes + (l * NT + tid) * 16) = v[l];
+  sh.tile.scales[tid] = sc;
+  lds_barrier();                                                // the tile is in LDS
+  if (!live) return;
+  const int64_t n_q = int64_t(a.B) * a.Sq;
+  uint64_t *cand_keys = static_cast<uint64_t *>(a.workspace);
+  uint64_t *cand_bound = cand_keys + n_q * a.plan.n_tiles * cand;
+  int *cand_count = reinterpret_cast<int *>(cand_bound + n_q * a.plan.n_tiles);
+  const int64_t out_slot = qi * a.plan.n_tiles + tile_id;
+  // scores: group j (16 entries) lands in lanes 16 (j % 4) .. + 15, slot j / 4 -- entry 64 slot + lane
+  const int g = lane >> 4, r = lane & 15;
+  constexpr int fmt = FMT == 1 ? 0 : 4;                        // instruction format code
+  uint64_t keys[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) keys[k] = 0;
+  const int ngroups = (vis + 15) >> 4;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+#pragma unroll 1
+   for (int jj = 0; jj < 4; ++jj) {
+    const int j = 4 * k + jj;
+    if (j < ngroups) {
+      const int el = 16 * j + r;
+      const uint8_t *cp = sh.tile.codes + el * RB + g * (FMT == 1 ? 32 : 16);
+      const uint4 x0 = *reinterpret_cast<const uint4 *>(cp);
+      const uint4 x1 = FMT == 1 ? *reinterpret_cast<const uint4 *>(cp + 16) : make_uint4(0, 0, 0, 0);
+      const uint32_t ksc = sh.tile.scales[el];
+      const v8i bop = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+      const int sb = FMT == 1 ? 127 : int((ksc >> (8 * g)) & 0xff);
+      v4f c[NHB];
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
+        c[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf.a[hb], bop, v4f{0.f, 0.f, 0.f, 0.f}, fmt, fmt, 0,
+                                                                 qf.sa[hb], 0, sb);
+      float acc = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc = fmaf(qf.f[hb][v], relu(c[hb][v]), acc);
+      acc = lane_group_sum(acc);
+      const float score = acc * (FMT == 1 ? __uint_as_float(ksc) : 1.0f);
+      if (g == jj && el < vis) keys[k] = make_key(score, uint32_t(e_begin + el));
+    }
+   }
+  }
+  uint64_t bound = 0;
+  if (vis > cand) bound = wave_cut(keys, cand, cand / 2, sh.hist[wave]);
+  // kept keys in ascending entry order (slot-major: entry 64 slot + lane)
+  uint64_t *dst = cand_keys + out_slot * cand;
+  int base = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const bool keep = keys[k] != 0 && keys[k] >= bound;
+    const uint64_t m = __ballot(keep);
+    if (keep) dst[base + __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0))] = keys[k];
+    base += __popcll(m);
+  }
+  if (lane == 0) { cand_count[out_slot] = base; cand_bound[out_slot] = bound; }
+}
+
 // ---- kernel 2: merge ----------------------------------------------------------------------
 struct alignas(16) MergeShared {
   QueryLds ql;
@@ -763,6 +967,10 @@ __global__ void __launch_bounds__(kMergeThreads) index_merge_kernel(IndexArgs a)
 template <int FMT, int NHB>
 hipError_t launch_score_t(const IndexArgs &a, hipStream_t stream) {
   hipError_t e = hipSuccess;
+  if (a.plan.multi) {
+    const dim3 mgrid(unsigned(a.plan.n_tiles), unsigned((a.Sq + kMultiQ - 1) / kMultiQ), unsigned(a.B));
+    return launch("index_score", index_score_multi_kernel<FMT, NHB>, mgrid, dim3(64 * kMultiQ), stream, a);
+  }
   dim3 grid(unsigned(a.plan.n_tiles), unsigned(int64_t(a.B) * a.Sq));
   switch (a.plan.tile) {
     case 64: case 128: case 256:
@@ -795,11 +1003,16 @@ hipError_t launch_merge_t(const IndexArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-IndexPlan plan_index(int64_t n_queries, int64_t N_cap, int topk) {
+IndexPlan plan_index(int64_t B, int64_t Sq, int64_t N_cap, int topk, int format) {
   IndexPlan p;
+  const int64_t n_queries = B * Sq;
+  // many queries per sequence (a prefill chunk) with quantised keys: tiles of 512 shared by eight
+  // queries (index_score_multi_kernel)
+  p.multi = (format != 0 && Sq >= kMultiQ && N_cap > kMultiTile && N_cap <= int64_t(kMaxCand / 8) * kMultiTile) ? 1 : 0;
   int tile = kMaxTile;
-  while (tile > 64 && n_queries * ((N_cap + tile - 1) / tile) < 512) tile >>= 1;
-  while (tile > 64 && tile / 2 >= N_cap) tile >>= 1;
+  if (p.multi) tile = kMultiTile;
+  while (!p.multi && tile > 64 && n_queries * ((N_cap + tile - 1) / tile) < 512) tile >>= 1;
+  while (!p.multi && tile > 64 && tile / 2 >= N_cap) tile >>= 1;
   p.tile = tile;
   p.n_tiles = int((N_cap + tile - 1) / tile);
   // keep ~4x the expected number of winners per tile, within the merge kernel's capacity
@@ -812,9 +1025,9 @@ IndexPlan plan_index(int64_t n_queries, int64_t N_cap, int topk) {
   return p;
 }
 
-size_t index_workspace_bytes(int64_t n_queries, int64_t N_cap, int topk) {
-  IndexPlan p = plan_index(n_queries, N_cap, topk);
-  const int64_t slots = n_queries * p.n_tiles;
+size_t index_workspace_bytes(int64_t B, int64_t Sq, int64_t N_cap, int topk, int format) {
+  IndexPlan p = plan_index(B, Sq, N_cap, topk, format);
+  const int64_t slots = B * Sq * p.n_tiles;
   return size_t(slots * p.cand * 8 + slots * 8 + slots * 4 + 256);
 }
 

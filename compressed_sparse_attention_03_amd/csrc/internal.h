@@ -55,9 +55,10 @@ struct IndexPlan {
   int tile;        // entries per tile (multiple of 64)
   int cand;        // candidates kept per tile (power of two, <= tile)
   int n_tiles;     // tiles per query
+  int multi;       // tiles shared by eight queries of a sequence (prefill-sized calls)
 };
-IndexPlan plan_index(int64_t n_queries, int64_t N_cap, int topk);
-size_t index_workspace_bytes(int64_t n_queries, int64_t N_cap, int topk);
+IndexPlan plan_index(int64_t B, int64_t Sq, int64_t N_cap, int topk, int format);
+size_t index_workspace_bytes(int64_t B, int64_t Sq, int64_t N_cap, int topk, int format);
 
 struct IndexArgs {
   const void *q_idx;

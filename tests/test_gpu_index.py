@@ -88,6 +88,51 @@ def test_few_visible_entries(fmt):
     run_quantised(q, w, k, fmt, 4, 16, [0], tag="few")
 
 
+def _both_paths(q, w, k, fmt, m, topk, t_first, n_entries, tag, sample=None):
+    """Run the call twice: without scores (many queries per sequence: key tiles shared by eight
+    queries) and with scores (one query per workgroup).  The shared-tile selection is checked
+    against the oracle (all queries, or ``sample``), and both selections must be identical (same
+    scores bit for bit, exact selection)."""
+    sel_shared = run_quantised(q, w, k, fmt, m, topk, t_first, n_entries=n_entries, tag=tag + " shared tiles",
+                               check_scores=False, sample=sample)
+    codes, scales = ops.csa_quantize_keys(dev_bf16(k), fmt)
+    sel_one, _ = ops.csa_index_topk(dev_bf16(q), dev(w), codes, scales, key_format=fmt,
+                                    n_entries=dev(np.asarray(n_entries, np.int64)),
+                                    q_pos0=dev(np.asarray(t_first, np.int64)), m=m, topk=topk, scores=True)
+    assert np.array_equal(sel_shared, sel_one.cpu().numpy()), f"{tag}: shared-tile and one-query selections differ"
+    return sel_shared
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_shared_key_tiles_for_many_queries(fmt):
+    # 37 queries per sequence (not a multiple of 8), causal visibility from 25 entries up, a cache
+    # that ends inside a tile and a sequence with fewer valid entries than its capacity
+    B, Sq, N, H_I = 2, 37, 3000, 64
+    q = gen.normal_bf16(64, 0, (B * Sq * H_I, 128)).reshape(B, Sq, H_I, 128)
+    w = gen.uniform_f32(64, 1, (B * Sq * H_I,)).reshape(B, Sq, H_I)
+    k = gen.normal_bf16(64, 2, (B * N, 128)).reshape(B, N, 128)
+    _both_paths(q, w, k, fmt, 4, 256, [100, 11000], [N, 2500], tag=f"shared {fmt}")
+
+
+def test_shared_key_tiles_clustered_winners_take_the_fallback():
+    # eight queries (one workgroup of the shared-tile kernel) whose 100 planted winners sit in one
+    # 512-entry tile: more than the tile keeps, so the merge re-scores it
+    N, H_I, Sq = 65536, 64, 8
+    q1 = gen.normal_bf16(65, 0, (H_I, 128)).reshape(1, 1, H_I, 128)
+    q = np.repeat(q1, Sq, axis=1)
+    w1 = gen.uniform_f32(65, 1, (1, H_I)).reshape(1, 1, H_I)
+    w = np.repeat(w1, Sq, axis=1)
+    kf = gen.normal_f32(65, 2, (N, 128))
+    kp = gen.planted_key(q1[0, 0], w1[0, 0])
+    g = np.random.default_rng(5)
+    hot = 2048 + g.choice(512, 100, replace=False)
+    kf[hot] = kp * g.uniform(0.5, 1.0, (hot.size, 1)).astype(np.float32)
+    k = gen.f32_to_bf16_bits(kf).reshape(1, N, 128)
+    sel = _both_paths(q, w, k, "fp8", 4, 1024, [4 * N - Sq], [N], tag="shared clustered", sample=[0, Sq - 1])
+    for s in range(Sq):
+        assert set(hot.tolist()) <= set(sel[0, s].tolist()), f"query {s}"
+
+
 def test_clustered_winners_take_the_exact_fallback():
     # 100 winners inside one 128-entry tile and 40 in another: more than a tile keeps as
     # candidates, so the merge must re-score those tiles.
@@ -149,6 +194,9 @@ def test_prefill_chunk_full_size_sampled():
     k_idx = gen.normal_bf16(w.cfg, gen.T_KIDX, (N, w.D_I)).reshape(1, N, w.D_I)
     g = np.random.default_rng(7)
     sample = sorted(set([0, 1, Sq - 1] + g.integers(0, Sq, 9).tolist()))
+    # scores and sets of the one-query path, then the shared-tile path (the call without scores)
+    # against the oracle and against the first selection
+    _both_paths(q_idx, w_idx, k_idx, w.key_format, w.m, w.topk, [w.T], [N], tag="prefill", sample=sample)
     run_quantised(q_idx, w_idx, k_idx, w.key_format, w.m, w.topk, [w.T], tag="prefill", sample=sample)
 
 
