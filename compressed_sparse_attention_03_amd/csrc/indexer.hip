@@ -14,6 +14,9 @@
 // or MXFP4 with its e8m0 block scales applied by the instruction).  The tile's scores stay in LDS;
 // a block radix select keeps the tile's `cand` best (score, index) keys, written in ascending
 // index order together with the smallest kept key.
+// Kernel 1b (index_score_multi_kernel, calls with eight or more queries per sequence): a tile of
+// 512 keys is loaded into LDS once and scored against eight queries, one per wave, each wave
+// keeping its own candidates (same scores, same candidate layout).
 // Kernel 2 (index_merge): one workgroup per query selects the k best keys among all candidates.
 // A tile whose smallest kept key beats the k-th best may hide further winners; such tiles are
 // re-scored in the merge workgroup (exact, slow, rare).
