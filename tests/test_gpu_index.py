@@ -103,15 +103,15 @@ def _both_paths(q, w, k, fmt, m, topk, t_first, n_entries, tag, sample=None):
     return sel_shared
 
 
-@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
-def test_shared_key_tiles_for_many_queries(fmt):
+@pytest.mark.parametrize("fmt,H_I", [("fp8", 64), ("mxfp4", 64), ("fp8", 16), ("mxfp4", 32)])
+def test_shared_key_tiles_for_many_queries(fmt, H_I):
     # 37 queries per sequence (not a multiple of 8), causal visibility from 25 entries up, a cache
     # that ends inside a tile and a sequence with fewer valid entries than its capacity
-    B, Sq, N, H_I = 2, 37, 3000, 64
+    B, Sq, N = 2, 37, 3000
     q = gen.normal_bf16(64, 0, (B * Sq * H_I, 128)).reshape(B, Sq, H_I, 128)
     w = gen.uniform_f32(64, 1, (B * Sq * H_I,)).reshape(B, Sq, H_I)
     k = gen.normal_bf16(64, 2, (B * N, 128)).reshape(B, N, 128)
-    _both_paths(q, w, k, fmt, 4, 256, [100, 11000], [N, 2500], tag=f"shared {fmt}")
+    _both_paths(q, w, k, fmt, 4, 256, [100, 11000], [N, 2500], tag=f"shared {fmt} H{H_I}")
 
 
 def test_shared_key_tiles_clustered_winners_take_the_fallback():
