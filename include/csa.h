@@ -44,7 +44,7 @@ extern "C" {
 typedef enum csa_status {
   CSA_OK = 0,
   CSA_ERR_INVALID = 1,     /* an argument is out of its documented range; nothing enqueued */
-  CSA_ERR_UNSUPPORTED = 2, /* a valid shape or format this build has no kernel for; nothing enqueued */
+  CSA_ERR_UNSUPPORTED = 2, /* a valid shape or format the library has no kernel for; nothing enqueued */
   CSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required; nothing enqueued */
   CSA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
 } csa_status;
