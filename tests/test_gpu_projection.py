@@ -23,6 +23,7 @@ def _case(M, H, D, G, N_g):
 @pytest.mark.parametrize("M,H,D,G,N_g", [
     (4, 64, 512, 8, 512),        # a decode step of four sequences: weights streamed (small-M path)
     (1, 16, 128, 2, 128),
+    (8, 4, 128, 2, 128),         # K per group 256: the eight-wave small-M kernel
     (16, 64, 512, 8, 512),       # largest small-M call
     (17, 64, 512, 8, 512),       # smallest tiled call, ragged tile
     (300, 16, 256, 4, 256),
