@@ -264,6 +264,33 @@ def cpu_baseline(w: gen.Workload, budget_s: float = 12.0):
                       f"top-{w.topk}, attention over {w.topk}+{w.window} rows); keys pre-quantised"}
 
 
+def stream_floor(nbytes: int, launches: int = 240):
+    """The library's plain streaming read (csa_measure_stream_read) of `nbytes`, timed like the
+    kernels (events in each dispatch), over enough rotating buffers to miss the 256 MB
+    Infinity Cache: the bandwidth a bandwidth-bound kernel of that byte count can reach here."""
+    nbytes = (int(nbytes) + 15) // 16 * 16
+    nbuf = max(2, math.ceil(2 * MALL_BYTES / nbytes))
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    for i, b in enumerate(bufs):
+        b.fill_(i + 1)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for i in range(2 * nbuf):                                  # warm-up
+        ops.measure_stream_read(bufs[i % nbuf], sink)
+    torch.cuda.synchronize()
+    ops.timing_enable(True)
+    for i in range(launches):
+        ops.measure_stream_read(bufs[i % nbuf], sink)
+    torch.cuda.synchronize()
+    ms, cnt = ops.timing_read("stream_read")
+    ops.timing_enable(False)
+    del bufs
+    torch.cuda.empty_cache()
+    us = 1000.0 * ms / cnt
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": "stream_read", "bytes": nbytes, "avg_us": us, "achieved": gbs, "unit": "GB/s",
+            "frac_of_peak": gbs / PEAK_HBM_GBS, "buffers": nbuf, "launches": cnt}
+
+
 COPY_BYTES, COPY_LAUNCHES = 1 << 30, 5
 
 
@@ -601,6 +628,11 @@ def main():
         "kernel_us": m["kernel_us"],
         "also": [results[k] for k in legs if k != main_name],
     }
+    # the plain streaming read of the dominant kernel's byte count, timed the same way
+    rf = line["roofline"]
+    rf["stream_floor"] = stream_floor(rf["algorithmic_bytes"])
+    rf["frac_of_stream_floor"] = rf["achieved"] / rf["stream_floor"]["achieved"]
+    log(json.dumps({"stream_floor": rf["stream_floor"]}))
     if not args.no_cpu and w.kind == "csa_decode":
         log("timing the CPU oracle ...")
         line["cpu_baseline"] = cpu_baseline(w)

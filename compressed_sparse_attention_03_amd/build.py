@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libcsa.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "compress.hip", "quantize.hip", "indexer.hip", "attend.hip", "projection.hip"]
+SOURCES = ["api.cpp", "compress.hip", "quantize.hip", "indexer.hip", "attend.hip", "projection.hip",
+           "measure.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

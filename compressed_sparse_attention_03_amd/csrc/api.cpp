@@ -265,6 +265,15 @@ csa_status csa_output_projection(const uint16_t *o, const uint16_t *w, int M, in
   return launched(e, "output projection launch");
 }
 
+csa_status csa_measure_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream) {
+  REQUIRE(bytes > 0 && bytes % 16 == 0, "bytes must be a positive multiple of 16");
+  REQUIRE(bytes <= (int64_t(1) << 40), "bytes must be <= 2^40");
+  REQUIRE_PTR(src);
+  REQUIRE(sink != nullptr && (reinterpret_cast<uintptr_t>(sink) & 3u) == 0, "sink must be a 4-byte aligned pointer");
+  hipError_t e = csa::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream));
+  return launched(e, "stream read launch");
+}
+
 csa_status csa_quantize_keys(const uint16_t *x, int64_t rows, int dim, int format, void *codes,
                              void *scales, void *stream) {
   REQUIRE(format == CSA_KEY_FP8_E4M3 || format == CSA_KEY_MXFP4, "format must be CSA_KEY_FP8_E4M3 or CSA_KEY_MXFP4");

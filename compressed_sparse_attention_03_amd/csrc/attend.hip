@@ -91,14 +91,16 @@ struct AttendTile {
   bool valid;
 };
 __device__ __forceinline__ AttendTile attend_tile(const AttendArgs &a, int64_t n_queries, int grid_splits) {
-  const int64_t L = blockIdx.x;
-  const int64_t x = L & 7, rest = L >> 3;
-  const int hb = int(rest % a.plan.n_hb);
-  const int64_t pair = (rest / a.plan.n_hb) * 8 + x;
+  // 32-bit unsigned arithmetic: the grid holds fewer than 2^31 workgroups
+  const uint32_t L = blockIdx.x;
+  const uint32_t x = L & 7u, rest = L >> 3;
+  const uint32_t n_hb = uint32_t(a.plan.n_hb), gs = uint32_t(grid_splits);
+  const uint32_t hb = rest % n_hb;
+  const uint32_t pair = (rest / n_hb) * 8u + x;
   AttendTile t;
-  t.valid = pair < n_queries * grid_splits;
-  t.qi = pair / grid_splits;
-  t.split = int(pair % grid_splits);
+  t.valid = int64_t(pair) < n_queries * grid_splits;
+  t.qi = int64_t(pair / gs);
+  t.split = int(pair % gs);
   t.hb = hb;
   return t;
 }
@@ -182,9 +184,9 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
   if (!tl.valid) return;
   const int hb = tl.hb;
   const int64_t qi = tl.qi;
-  const int b = int(qi / a.Sq), s_idx = int(qi % a.Sq);
+  const int b = int(uint32_t(qi) / uint32_t(a.Sq)), s_idx = int(qi) - b * a.Sq;   // B * Sq < 2^16
   const int64_t t = a.q_pos0[b] + s_idx;
-  const int64_t n_vis = a.topk_idx ? 0 : min(a.n_entries[b], (t + 1) / a.m);
+  const int64_t n_vis = a.topk_idx ? 0 : min(a.n_entries[b], div_count(t + 1, a.m));
   const int split_first = FUSED ? 0 : tl.split;
   const int split_end = FUSED ? a.plan.n_splits : tl.split + 1;
 

@@ -20,6 +20,14 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ---- bf16 storage ---------------------------------------------------------------------------
+// Entries visible at position x - 1, i.e. x / m for a token count x >= 0 (C division): 32-bit
+// unsigned division whenever x fits, which is every real position (a 64-bit division by a runtime
+// value is a long scalar sequence in a kernel prologue).
+__device__ __forceinline__ int64_t div_count(int64_t x, int m) {
+  if (x >= 0 && x <= int64_t(0xffffffffu)) return int64_t(uint32_t(x) / uint32_t(m));
+  return x / m;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

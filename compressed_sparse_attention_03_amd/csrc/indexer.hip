@@ -235,35 +235,47 @@ __device__ __forceinline__ void load_batch(const TileKeys<FMT> &tk, int g0, int 
 // every negative float (and -0) is a negative integer.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-// Scores of one batch of groups: every MFMA first, then the per-head ReLU/weight epilogues, so the
-// epilogues do not wait on MFMA latency.  Each entry's score is reduced across its 4 lanes and
-// written to s_scores by lanes 0..15; entries at tile-local index >= vis get -inf.
+// Scores of one group of 16 entries: the NHB MFMAs of the group (query head blocks x the group's
+// keys), then the per-head ReLU/weight epilogue.  Each entry's score is reduced across its 4 lanes
+// and written to s_scores by lanes 0..15; entries at tile-local index >= vis get -inf.
+template <int FMT, int NHB>
+__device__ __forceinline__ void group_mfma(const QueryFrag<NHB> &qf, const KeyFrag<FMT> &kf, int lane, v4f (&c)[NHB]) {
+  constexpr int fmt = FMT == 1 ? 0 : 4;   // instruction format code: 0 = fp8 e4m3, 4 = fp4 e2m1
+  const uint4 x0 = kf.c0, x1 = FMT == 1 ? kf.c1 : make_uint4(0, 0, 0, 0);
+  const v8i bop = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+  const int sb = FMT == 1 ? 127 : int((kf.s >> (8 * (lane >> 4))) & 0xff);
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb)
+    c[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf.a[hb], bop, v4f{0.f, 0.f, 0.f, 0.f}, fmt, fmt, 0,
+                                                             qf.sa[hb], 0, sb);
+}
+
+template <int FMT, int NHB>
+__device__ __forceinline__ void group_epilogue(const QueryFrag<NHB> &qf, const v4f (&c)[NHB], uint32_t s, int grp,
+                                               int ngroups, int vis, int lane, float *s_scores) {
+  float acc = 0.f;
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc = fmaf(qf.f[hb][v], relu(c[hb][v]), acc);
+  acc = lane_group_sum(acc);
+  const int el = grp * 16 + (lane & 15);
+  const float ks = FMT == 1 ? __uint_as_float(s) : 1.0f;
+  if (lane < 16 && grp < ngroups) s_scores[el] = el < vis ? acc * ks : -INFINITY;
+}
+
+// Scores of one batch of groups, software-pipelined by one group: the MFMAs of group u + 1 are
+// issued before the epilogue of group u, so an epilogue does not wait on MFMA latency and only two
+// groups' results are live at a time.
 template <int FMT, int NHB>
 __device__ __forceinline__ void score_batch(const QueryFrag<NHB> &qf, const KeyFrag<FMT> (&kf)[batch_of<FMT>()], int g0,
                                             int ngroups, int vis, int lane, float *s_scores) {
-  constexpr int fmt = FMT == 1 ? 0 : 4;   // instruction format code: 0 = fp8 e4m3, 4 = fp4 e2m1
-  v4f c[batch_of<FMT>()][NHB];
+  v4f c[2][NHB];
+  group_mfma<FMT, NHB>(qf, kf[0], lane, c[0]);
 #pragma unroll
   for (int u = 0; u < batch_of<FMT>(); ++u) {
-    const uint4 x0 = kf[u].c0, x1 = FMT == 1 ? kf[u].c1 : make_uint4(0, 0, 0, 0);
-    const v8i bop = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
-    const int sb = FMT == 1 ? 127 : int((kf[u].s >> (8 * (lane >> 4))) & 0xff);
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb)
-      c[u][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf.a[hb], bop, v4f{0.f, 0.f, 0.f, 0.f}, fmt,
-                                                                  fmt, 0, qf.sa[hb], 0, sb);
-  }
-#pragma unroll
-  for (int u = 0; u < batch_of<FMT>(); ++u) {
-    float acc = 0.f;
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc = fmaf(qf.f[hb][v], relu(c[u][hb][v]), acc);
-    acc = lane_group_sum(acc);
-    const int el = (g0 + u) * 16 + (lane & 15);
-    const float ks = FMT == 1 ? __uint_as_float(kf[u].s) : 1.0f;
-    if (lane < 16 && g0 + u < ngroups) s_scores[el] = el < vis ? acc * ks : -INFINITY;
+    if (u + 1 < batch_of<FMT>()) group_mfma<FMT, NHB>(qf, kf[u + 1], lane, c[(u + 1) & 1]);
+    group_epilogue<FMT, NHB>(qf, c[u & 1], kf[u].s, g0 + u, ngroups, vis, lane, s_scores);
   }
 }
 
@@ -472,7 +484,7 @@ __global__ void __launch_bounds__(NT) index_score_kernel(IndexArgs a) {
   __shared__ ScoreShared sh;
   const int tile_id = blockIdx.x;
   const int64_t qi = blockIdx.y;                               // query = b * Sq + s
-  const int b = int(qi / a.Sq), s = int(qi % a.Sq);
+  const int b = int(blockIdx.y / uint32_t(a.Sq)), s = int(blockIdx.y) - b * a.Sq;
   const int tile = a.plan.tile, cand = a.plan.cand;
   const int64_t e_begin = int64_t(tile_id) * tile;
   const int64_t out_slot = qi * a.plan.n_tiles + tile_id;
@@ -498,7 +510,7 @@ __global__ void __launch_bounds__(NT) index_score_kernel(IndexArgs a) {
     load_batch<FMT>(tk, g_first + (NT / 64) * batch_of<FMT>(), threadIdx.x & 63, kb);
   }
   const int64_t t = a.q_pos0[b] + s;
-  const int64_t n_vis = min(a.n_entries[b], (t + 1) / a.m);
+  const int64_t n_vis = min(a.n_entries[b], div_count(t + 1, a.m));
   const int vis = int(max(int64_t(0), min(int64_t(tile), n_vis - e_begin)));
 
   if (vis == 0 && a.scores == nullptr) {                      // nothing visible in this tile
@@ -688,7 +700,7 @@ __global__ void __launch_bounds__(64 * kMultiQ, 2) index_score_multi_kernel(Inde
   QueryFrag<NHB> qf;
   load_query_frag<FMT, NHB>(sh.q[wave], lane, qf);
   const int64_t t = a.q_pos0[b] + s;
-  const int64_t n_vis = min(a.n_entries[b], (t + 1) / a.m);
+  const int64_t n_vis = min(a.n_entries[b], div_count(t + 1, a.m));
   const int vis = int(max(int64_t(0), min(int64_t(tile), n_vis - e_begin)));
   lds_barrier();                                                // every wave has its query
 #pragma unroll
@@ -897,10 +909,10 @@ __global__ void __launch_bounds__(kMergeThreads) index_merge_kernel(IndexArgs a)
   constexpr int NT = kMergeThreads;
   const int tid = threadIdx.x;
   const int64_t qi = blockIdx.x;
-  const int b = int(qi / a.Sq), s = int(qi % a.Sq);
+  const int b = int(blockIdx.x / uint32_t(a.Sq)), s = int(blockIdx.x) - b * a.Sq;
   const int cand = a.plan.cand, n_tiles = a.plan.n_tiles;
   const int64_t t = a.q_pos0[b] + s;
-  const int64_t n_vis = min(a.n_entries[b], (t + 1) / a.m);
+  const int64_t n_vis = min(a.n_entries[b], div_count(t + 1, a.m));
   const int k_eff = int(min(int64_t(a.topk), n_vis));
   const int64_t n_q = int64_t(a.B) * a.Sq;
   const uint64_t *cand_keys = static_cast<const uint64_t *>(a.workspace);

@@ -114,6 +114,9 @@ struct AttendArgs {
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream);
 hipError_t launch_combine(const AttendArgs &a, hipStream_t stream);
 
+// Plain streaming read of `bytes` (a positive multiple of 16) at `src` (measure.hip).
+hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t stream);
+
 // Kernel timing (api.cpp).  When timing is on, timing_events hands out a start/stop event pair
 // filed under `name`; launch() then passes them in the kernel's own dispatch, so they take the
 // kernel's start and end timestamps (no separate marker packets around it).

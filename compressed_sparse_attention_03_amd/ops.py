@@ -43,6 +43,7 @@ _SIGS = {
     "csa_status_string": (ctypes.c_char_p, [I32]),
     "csa_last_error": (ctypes.c_char_p, []),
     "csa_timing_enable": (None, [I32]),
+    "csa_measure_stream_read": (I32, [P, I64, P, P]),
     "csa_timing_read": (I32, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
 }
 
@@ -387,6 +388,17 @@ def csa_output_projection(o, w, out=None):
 
 def timing_enable(on: bool):
     lib().csa_timing_enable(1 if on else 0)
+
+
+def measure_stream_read(src, sink):
+    """Plain streaming read of every byte of ``src`` (a CUDA tensor of a multiple of 16 bytes);
+    ``sink`` is a CUDA tensor of at least 4 bytes that the read may write."""
+    if not (isinstance(src, torch.Tensor) and src.is_cuda and src.is_contiguous()):
+        raise TypeError("src must be a contiguous CUDA (HIP) tensor")
+    if not (isinstance(sink, torch.Tensor) and sink.is_cuda and sink.numel() * sink.element_size() >= 4):
+        raise TypeError("sink must be a CUDA (HIP) tensor of at least 4 bytes")
+    _check(lib().csa_measure_stream_read(ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size(),
+                                         ctypes.c_void_p(sink.data_ptr()), _stream()), "csa_measure_stream_read")
 
 
 def timing_read(kernel: str):

@@ -287,11 +287,23 @@ const char *csa_last_error(void);
  * Kernel timing for measurement tools.  csa_timing_enable(1) clears the counters and makes every
  * later launch record a pair of HIP events on its stream; csa_timing_enable(0) stops recording.
  * csa_timing_read() waits for the recorded events and returns the summed duration (ms) and the
- * launch count for one kernel name: "compress", "quantize", "index_score", "index_merge",
- * "attend_split", "attend_combine".  Not for use while a stream is being captured into a graph.
+ * launch count for one kernel name: "compress", "compress_keys", "quantize", "decode_append",
+ * "decode_append_keys", "index_score", "index_merge", "attend_split", "attend_combine", "oproj",
+ * "stream_read".  Not for use while a stream is being captured into a graph.
  */
 void csa_timing_enable(int on);
 csa_status csa_timing_read(const char *kernel, double *total_ms, int64_t *launches);
+
+/*
+ * Bandwidth floor for measurement tools: a plain streaming read of `bytes` bytes at `src` (device,
+ * 16-byte aligned; bytes a positive multiple of 16, at most 2^40), every 16-byte word loaded once
+ * by 4,096 workgroups of 512 threads.  Nothing is computed from the bytes; `sink` (device, 4-byte
+ * aligned, 4 bytes) is written at most once, with a value of no meaning.  Enqueued on `stream`;
+ * recorded under the timing name "stream_read".  A bandwidth-bound kernel of this library is
+ * compared with this read of its own byte count as well as with the device's published peak.
+ * Errors: CSA_ERR_INVALID for a bad size or pointer (before any HIP call); CSA_ERR_HIP on launch.
+ */
+csa_status csa_measure_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

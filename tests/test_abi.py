@@ -208,3 +208,13 @@ def test_quantize_rejects_bad_arguments():
     assert L.csa_quantize_keys(v, 10, 128, 0, v, v, None) == 1      # fp32 is not a code format
     assert L.csa_quantize_keys(v, 10, 100, 1, v, v, None) == 1
     assert L.csa_quantize_keys(v, 0, 128, 1, None, None, None) == 0
+
+
+def test_stream_read_rejects_bad_arguments():
+    L = ops.lib()
+    v = ctypes.c_void_p(16)
+    assert L.csa_measure_stream_read(v, 0, v, None) == 1          # empty
+    assert L.csa_measure_stream_read(v, 100, v, None) == 1        # not a multiple of 16
+    assert L.csa_measure_stream_read(None, 1024, v, None) == 1
+    assert L.csa_measure_stream_read(ctypes.c_void_p(8), 1024, v, None) == 1   # src misaligned
+    assert L.csa_measure_stream_read(v, 1024, None, None) == 1
