@@ -2,8 +2,8 @@
 // (selected compressed entries, or every visible entry for HCA) followed by the sliding-window
 // rows, in one joint softmax.
 //
-// "DeepSeek-V4: Million-Token Context" (codexsims explainer), CSA walk-through: each query head
-// attends to the picked set plus a sliding window of the most recent tokens; HCA walk-through:
+// "DeepSeek-V4: Million-Token Context" (codexsims explainer), CSA walk-through: every query head's
+// attention covers the selected entries together with a window of the newest tokens; HCA walk-through:
 // dense multi-query attention over every compressed entry plus the window.  paperlayer summary,
 // section 2.3: shared-KV multi-query attention; RMSNorm on the query heads before core attention.
 // dev.to "Two Compression Strategies": partial RoPE.

@@ -1,9 +1,9 @@
 // KV compressor: per-channel softmax pooling of each entry's tokens, RMSNorm, partial RoPE.
 //
-// "DeepSeek-V4: Million-Token Context" (codexsims explainer), CSA walk-through: every m tokens
-// become one entry through a learned softmax weighting; HCA walk-through: non-overlapping windows
-// of m' = 128 tokens.  "Follow the white rabbit" (sambatista.com), CSA paragraph: each entry also
-// draws on the previous group; HCA paragraph: weights differ per part of the representation.
+// "DeepSeek-V4: Million-Token Context" (codexsims explainer), CSA walk-through: each group of m
+// tokens is pooled into one entry with softmax weights that are learned; HCA walk-through: HCA
+// pools disjoint runs of m' = 128 tokens.  "Follow the white rabbit" (sambatista.com), CSA paragraph: an entry's pooling
+// reaches back over the preceding group as well; HCA paragraph: the pooling weights vary by channel.
 // paperlayer summary, section 2.3 "Other details": RMSNorm on compressed entries.
 //
 // Layout: one workgroup (4 waves) per entry.  A lane owns CPL = d/64 consecutive channels, so a

@@ -1,10 +1,10 @@
 // Lightning indexer and top-k selector.
 //
-// "DeepSeek-V4: Million-Token Context" (codexsims explainer), CSA walk-through: a small attention
-// head scores every compressed block against the current query and a top-k selector keeps only
-// the best.  "Follow the white rabbit" (sambatista.com), indexer paragraph: about 262,000 entries
-// at the longest context, the top 1,024 pass on; the pass is cheap because it uses smaller
-// representations and lower-precision numbers; its work grows with the context.
+// "DeepSeek-V4: Million-Token Context" (codexsims explainer), CSA walk-through: a lightweight
+// scoring head rates each compressed block for the present query and only the k highest-rated
+// blocks are kept.  "Follow the white rabbit" (sambatista.com), indexer paragraph: at the longest
+// context some 262,000 entries are rated and 1,024 survive; compact, low-precision operands keep
+// the rating cheap, though its cost still rises with the context length.
 //
 // score[i] = sum_h w[h] * max(0, <q~_h, k~_i>)  (the form stated in csa.h).
 //

@@ -1,8 +1,8 @@
 // Grouped output projection after core attention.
 //
 // "DeepSeek-V4: Towards Highly Efficient Million-Token Context Intelligence" (paperlayer summary),
-// section 2.3, shared-KV and output-projection paragraph: CSA and HCA both use a grouped output
-// projection, which makes projecting the many head outputs back to the hidden state cheaper.
+// section 2.3, shared-KV and output-projection paragraph: both attention types map their many head
+// outputs back to the model width through a projection split into groups, to cut that cost.
 //
 // y[m, g N_g + n] = sum_k o[m, g K_g + k] * w[g, n, k]: the heads fall into G groups; each group's
 // concatenated head outputs (K_g = H D / G values) go through its own weight [N_g, K_g] (stored

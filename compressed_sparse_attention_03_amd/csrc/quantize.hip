@@ -1,7 +1,7 @@
 // Quantise-on-write of lightning-indexer keys (fp8 e4m3 with a power-of-two row scale, or OCP
 // MXFP4).  "How DeepSeek-V4 Achieves Million-Token Contexts..." (dev.to), "Two Compression
 // Strategies": the indexer runs in FP4; "Follow the white rabbit" (sambatista.com), indexer
-// paragraph: smaller representations and lower-precision numbers.
+// paragraph: the indexer works on compact, low-precision operands.
 //
 // One wave per row, each lane owns 32/64-aligned runs of the row; integer-exact rules stated in
 // csa.h.

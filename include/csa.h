@@ -60,8 +60,8 @@ typedef enum csa_key_format {
 /*
  * csa_compress -- the KV compressor.
  * [EXPLAINER] CSA walk-through: every m tokens become one entry through a learned softmax
- * weighting; [RABBIT] CSA paragraph: each entry also draws on the previous group; [EXPLAINER] HCA
- * walk-through: non-overlapping windows of m' = 128 tokens; [SUMMARY] 2.3 "Other details": RMSNorm
+ * weighting; [RABBIT] CSA paragraph: an entry's pooling reaches back over the preceding group as
+ * well; [EXPLAINER] HCA walk-through: HCA pools disjoint runs of m' = 128 tokens; [SUMMARY] 2.3 "Other details": RMSNorm
  * on the compressed entries; [DEVTO] partial RoPE.
  *
  * For entry i and channel j the weights are a softmax over the entry's tokens of
@@ -125,9 +125,9 @@ csa_status csa_decode_append(const uint16_t *c_new, const uint16_t *z_new, const
 
 /*
  * csa_compress_index_keys -- lightning-indexer keys produced by compression, quantised on write.
- * [EXPLAINER] CSA walk-through: the indexer scores compressed blocks, each made from its group of
- * tokens by a learned softmax weighting; [RABBIT] indexer paragraph: the indexer works on smaller
- * representations in lower precision.
+ * [EXPLAINER] CSA walk-through: the indexer rates compressed blocks, each pooled from its group of
+ * tokens with learned softmax weights; [RABBIT] indexer paragraph: the indexer's operands are
+ * compact and low-precision.
  *
  * A per-token indexer stream c_i with logits z_i and bias bias_i is pooled exactly as
  * csa_compress pools (same groups, overlap, bias slots, entry 0 alone), with no RMSNorm and no
@@ -162,7 +162,7 @@ csa_status csa_decode_append_index(const uint16_t *c_i_new, const uint16_t *z_i_
 /*
  * csa_quantize_keys -- quantise lightning-indexer keys to their storage format (quantise on write).
  * [DEVTO] "Two Compression Strategies": the indexer runs in FP4; [RABBIT] indexer paragraph:
- * smaller representations and lower-precision numbers.
+ * the indexer works on compact, low-precision operands.
  *
  *   x       bf16 [rows, dim] keys.
  *   format  CSA_KEY_FP8_E4M3: codes uint8 [rows, dim]; scales fp32 [rows] = 2^e, e the smallest
@@ -179,9 +179,9 @@ csa_status csa_quantize_keys(const uint16_t *x, int64_t rows, int dim, int forma
 
 /*
  * csa_index_topk -- lightning-indexer scores and per-query top-k selection.
- * [EXPLAINER] CSA walk-through: a small attention head scores every compressed block against the
- * current query and the top-k selector keeps the best; [RABBIT] indexer paragraph: the top 1,024
- * of about 262,000 entries pass to attention.
+ * [EXPLAINER] CSA walk-through: a lightweight scoring head rates each compressed block for the
+ * present query and only the k highest-rated blocks are kept; [RABBIT] indexer paragraph: of some
+ * 262,000 entries at the longest context, 1,024 go on to attention.
  *
  * For query s of sequence b at position t = q_pos0[b] + s the visible entries are
  * i < min(n_entries[b], (t+1)/m) (an entry is usable once its last token exists).  Its score is
@@ -212,10 +212,10 @@ size_t csa_index_topk_workspace_bytes(int B, int Sq, int64_t N_cap, int topk);
 /*
  * csa_attend -- CSA core attention: shared-KV multi-query attention over the selected compressed
  * entries plus the sliding window, in one joint softmax.
- * [EXPLAINER] CSA walk-through: each query head attends to the picked set plus a sliding window of
- * the most recent tokens; [SUMMARY] 2.3: shared-KV multi-query attention, RMSNorm on the query
- * heads before core attention; [DEVTO] partial RoPE; [RABBIT] sliding-window paragraph: the
- * window holds the most recent 128 tokens.
+ * [EXPLAINER] CSA walk-through: every query head's attention covers the selected entries together
+ * with a window of the newest tokens; [SUMMARY] 2.3: shared-KV multi-query attention, RMSNorm on
+ * the query heads before core attention; [DEVTO] partial RoPE; [RABBIT] sliding-window paragraph:
+ * the window is the newest 128 tokens.
  *
  * For query s of sequence b at t = q_pos0[b] + s, every head h uses
  *     q^ = RoPE(RMSNorm(q[b,s,h,:]; q_norm_w, eps), t)
@@ -246,9 +246,9 @@ size_t csa_attend_workspace_bytes(int B, int Sq, int H, int D, int topk, int win
 
 /*
  * hca_attend -- HCA core attention: dense over every visible compressed entry plus the window.
- * [EXPLAINER] HCA walk-through: every query attends to all compressed entries -- the same
- * multi-query attention math on a much shorter sequence -- plus a sliding window of recent
- * uncompressed tokens.
+ * [EXPLAINER] HCA walk-through: no selection step -- each query sees every compressed entry
+ * (ordinary multi-query attention, over a far shorter sequence) together with a short window of
+ * the newest raw tokens.
  *
  * As csa_attend with the selection replaced by entries 0 .. min(n_entries[b], (t+1)/m) - 1.
  * Limits as csa_attend; N_cap < 2^31.
@@ -263,8 +263,8 @@ size_t hca_attend_workspace_bytes(int B, int Sq, int H, int D, int64_t N_cap, in
 
 /*
  * csa_output_projection -- grouped output projection of the core-attention head outputs.
- * [SUMMARY] 2.3, shared-KV and output-projection paragraph: CSA and HCA use a grouped output
- * projection, which makes projecting the many head outputs back to the hidden state cheaper.
+ * [SUMMARY] 2.3, shared-KV and output-projection paragraph: both attention types map their many
+ * head outputs back to the model width through a projection split into groups, to cut that cost.
  *
  * The H heads fall into G equal groups in head order; group g's concatenated head outputs
  * (K_g = H*D/G values) are projected by its own weight w[g] [N_g, K_g] (a linear layer's

@@ -22,10 +22,10 @@ page fixes and that no independent pin can fix are marked "parity unpinned" in t
 
 * the RoPE frequency schedule (base 10000, interleaved pairs): pinned only against GPT-J's
   interleaved rotary implementation, i.e. a convention, not a statement of the pages;
-* the indexer activation (ReLU) and head weighting: the pages only call the indexer "a small
-  attention head that scores" entries -- parity unpinned;
+* the indexer activation (ReLU) and head weighting: the pages describe the indexer only as a
+  lightweight scoring head -- parity unpinned;
 * the quantisation granularity of the indexer (per-row power-of-two fp8 scale; OCP MX blocks of
-  32 for fp4) -- the pages only say "lower-precision numbers" / "FP4": parity unpinned for the
+  32 for fp4) -- the pages name only low precision and FP4: parity unpinned for the
   granularity (the element encodings themselves are pinned against library casts).
 """
 from . import compress, quant, indexer, attention, pipeline  # noqa: F401

@@ -23,8 +23,8 @@ def prepare_query(q: np.ndarray, t: int, rope_dim: int, norm_w=None, eps=1e-6, r
 def window_positions(t: int, window: int):
     """Positions seen raw through the sliding window: max(0, t-W+1) .. t (always contains t).
 
-    [RABBIT] sliding-window paragraph: the most recent 128 tokens keep separate representations,
-    so tokens of an unfinished group are visible at once.
+    [RABBIT] sliding-window paragraph: the newest 128 tokens are also kept as their own rows, so
+    a token whose group is not yet complete can still be seen right away.
     """
     return list(range(max(0, t - window + 1), t + 1))
 
@@ -33,7 +33,7 @@ def mqa(q_hat: np.ndarray, X: np.ndarray, scale: float):
     """Softmax attention of every query head over the same rows X (shared KV: K = V = X).
 
     [SUMMARY] section 2.3, "Shared KV and output projection": shared-KV multi-query attention.
-    [EXPLAINER] HCA walk-through: the same vanilla multi-query attention math.
+    [EXPLAINER] HCA walk-through: HCA uses ordinary multi-query attention arithmetic.
     Reading: K and V are the same prepared row; logits are <q_h, x> * scale; one softmax per head
     over all rows (max-subtracted); lse is the natural-log normaliser.
     Returns (o [H, D], lse [H]).
@@ -50,8 +50,8 @@ def mqa(q_hat: np.ndarray, X: np.ndarray, scale: float):
 def gather_rows(entries, sel, win_rows, win_pos0: int, t: int, window: int):
     """X(t) = selected compressed entries followed by the window rows (one joint softmax).
 
-    [EXPLAINER] CSA walk-through: each query head attends to the picked set plus a sliding window
-    of the most recent tokens.  Reading: one joint softmax over the union (equivalently two
+    [EXPLAINER] CSA walk-through: every query head's attention covers the selected entries
+    together with a window of the newest tokens.  Reading: one joint softmax over the union (equivalently two
     branches merged by their log-sum-exp); a token may be seen both raw and inside an entry.
     """
     sel = [int(i) for i in sel if i >= 0]
@@ -77,8 +77,8 @@ def hca_attend(q, entries, n_visible, win_rows, win_pos0, t, window, rope_dim, s
                q_norm_w=None, eps=1e-6, rope_base=10000.0):
     """HCA core attention: dense over every visible compressed entry plus the window.
 
-    [EXPLAINER] HCA walk-through: every query attends to all compressed entries, plus a small
-    sliding window of recent uncompressed tokens.
+    [EXPLAINER] HCA walk-through: no selection step -- each query sees every compressed entry,
+    together with a short window of the newest raw tokens.
     """
     return csa_attend(q, entries, list(range(n_visible)), win_rows, win_pos0, t, window, rope_dim,
                       scale, q_norm_w, eps, rope_base)

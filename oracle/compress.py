@@ -11,8 +11,8 @@ def entry_tokens(i: int, m: int, overlap: int):
     """Token positions pooled into compressed entry ``i`` and the bias slot of each.
 
     [EXPLAINER] CSA walk-through: every m = 4 raw tokens become one compressed entry.
-    [RABBIT] CSA paragraph: each entry also draws on the previous group of four tokens.
-    [EXPLAINER] HCA walk-through: non-overlapping windows of m' = 128 tokens.
+    [RABBIT] CSA paragraph: an entry's pooling also covers the four tokens of the group before it.
+    [EXPLAINER] HCA walk-through: HCA pools disjoint runs of m' = 128 tokens.
 
     Reading: with overlap the entry spans its own group [i*m, (i+1)*m) and the previous group
     [(i-1)*m, i*m); bias slots 0..m-1 belong to the previous group and m..2m-1 to the own group,
@@ -33,10 +33,10 @@ def pool_entry(c: np.ndarray, z: np.ndarray, bias: np.ndarray, i: int, m: int, o
                pos_first: int = 0):
     """Softmax-weighted pooling of one entry, channel by channel.
 
-    [EXPLAINER] CSA walk-through: "a learned softmax weighting" over the group's tokens.
-    [DEVTO] "Two Compression Strategies": consecutive tokens are merged "using softmax-weighted
-    pooling".  [RABBIT] HCA paragraph: weighted averages, with different weights for different
-    parts of the representation (so the softmax is taken per channel).
+    [EXPLAINER] CSA walk-through: the group's tokens are combined with learned softmax weights.
+    [DEVTO] "Two Compression Strategies": runs of consecutive tokens are merged by pooling with
+    softmax weights.  [RABBIT] HCA paragraph: the averages are weighted, and the weights change
+    from one channel of the representation to another (so the softmax is taken per channel).
 
     Reading: the weight logit of token t in channel j is z[t, j] + bias[slot(t), j].
 
@@ -57,8 +57,8 @@ def pool_entry(c: np.ndarray, z: np.ndarray, bias: np.ndarray, i: int, m: int, o
 def rms_norm(x: np.ndarray, weight: np.ndarray | None = None, eps: float = 1e-6) -> np.ndarray:
     """RMSNorm over the last axis.
 
-    [SUMMARY] section 2.3, "Other details": RMSNorm is applied to the query heads and to the
-    compressed KV entries right before core attention.  [DEVTO]: query and KV normalisation.
+    [SUMMARY] section 2.3, "Other details": both the query heads and the compressed KV entries
+    are RMS-normalised just before core attention.  [DEVTO]: query and KV normalisation.
     Reading: eps = 1e-6; weight defaults to ones (no trained weights exist here).
     """
     x = x.astype(np.float64)
@@ -123,8 +123,8 @@ def compress(c, z, bias, m, overlap, rope_dim, norm_w=None, eps=1e-6, rope_base=
 def window_rows(c, rope_dim, norm_w=None, eps=1e-6, rope_base=10000.0, pos_first=0):
     """Per-token rows for the sliding window: RMSNorm then RoPE at the token's own position.
 
-    [RABBIT] sliding-window paragraph: a window keeps separate representations of the most
-    recent 128 tokens.  Reading: these rows get the same normalisation and rotation as the
+    [RABBIT] sliding-window paragraph: the newest 128 tokens are also kept uncompressed, each as
+    its own row.  Reading: these rows get the same normalisation and rotation as the
     compressed entries, so every key in the joint softmax sits on one scale.
     """
     pos = pos_first + np.arange(c.shape[0])

@@ -12,8 +12,8 @@ from . import quant
 def visible_count(t: int, n_entries: int, m: int) -> int:
     """Number of compressed entries a query at position ``t`` may use.
 
-    [EXPLAINER] CSA walk-through: "compress then cherry-pick" -- only existing entries can be
-    scored.  Reading: entry i becomes usable once its last token exists, (i+1)*m - 1 <= t, so the
+    [EXPLAINER] CSA walk-through: compression comes first and selection second, so only entries
+    that already exist can be scored.  Reading: entry i becomes usable once its last token exists, (i+1)*m - 1 <= t, so the
     visible set is the prefix [0, min(n_entries, (t+1) // m)).
     """
     return int(min(n_entries, (t + 1) // m))
@@ -50,9 +50,9 @@ def compress_keys(c_i, z_i, bias_i, m: int, overlap: int, pos_first: int = 0):
     """Indexer keys of the compressed entries, produced by compression of a per-token stream.
 
     [EXPLAINER] CSA walk-through: the lightning indexer scores compressed blocks, so each entry
-    carries its own indexer key; the compressor makes every entry from its group of tokens by a
-    learned softmax weighting.  [RABBIT] indexer paragraph: the indexer works on smaller
-    representations (a narrower key than the attention rows).
+    carries its own indexer key; the compressor pools every entry from its group of tokens with
+    learned softmax weights.  [RABBIT] indexer paragraph: the indexer's operands are compact (a
+    narrower key than the attention rows).
 
     Reading: a per-token indexer stream c_i [T, D_I] with logits z_i and position bias bias_i
     [(1+overlap) m, D_I] is pooled exactly as the KV compressor pools (same token groups, same
@@ -77,9 +77,9 @@ def dequantize_keys(codes, scales, fmt: str) -> np.ndarray:
 def index_scores(q_tilde: np.ndarray, w: np.ndarray, k_tilde: np.ndarray, n_visible: int) -> np.ndarray:
     """Relevance of every visible compressed entry to one query token.
 
-    [EXPLAINER] CSA walk-through: the lightning indexer is a small attention head that scores
-    every compressed block against the current query.  [RABBIT] indexer paragraph: it checks
-    every compressed entry, so its work grows with the context.
+    [EXPLAINER] CSA walk-through: the lightning indexer is a lightweight scoring head that rates
+    each compressed block for the present query.  [RABBIT] indexer paragraph: it visits all
+    compressed entries, so its cost rises with the context length.
 
     Reading (parity unpinned by the pages): s[i] = sum_h w[h] * max(0, <q_h, k_i>) over the
     indexer heads h, the lightning-indexer form of the predecessor's sparse attention that the

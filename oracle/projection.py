@@ -11,8 +11,8 @@ def grouped_output_projection(o: np.ndarray, w: np.ndarray) -> np.ndarray:
     """Hidden state from the core-attention head outputs through a grouped projection.
 
     [SUMMARY] 2.3 "Hybrid Attention with CSA and HCA", shared-KV and output-projection paragraph:
-    both attention kinds use a grouped output projection, which makes projecting the many head
-    outputs back to the hidden state cheaper.
+    both attention types map their many head outputs back to the model width through a
+    projection split into groups, to cut that cost.
 
     Reading: the heads are split into G equal groups in head order; group g's head outputs,
     concatenated in head order, are projected by its own weight w[g] (out_features x

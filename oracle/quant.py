@@ -1,8 +1,8 @@
 """Oracle step 2a: low-precision encodings used by the lightning indexer.
 
 [DEVTO] "Two Compression Strategies": the lightning indexer runs in FP4 precision.
-[RABBIT] lightning-indexer paragraph: the first pass is cheap because it uses smaller
-representations and lower-precision numbers.
+[RABBIT] lightning-indexer paragraph: compact, low-precision operands are what keep the
+indexer's first pass cheap.
 
 Two encodings are provided: fp8 e4m3 (OCP "E4M3FN": bias 7, no infinities, 448 largest finite)
 with one power-of-two scale per row, and MXFP4 (OCP Microscaling v1.0: e2m1 elements with one
