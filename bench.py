@@ -1,7 +1,8 @@
 """Benchmark: CSA decode query-tokens/s at 1M and 128K context on one MI355X, with the roofline of
 the dominant kernel and the CPU oracle timed beside it.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs main,d128,c32k,hca,prefill,compress]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--legs main,d128,c32k,hca,flash,append,prefill,compress,oproj]
                     [--mode bench|copy|summarize-trace|summarize-traffic]
 
 One step = one decode pass of the whole hot path over one batch: csa_index_topk (lightning-indexer
@@ -9,7 +10,8 @@ scores + top-k) then csa_attend (shared-KV attention over the selected entries +
 hca_attend for HCA.  Inputs are seeded synthetic tensors resident in HBM before timing.  Every
 step reads one of several copies of the caches, enough copies that the working set exceeds the
 256 MB Infinity Cache by 4x, so each step streams from HBM.  The steps are replayed from a HIP
-graph (launch overhead would otherwise exceed the ~15 us step).  Prints one JSON line.
+graph (host launch overhead would otherwise be a large part of the ~50 us step).  Prints one JSON
+line.
 """
 from __future__ import annotations
 
