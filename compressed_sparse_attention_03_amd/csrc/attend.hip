@@ -185,13 +185,12 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
   const int hb = tl.hb;
   const int64_t qi = tl.qi;
   const int b = int(uint32_t(qi) / uint32_t(a.Sq)), s_idx = int(qi) - b * a.Sq;   // B * Sq < 2^16
-  const int64_t t = a.q_pos0[b] + s_idx;
-  const int64_t n_vis = a.topk_idx ? 0 : min(a.n_entries[b], div_count(t + 1, a.m));
   const int split_first = FUSED ? 0 : tl.split;
   const int split_end = FUSED ? a.plan.n_splits : tl.split + 1;
 
-  // ---- prologue.  The raw q chunk (and norm weights) of this thread are loaded first: loads
-  // complete in issue order, so anything issued later (the row prefetch) does not delay them.
+  // ---- prologue.  The raw q chunk (and norm weights) of this thread are loaded first -- before
+  // the query's position is read, whose round trip they do not need -- and loads complete in
+  // issue order, so anything issued later (the row prefetch) does not delay them.
   const bool qthread = tid < 16 * QCH;
   const int qh = tid / QCH, qc = tid % QCH;
   const int qhead = hb * 16 + qh;
@@ -204,6 +203,9 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
 #pragma unroll
     for (int k = 0; k < 4; ++k) { qraw[k] = src[k]; wraw[k] = wsrc[k]; }
   }
+  __builtin_amdgcn_sched_barrier(0);             // keep the q loads ahead of the position wait
+  const int64_t t = a.q_pos0[b] + s_idx;
+  const int64_t n_vis = a.topk_idx ? 0 : min(a.n_entries[b], div_count(t + 1, a.m));
   const int npairs = a.rope_dim / 2;
   const double rate = rope_rate(a.rope_dim, a.log2_base);
   for (int u = tid; u < npairs; u += NT) rope_cos_sin(t, u, rate, &s_cs[u], &s_sn[u]);

@@ -911,9 +911,6 @@ __global__ void __launch_bounds__(kMergeThreads) index_merge_kernel(IndexArgs a)
   const int64_t qi = blockIdx.x;
   const int b = int(blockIdx.x / uint32_t(a.Sq)), s = int(blockIdx.x) - b * a.Sq;
   const int cand = a.plan.cand, n_tiles = a.plan.n_tiles;
-  const int64_t t = a.q_pos0[b] + s;
-  const int64_t n_vis = min(a.n_entries[b], div_count(t + 1, a.m));
-  const int k_eff = int(min(int64_t(a.topk), n_vis));
   const int64_t n_q = int64_t(a.B) * a.Sq;
   const uint64_t *cand_keys = static_cast<const uint64_t *>(a.workspace);
   const uint64_t *cand_bound = cand_keys + n_q * n_tiles * cand;
@@ -938,9 +935,27 @@ __global__ void __launch_bounds__(kMergeThreads) index_merge_kernel(IndexArgs a)
       keys[k] = slot < slots ? cand_keys[qi * slots + slot] : 0;
     }
   }
-  for (int i = tid; i < n_tiles; i += NT) {
-    sh.counts[i] = cand_count[qi * n_tiles + i];
-    sh.bounds[i] = cand_bound[qi * n_tiles + i];
+  // per-tile counts and bounds (n_tiles <= 2 NT), held in registers until the position is known
+  static_assert(kMaxCand / 8 <= 2 * NT, "two tiles' counts per thread");
+  // (loaded unconditionally from a clamped slot, so no branch separates the loads from the ones above)
+  int cnt[2];
+  uint64_t bnd[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = min(tid + j * NT, n_tiles - 1);
+    cnt[j] = cand_count[qi * n_tiles + i];
+    bnd[j] = cand_bound[qi * n_tiles + i];
+  }
+  // the query's position is read only now, while the candidate loads are in flight
+  __builtin_amdgcn_sched_barrier(0);
+  const int64_t t = a.q_pos0[b] + s;
+  const int64_t n_vis = min(a.n_entries[b], div_count(t + 1, a.m));
+  const int k_eff = int(min(int64_t(a.topk), n_vis));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid + j * NT;
+    if (i < n_tiles) { sh.counts[i] = cnt[j]; sh.bounds[i] = bnd[j]; }
   }
   if (tid == 0) sh.flag = 0;
   lds_barrier();
