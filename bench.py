@@ -536,13 +536,40 @@ def summarize_traffic(fetch_db: str, write_db: str, copy_fetch_db: str, copy_wri
         f"traffic_bytes_per_dispatch = {traffic:.0f}"])
 
 
+MFMA_COUNTERS = ("MfmaUtil", "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_F6F4",
+                 "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+
+
+def summarize_mfma(db: str, kernels) -> str:
+    """Per-kernel MFMA evidence from one `rocprofv3 --pmc` run of MFMA_COUNTERS: MfmaUtil (percent of
+    SIMD cycles the matrix unit is busy while the GPU is active) and the MFMA operations counted per
+    data type (the counters count add and multiply operations in units of 512), per dispatch."""
+    import sqlite3
+    cur = sqlite3.connect(db).cursor()
+    out = ["| kernel | dispatches | MfmaUtil % | fp8 GFLOP | fp6/fp4 GFLOP | bf16 GFLOP |", "|---|---|---|---|---|---|"]
+    for k in kernels:
+        vals = {}
+        n = 0
+        for c in MFMA_COUNTERS:
+            r = cur.execute("select avg(v), count(*) from (select sum(counter_value) as v from pmc_events where "
+                            "counter_name = ? and name like ? group by dispatch_id)", (c, f"%{k}%")).fetchone()
+            vals[c] = r[0] if r and r[1] else None
+            n = max(n, r[1] if r else 0)
+        g = lambda c: "-" if vals[c] is None else f"{vals[c] * 512 / 1e9:.1f}"
+        u = "-" if vals["MfmaUtil"] is None else f"{vals['MfmaUtil']:.1f}"
+        out.append(f"| {k} | {n} | {u} | {g('SQ_INSTS_VALU_MFMA_MOPS_F8')} | {g('SQ_INSTS_VALU_MFMA_MOPS_F6F4')} | "
+                   f"{g('SQ_INSTS_VALU_MFMA_MOPS_BF16')} |")
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--legs", default="main,d128,c32k,hca,flash,append,prefill,compress,oproj")
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "summarize-trace", "summarize-traffic"])
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "summarize-trace", "summarize-traffic",
+                                                        "summarize-mfma"])
     ap.add_argument("--db", nargs="*", default=[], help="rocprofv3 databases for the summarize modes: one "
                     "kernel-trace db; or FETCH, WRITE, copy-FETCH, copy-WRITE dbs")
     ap.add_argument("--kernel", default="index_score_kernel")
@@ -558,6 +585,9 @@ def main():
         return
     if args.mode == "summarize-trace":
         print(summarize_trace(args.db[0]))
+        return
+    if args.mode == "summarize-mfma":
+        print(summarize_mfma(args.db[0], args.kernel.split(",")))
         return
     if args.mode == "summarize-traffic":
         print(summarize_traffic(*args.db[:4], kernel=args.kernel, source=args.source))
