@@ -1,6 +1,6 @@
 """bench.py's host side, on the CPU: a request for more than one GPU exits with a message; the
 algorithmic byte counts are the sums of what one step must touch; the committed traffic summary is
-used only while it matches the kernel source; the trace summariser reads a rocprofv3 kernel table."""
+used only while it matches the kernel source; the trace and MFMA summarisers read rocprofv3 tables."""
 import os
 import shutil
 import sqlite3
@@ -72,3 +72,19 @@ def test_summarize_trace_reads_a_kernel_table(tmp_path):
     out = bench.summarize_trace(str(db)).splitlines()
     assert out[2] == "| k<1> | 64x1 | 64 | 3 | 2.00 | 1.00 | 3.00 |"
     assert len(out) == 3
+
+
+def test_summarize_mfma_sums_shader_engines_per_dispatch(tmp_path):
+    db = tmp_path / "pmc.db"
+    con = sqlite3.connect(db)
+    con.execute("create table pmc_events (name text, dispatch_id int, counter_name text, counter_value real)")
+    rows = []
+    for d in (1, 2):                                    # two dispatches, 32 shader-engine rows each
+        rows.append(("k<1>", d, "MfmaUtil", 20.0 + d))
+        rows += [("k<1>", d, "SQ_INSTS_VALU_MFMA_MOPS_F8", 1e6 / 32) for _ in range(32)]
+        rows += [("k<1>", d, c, 0.0) for c in ("SQ_INSTS_VALU_MFMA_MOPS_F6F4", "SQ_INSTS_VALU_MFMA_MOPS_BF16")]
+    con.executemany("insert into pmc_events values (?, ?, ?, ?)", rows)
+    con.commit()
+    con.close()
+    out = bench.summarize_mfma(str(db), ["k<1>"]).splitlines()
+    assert out[2] == "| k<1> | 2 | 21.5 | 0.5 | 0.0 | 0.0 |"      # 1e6 x 512 ops = 0.512 GFLOP
