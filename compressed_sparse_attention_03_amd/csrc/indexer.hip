@@ -653,6 +653,34 @@ struct alignas(16) MultiShared {
   uint32_t hist[kMultiQ][256];            // each wave's select histogram
 };
 
+// Workspace of the shared-tile path: after the candidate slots, bounds and counts (as in the
+// one-query path), every query's quantised query (a QueryLds image), 16-byte aligned.
+__host__ __device__ inline size_t prepared_query_offset(int64_t n_q, const IndexPlan &p) {
+  const int64_t slots = n_q * p.n_tiles;
+  const size_t off = size_t(slots * p.cand * 8 + slots * 8 + slots * 4);
+  return (off + 255) / 256 * 256;
+}
+
+// Shared-tile path, step 0: every query quantised once (the same encoders, so the same bytes, as
+// the one-query kernel's) into the workspace; the tile workgroups then copy it instead of
+// re-quantising the query for each of their tiles.
+template <int FMT>
+__global__ void __launch_bounds__(256) index_query_prep_kernel(IndexArgs a) {
+  __shared__ QueryLds ql;
+  const int64_t qi = blockIdx.x;
+  const int t = threadIdx.x;
+  QueryRaw raw;
+  load_query_raw(static_cast<const uint16_t *>(a.q_idx) + qi * a.H_I * 128, a.w_idx + qi * a.H_I, a.H_I, raw, t);
+  prep_query_slot<FMT>(raw, t, a.H_I, ql);
+  lds_barrier();
+  constexpr int W = int(sizeof(QueryLds) / 16);
+  const int64_t n_q = int64_t(a.B) * a.Sq;
+  uint4 *dst = reinterpret_cast<uint4 *>(static_cast<uint8_t *>(a.workspace) + prepared_query_offset(n_q, a.plan)) +
+               qi * W;
+  const uint4 *src = reinterpret_cast<const uint4 *>(&ql);
+  for (int i = t; i < W; i += 256) dst[i] = src[i];
+}
+
 template <int FMT, int NHB>
 __global__ void __launch_bounds__(64 * kMultiQ, 2) index_score_multi_kernel(IndexArgs a) {
   __shared__ MultiShared sh;
@@ -681,20 +709,18 @@ __global__ void __launch_bounds__(64 * kMultiQ, 2) index_score_multi_kernel(Inde
       v[l] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, uint32_t((l * NT + tid) * 16), 0, 0));
     sc = __builtin_amdgcn_raw_buffer_load_b32(rs, uint32_t(tid * 4), 0, 0);
   }
-  // this wave's query, quantised into its LDS slot four (head, quarter) slots per lane at a time
-  // (the encoders of the one-query kernel), then read back as MFMA operands
+  // this wave's query, already quantised by index_query_prep_kernel, copied into its LDS slot,
+  // then read back as MFMA operands
   const int s = s0 + wave;
   const bool live = s < a.Sq;
   const int64_t qi = int64_t(b) * a.Sq + (live ? s : a.Sq - 1);
   {
-    const uint16_t *qsrc = static_cast<const uint16_t *>(a.q_idx) + qi * a.H_I * 128;
-    const float *wsrc = a.w_idx + qi * a.H_I;
-#pragma unroll 1
-    for (int it = 0; it < 4; ++it) {
-      QueryRaw raw;
-      load_query_raw(qsrc, wsrc, a.H_I, raw, it * 64 + lane);
-      prep_query_slot<FMT>(raw, it * 64 + lane, a.H_I, sh.q[wave]);
-    }
+    constexpr int W = int(sizeof(QueryLds) / 16);
+    const int64_t n_q = int64_t(a.B) * a.Sq;
+    const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(a.workspace) +
+                                                       prepared_query_offset(n_q, a.plan)) + qi * W;
+    uint4 *dst = reinterpret_cast<uint4 *>(&sh.q[wave]);
+    for (int i = lane; i < W; i += 64) dst[i] = src[i];
   }
   wave_lds_sync();
   QueryFrag<NHB> qf;
@@ -998,6 +1024,9 @@ template <int FMT, int NHB>
 hipError_t launch_score_t(const IndexArgs &a, hipStream_t stream) {
   hipError_t e = hipSuccess;
   if (a.plan.multi) {
+    e = launch("index_query_prep", index_query_prep_kernel<FMT>, dim3(unsigned(int64_t(a.B) * a.Sq)), dim3(256),
+               stream, a);
+    if (e != hipSuccess) return e;
     const dim3 mgrid(unsigned(a.plan.n_tiles), unsigned((a.Sq + kMultiQ - 1) / kMultiQ), unsigned(a.B));
     return launch("index_score", index_score_multi_kernel<FMT, NHB>, mgrid, dim3(64 * kMultiQ), stream, a);
   }
@@ -1058,6 +1087,7 @@ IndexPlan plan_index(int64_t B, int64_t Sq, int64_t N_cap, int topk, int format)
 size_t index_workspace_bytes(int64_t B, int64_t Sq, int64_t N_cap, int topk, int format) {
   IndexPlan p = plan_index(B, Sq, N_cap, topk, format);
   const int64_t slots = B * Sq * p.n_tiles;
+  if (p.multi) return prepared_query_offset(B * Sq, p) + size_t(B * Sq) * sizeof(QueryLds) + 256;
   return size_t(slots * p.cand * 8 + slots * 8 + slots * 4 + 256);
 }
 

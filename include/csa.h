@@ -288,7 +288,7 @@ const char *csa_last_error(void);
  * later launch record a pair of HIP events on its stream; csa_timing_enable(0) stops recording.
  * csa_timing_read() waits for the recorded events and returns the summed duration (ms) and the
  * launch count for one kernel name: "compress", "compress_keys", "quantize", "decode_append",
- * "decode_append_keys", "index_score", "index_merge", "attend_split", "attend_combine", "oproj",
+ * "decode_append_keys", "index_query_prep", "index_score", "index_merge", "attend_split", "attend_combine", "oproj",
  * "stream_read".  Not for use while a stream is being captured into a graph.
  */
 void csa_timing_enable(int on);
