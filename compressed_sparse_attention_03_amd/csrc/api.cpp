@@ -288,12 +288,28 @@ csa_status csa_quantize_keys(const uint16_t *x, int64_t rows, int dim, int forma
   return launched(e, "quantize launch");
 }
 
+csa_status csa_quantize_query(const uint16_t *q_idx, const float *w_idx, int64_t n, int H_I, int key_format,
+                              void *codes, void *scale_bytes, float *factors, void *stream) {
+  REQUIRE(key_format == CSA_KEY_FP8_E4M3 || key_format == CSA_KEY_MXFP4,
+          "key_format must be CSA_KEY_FP8_E4M3 or CSA_KEY_MXFP4");
+  REQUIRE(H_I == 16 || H_I == 32 || H_I == 48 || H_I == 64, "H_I must be one of 16, 32, 48, 64");
+  REQUIRE(n >= 0 && n <= 65535, "n must be in [0, 65535]");
+  if (n == 0) return CSA_OK;
+  REQUIRE_PTR(q_idx); REQUIRE_PTR(w_idx); REQUIRE_PTR(codes); REQUIRE_PTR(factors);
+  if (key_format == CSA_KEY_MXFP4) REQUIRE_PTR(scale_bytes);
+  hipError_t e = csa::launch_query_codes(q_idx, w_idx, n, H_I, key_format, codes, scale_bytes, factors,
+                                         static_cast<hipStream_t>(stream));
+  return launched(e, "quantize_query launch");
+}
+
 size_t csa_index_topk_workspace_bytes(int B, int Sq, int64_t N_cap, int topk) {
   if (B <= 0 || Sq <= 0 || N_cap <= 0 || topk <= 0) return 256;
-  // the larger of the two plans (tiles shared by several queries, or one query per workgroup):
-  // the plan depends on the key format and on whether full scores are asked for
-  return std::max(csa::index_workspace_bytes(B, Sq, N_cap, topk, CSA_KEY_F32),
-                  csa::index_workspace_bytes(B, Sq, N_cap, topk, CSA_KEY_FP8_E4M3));
+  // the largest of the plans (tiles shared by several queries, one query per segment or per
+  // tile): the plan depends on the key format and on whether full scores are asked for
+  size_t n = csa::index_workspace_bytes(B, Sq, N_cap, topk, CSA_KEY_F32, false);
+  for (int f : {CSA_KEY_FP8_E4M3, CSA_KEY_MXFP4})
+    for (bool shared : {true, false}) n = std::max(n, csa::index_workspace_bytes(B, Sq, N_cap, topk, f, shared));
+  return n;
 }
 
 csa_status csa_index_topk(const void *q_idx, const float *w_idx, const void *k_codes,
@@ -321,9 +337,9 @@ csa_status csa_index_topk(const void *q_idx, const float *w_idx, const void *k_c
   REQUIRE_PTR(q_pos0); REQUIRE_PTR(topk_idx);
   if (key_format != CSA_KEY_F32) REQUIRE_PTR(k_scales);
   REQUIRE_PTR_OR_NULL(scores);
-  // full scores are written by the one-query-per-workgroup kernel only
-  const int plan_format = scores ? CSA_KEY_F32 : key_format;
-  const size_t need = csa::index_workspace_bytes(B, Sq, N_cap, topk, plan_format);
+  // full scores are written by the one-query-per-workgroup kernels only (no shared tiles)
+  const bool shared = scores == nullptr;
+  const size_t need = csa::index_workspace_bytes(B, Sq, N_cap, topk, key_format, shared);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(CSA_ERR_WORKSPACE, "index_topk needs %zu workspace bytes, got %zu", need, workspace_bytes);
   REQUIRE_PTR(workspace);
@@ -332,12 +348,10 @@ csa_status csa_index_topk(const void *q_idx, const float *w_idx, const void *k_c
   a.n_entries = n_entries; a.q_pos0 = q_pos0; a.topk_idx = topk_idx; a.scores = scores;
   a.workspace = workspace; a.format = key_format; a.B = B; a.Sq = Sq; a.H_I = H_I; a.D_I = D_I;
   a.m = m; a.topk = topk; a.N_cap = N_cap;
-  a.plan = csa::plan_index(B, Sq, N_cap, topk, plan_format);
+  a.plan = csa::plan_index(B, Sq, N_cap, topk, key_format, shared);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = csa::launch_index_score(a, st);
-  if (e != hipSuccess) return launched(e, "index_score launch");
-  e = csa::launch_index_merge(a, st);
-  return launched(e, "index_merge launch");
+  return launched(e, "index_topk launch");
 }
 
 static csa_status check_attend_common(const uint16_t *q, const uint16_t *q_norm_w, const uint16_t *entries,
@@ -369,9 +383,7 @@ static csa_status run_attend(csa::AttendArgs &a, void *stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = csa::launch_attend(a, st);
   if (e != hipSuccess) return launched(e, "attend launch");
-  if (a.plan.n_splits > 1 && !a.plan.fused) {
-      e = csa::launch_combine(a, st);
-  }
+  if (a.plan.n_splits > 1 && !a.plan.fused) e = csa::launch_combine(a, st);
   return launched(e, "combine launch");
 }
 

@@ -19,6 +19,68 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// ---- hand-over between the workgroups of one launch -------------------------------------------
+// Several kernels let the last of a group of workgroups to finish (decided by a device-scope atomic
+// counter) combine what the others produced.  The handed-over values are written and read with the
+// coherent cache policy (sc1) -- the policy of device-scope atomic stores and loads, which keeps
+// them at the device's coherence point rather than in one XCD's L2 -- so no L2 write-back or
+// invalidation is needed: a writer waits until its coherent stores have completed and only then
+// counts itself in; the last workgroup reads them back coherently after the count.  (A device-scope
+// release fence would write back the whole L2 of the XCD, which costs microseconds when every
+// workgroup of a launch does it.)  Counters sit on separate 256-byte lines so that arrivals for
+// different groups do not queue behind each other.
+constexpr int kCoherent = 16;                         // buffer cache-policy operand: sc1
+constexpr int kCounterStride = 64;                    // ints between two arrival counters
+constexpr int kRawBufferDesc3 = 0x00020000;           // raw-buffer descriptor word 3 (32-bit format)
+
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+__device__ __forceinline__ void store_coherent(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(int *p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_coherent(const uint64_t *p) {
+  return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int load_coherent(const int *p) {
+  return __hip_atomic_load(const_cast<int *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16-byte coherent accesses through a buffer resource over [base, base + bytes) (base uniform).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_region(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), short(0), int(bytes), kRawBufferDesc3);
+}
+__device__ __forceinline__ uint4 load_coherent16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
+}
+__device__ __forceinline__ void store_coherent16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
+                                         off, 0, kCoherent);
+}
+
+// Count the calling workgroup in on `counter` after every wave's coherent stores have completed.
+// Returns true (in every thread) for the workgroup that arrives last, which also resets the counter
+// to zero for the next launch.  `flag` is an LDS int.  No workgroup waits for another.
+__device__ __forceinline__ bool arrive_last(int *counter, int group_size, int *flag) {
+  wait_stores();
+  lds_barrier();
+  if (threadIdx.x == 0) {
+    const int before = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = before == group_size - 1;
+    if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  lds_barrier();
+  return *flag != 0;
+}
+
 // ---- bf16 storage ---------------------------------------------------------------------------
 // Entries visible at position x - 1, i.e. x / m for a token count x >= 0 (C division): 32-bit
 // unsigned division whenever x fits, which is every real position (a 64-bit division by a runtime

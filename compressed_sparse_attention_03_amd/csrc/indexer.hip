@@ -33,9 +33,8 @@ constexpr int kMaxCand = 8192;        // candidates per query seen by the merge 
 constexpr int kMergeThreads = 512;
 constexpr int kMaxTile = 2048;
 constexpr int kMaxK = 2048;
-// groups of 16 entries per wave per load batch: 4 KB of keys in flight per wave and batch
-template <int FMT>
-constexpr int batch_of() { return FMT == 1 ? 2 : 4; }
+constexpr int kFusedKeys = 8;                     // candidate slots per thread of a merging tile workgroup
+constexpr int kFusedSlots = 512 * kFusedKeys;
 
 // Cross-lane moves use DPP (a VALU operand modifier: no LDS round trip) inside rows of 16 lanes and
 // v_readlane for the four row results, so a scan or reduction is a short VALU chain.
@@ -97,57 +96,60 @@ __device__ __forceinline__ void load_query_raw(const uint16_t *q, const float *w
 // 32*(t%4) .. +31; heads >= H_I are written as zeros (factor 0) so 4 head blocks are always valid.
 // Slot t (< 256) of the quantised query: head t/4, values 32*(t%4) .. +31; the 4 slots of a head
 // are 4 consecutive lanes (the head's maximum is reduced over them).
+// The e4m3 / e2m1 codes are produced by the gfx950 conversion instructions (v_cvt_pk_fp8_f32,
+// v_cvt_scalef32_pk_fp4_f32 with unit scale) from values already divided by the power-of-two
+// scale (an exact division).  In the range those scales produce (|x| <= 448 for e4m3, |x| < 8 for
+// e2m1) their rounding -- nearest, ties to the even code, saturating -- is that of f32_to_e4m3 /
+// f32_to_e2m1 (the encoders csa_quantize_keys uses) for every bf16 input, and the GPU tests hold
+// the resulting codes to the oracle's bit for bit.
 template <int FMT>
 __device__ __forceinline__ void prep_query_slot(const QueryRaw &raw, int t, int H_I, QueryLds &ql) {
-  {
-    const bool act = t < 4 * H_I;
-    const int h = t >> 2, c = t & 3;
-    uint32_t wv[16];
+  const bool act = t < 4 * H_I;
+  const int h = t >> 2, c = t & 3;
+  uint32_t wv[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) wv[k] = act ? raw.wv[k] : 0u;
-    const float wh = raw.w;
-    float amax = 0.f;
+  for (int k = 0; k < 16; ++k) wv[k] = act ? raw.wv[k] : 0u;
+  const float wh = raw.w;
+  float amax = 0.f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fmaxf(fabsf(bf16lo(wv[k])), fabsf(bf16hi(wv[k]))));
-    if (FMT == 1) {
-      amax = fmaxf(amax, __int_as_float(dpp<kDppQuadXor1>(__float_as_int(amax))));
-      amax = fmaxf(amax, __int_as_float(dpp<kDppQuadXor2>(__float_as_int(amax))));
-      const int e = e4m3_row_exp(amax);
-      const float inv = ldexpf(1.0f, -e);
-      uint32_t outw[8];
+  for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fmaxf(fabsf(bf16lo(wv[k])), fabsf(bf16hi(wv[k]))));
+  if (FMT == 1) {
+    amax = fmaxf(amax, __int_as_float(dpp<kDppQuadXor1>(__float_as_int(amax))));
+    amax = fmaxf(amax, __int_as_float(dpp<kDppQuadXor2>(__float_as_int(amax))));
+    const int e = e4m3_row_exp(amax);
+    const float inv = ldexpf(1.0f, -e);
+    uint32_t outw[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        uint32_t b0 = f32_to_e4m3(bf16lo(wv[2 * k]) * inv), b1 = f32_to_e4m3(bf16hi(wv[2 * k]) * inv);
-        uint32_t b2 = f32_to_e4m3(bf16lo(wv[2 * k + 1]) * inv), b3 = f32_to_e4m3(bf16hi(wv[2 * k + 1]) * inv);
-        outw[k] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-      }
-      uint4 *dst = reinterpret_cast<uint4 *>(ql.codes + h * 128 + c * 32);
-      dst[0] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
-      dst[1] = make_uint4(outw[4], outw[5], outw[6], outw[7]);
-      if (c == 0) ql.f[h] = act ? wh * ldexpf(1.0f, e) : 0.f;
-    } else {
-      const uint32_t sb = mx_scale_byte(amax);
-      const float inv = ldexpf(1.0f, 127 - int(sb));
-      uint32_t outw[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint32_t p = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t lo = f32_to_e2m1(bf16lo(wv[4 * k + j]) * inv), hi = f32_to_e2m1(bf16hi(wv[4 * k + j]) * inv);
-          p |= (lo | (hi << 4)) << (8 * j);
-        }
-        outw[k] = p;
-      }
-      *reinterpret_cast<uint4 *>(ql.codes + h * 64 + c * 16) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
-      ql.sbytes[h * 4 + c] = uint8_t(sb);
-      if (c == 0) ql.f[h] = act ? wh : 0.f;
+    for (int k = 0; k < 8; ++k) {
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(bf16lo(wv[2 * k]) * inv, bf16hi(wv[2 * k]) * inv, 0, false);
+      outw[k] = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(bf16lo(wv[2 * k + 1]) * inv, bf16hi(wv[2 * k + 1]) * inv, lo,
+                                                         true));
     }
+    uint4 *dst = reinterpret_cast<uint4 *>(ql.codes + h * 128 + c * 32);
+    dst[0] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+    dst[1] = make_uint4(outw[4], outw[5], outw[6], outw[7]);
+    if (c == 0) ql.f[h] = act ? wh * ldexpf(1.0f, e) : 0.f;
+  } else {
+    const uint32_t sb = mx_scale_byte(amax);
+    const float inv = ldexpf(1.0f, 127 - int(sb));
+    uint32_t outw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t p = 0;
+      p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, bf16lo(wv[4 * k]) * inv, bf16hi(wv[4 * k]) * inv, 1.0f, 0);
+      p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, bf16lo(wv[4 * k + 1]) * inv, bf16hi(wv[4 * k + 1]) * inv, 1.0f, 1);
+      p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, bf16lo(wv[4 * k + 2]) * inv, bf16hi(wv[4 * k + 2]) * inv, 1.0f, 2);
+      p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, bf16lo(wv[4 * k + 3]) * inv, bf16hi(wv[4 * k + 3]) * inv, 1.0f, 3);
+      outw[k] = p;
+    }
+    *reinterpret_cast<uint4 *>(ql.codes + h * 64 + c * 16) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+    ql.sbytes[h * 4 + c] = uint8_t(sb);
+    if (c == 0) ql.f[h] = act ? wh : 0.f;
   }
 }
 
 template <int FMT>
-__device__ void prep_query_lds(const QueryRaw &raw, int H_I, QueryLds &ql) {
+__device__ __forceinline__ void prep_query_lds(const QueryRaw &raw, int H_I, QueryLds &ql) {
   if (threadIdx.x < 256) prep_query_slot<FMT>(raw, int(threadIdx.x), H_I, ql);
 }
 
@@ -193,7 +195,6 @@ struct KeyFrag {
 // per-lane offset operand, which the hardware range check always covers: rows past the tile's last
 // valid row, and whole groups past the tile, read as zeros without touching memory (their scores are
 // discarded), so loads are issued unconditionally and nothing is clamped.
-constexpr int kRawBufferWord3 = 0x00020000;   // gfx9 raw-buffer descriptor word 3 (32-bit data format)
 
 template <int FMT>
 struct TileKeys {
@@ -207,9 +208,9 @@ __device__ __forceinline__ TileKeys<FMT> make_tile_keys(const void *codes, const
   constexpr int RB = FMT == 1 ? 128 : 64;     // code bytes per row
   TileKeys<FMT> tk;
   tk.codes = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(static_cast<const uint8_t *>(codes) + row0 * RB), short(0), rows * RB, kRawBufferWord3);
+      const_cast<uint8_t *>(static_cast<const uint8_t *>(codes) + row0 * RB), short(0), rows * RB, kRawBufferDesc3);
   tk.scales = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(static_cast<const uint8_t *>(scales) + row0 * 4), short(0), rows * 4, kRawBufferWord3);
+      const_cast<uint8_t *>(static_cast<const uint8_t *>(scales) + row0 * 4), short(0), rows * 4, kRawBufferDesc3);
   tk.code_off = uint32_t((lane & 15) * RB + (lane >> 4) * (FMT == 1 ? 32 : 16));
   tk.scale_off = uint32_t((lane & 15) * 4);
   return tk;
@@ -225,84 +226,10 @@ __device__ __forceinline__ void load_key_frag(const TileKeys<FMT> &tk, int grp, 
   kf.s = __builtin_amdgcn_raw_buffer_load_b32(tk.scales, tk.scale_off + uint32_t(grp) * 64, 0, 0);
 }
 
-template <int FMT>
-__device__ __forceinline__ void load_batch(const TileKeys<FMT> &tk, int g0, int lane, KeyFrag<FMT> (&kf)[batch_of<FMT>()]) {
-#pragma unroll
-  for (int u = 0; u < batch_of<FMT>(); ++u) load_key_frag<FMT>(tk, g0 + u, lane, kf[u]);
-}
 
 // max(x, 0) for a float: non-negative floats order like their bit patterns as signed integers, and
 // every negative float (and -0) is a negative integer.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
-
-// Scores of one group of 16 entries: the NHB MFMAs of the group (query head blocks x the group's
-// keys), then the per-head ReLU/weight epilogue.  Each entry's score is reduced across its 4 lanes
-// and written to s_scores by lanes 0..15; entries at tile-local index >= vis get -inf.
-template <int FMT, int NHB>
-__device__ __forceinline__ void group_mfma(const QueryFrag<NHB> &qf, const KeyFrag<FMT> &kf, int lane, v4f (&c)[NHB]) {
-  constexpr int fmt = FMT == 1 ? 0 : 4;   // instruction format code: 0 = fp8 e4m3, 4 = fp4 e2m1
-  const uint4 x0 = kf.c0, x1 = FMT == 1 ? kf.c1 : make_uint4(0, 0, 0, 0);
-  const v8i bop = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
-  const int sb = FMT == 1 ? 127 : int((kf.s >> (8 * (lane >> 4))) & 0xff);
-#pragma unroll
-  for (int hb = 0; hb < NHB; ++hb)
-    c[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf.a[hb], bop, v4f{0.f, 0.f, 0.f, 0.f}, fmt, fmt, 0,
-                                                             qf.sa[hb], 0, sb);
-}
-
-template <int FMT, int NHB>
-__device__ __forceinline__ void group_epilogue(const QueryFrag<NHB> &qf, const v4f (&c)[NHB], uint32_t s, int grp,
-                                               int ngroups, int vis, int lane, float *s_scores) {
-  float acc = 0.f;
-#pragma unroll
-  for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) acc = fmaf(qf.f[hb][v], relu(c[hb][v]), acc);
-  acc = lane_group_sum(acc);
-  const int el = grp * 16 + (lane & 15);
-  const float ks = FMT == 1 ? __uint_as_float(s) : 1.0f;
-  if (lane < 16 && grp < ngroups) s_scores[el] = el < vis ? acc * ks : -INFINITY;
-}
-
-// Scores of one batch of groups, software-pipelined by one group: the MFMAs of group u + 1 are
-// issued before the epilogue of group u, so an epilogue does not wait on MFMA latency and only two
-// groups' results are live at a time.
-template <int FMT, int NHB>
-__device__ __forceinline__ void score_batch(const QueryFrag<NHB> &qf, const KeyFrag<FMT> (&kf)[batch_of<FMT>()], int g0,
-                                            int ngroups, int vis, int lane, float *s_scores) {
-  v4f c[2][NHB];
-  group_mfma<FMT, NHB>(qf, kf[0], lane, c[0]);
-#pragma unroll
-  for (int u = 0; u < batch_of<FMT>(); ++u) {
-    if (u + 1 < batch_of<FMT>()) group_mfma<FMT, NHB>(qf, kf[u + 1], lane, c[(u + 1) & 1]);
-    group_epilogue<FMT, NHB>(qf, c[u & 1], kf[u].s, g0 + u, ngroups, vis, lane, s_scores);
-  }
-}
-
-// Score the `tile` entries of a tile into s_scores (LDS); entries at tile-local index >= vis are
-// written as -inf.  The block's waves split the groups; each wave alternates two load batches so the
-// next batch is in flight while the current one is scored.  `ka` holds the wave's first batch,
-// issued by the caller.
-template <int FMT, int NHB>
-__device__ void score_tile_mfma(const QueryFrag<NHB> &qf, KeyFrag<FMT> (&ka)[batch_of<FMT>()],
-                                KeyFrag<FMT> (&kb)[batch_of<FMT>()], const TileKeys<FMT> &tk, int tile, int vis,
-                                float *s_scores) {
-  // the wave index is uniform: say so, so group offsets stay scalar (no per-lane loop over them)
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nwaves = blockDim.x >> 6;
-  const int ngroups = tile >> 4;
-  const int stride = nwaves * batch_of<FMT>();
-  // On entry ka holds groups from wave * batch and kb the batch one stride later (both in flight).
-  // Each batch is scored while the other one's loads are in flight; loads are unconditional, so
-  // the count of loads in flight is the same on every path and each wait covers only the batch
-  // about to be scored.
-  for (int g0 = wave * batch_of<FMT>(); g0 < ngroups; g0 += 2 * stride) {
-    score_batch<FMT, NHB>(qf, ka, g0, ngroups, vis, lane, s_scores);
-    load_batch<FMT>(tk, g0 + 2 * stride, lane, ka);
-    if (g0 + stride < ngroups) score_batch<FMT, NHB>(qf, kb, g0 + stride, ngroups, vis, lane, s_scores);
-    load_batch<FMT>(tk, g0 + 3 * stride, lane, kb);
-  }
-}
 
 // fp32 keys: one thread per entry, query heads from LDS.
 __device__ void score_tile_f32(const float *q_lds, const float *w, int H_I, int D_I, const float *keys,
@@ -323,6 +250,50 @@ __device__ void score_tile_f32(const float *q_lds, const float *w, int H_I, int 
       }
     }
     s_scores[i] = s;
+  }
+}
+
+// Scores of a tile for the merge's exact fallback, which runs after the scoring: the query's MFMA
+// operands are read from LDS for every group and one group per wave is in flight, so it needs few
+// registers.  Same MFMA operands and epilogue order (heads in order, then the four values of each)
+// as the streaming kernel's scorer, hence the same scores bit for bit.
+template <int FMT, int NHB>
+__device__ __forceinline__ void score_tile_lean(const QueryLds &ql, const TileKeys<FMT> &tk, int tile, int vis, float *s_scores) {
+  constexpr int fmt = FMT == 1 ? 0 : 4;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6, ngroups = tile >> 4;
+  const int g = lane >> 4, r = lane & 15;
+  for (int grp = wave; grp < ngroups; grp += nwaves) {
+    KeyFrag<FMT> kf;
+    load_key_frag<FMT>(tk, grp, lane, kf);
+    const uint4 x0 = kf.c0, x1 = FMT == 1 ? kf.c1 : make_uint4(0, 0, 0, 0);
+    const v8i bop = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+    const int sb = FMT == 1 ? 127 : int((kf.s >> (8 * g)) & 0xff);
+    float acc = 0.f;
+#pragma unroll 1
+    for (int hb = 0; hb < NHB; ++hb) {
+      const int head = hb * 16 + r;
+      v8i qa;
+      int sa;
+      if (FMT == 1) {
+        const uint4 *q = reinterpret_cast<const uint4 *>(ql.codes + head * 128 + g * 32);
+        const uint4 y0 = q[0], y1 = q[1];
+        qa = v8i{int(y0.x), int(y0.y), int(y0.z), int(y0.w), int(y1.x), int(y1.y), int(y1.z), int(y1.w)};
+        sa = 127;
+      } else {
+        const uint4 y0 = *reinterpret_cast<const uint4 *>(ql.codes + head * 64 + g * 16);
+        qa = v8i{int(y0.x), int(y0.y), int(y0.z), int(y0.w), 0, 0, 0, 0};
+        sa = ql.sbytes[head * 4 + g];
+      }
+      const v4f c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, bop, v4f{0.f, 0.f, 0.f, 0.f}, fmt, fmt, 0,
+                                                                     sa, 0, sb);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc = fmaf(ql.f[hb * 16 + g * 4 + v], relu(c[v]), acc);
+    }
+    acc = lane_group_sum(acc);
+    const int el = grp * 16 + r;
+    const float ks = FMT == 1 ? __uint_as_float(kf.s) : 1.0f;
+    if (lane < 16) s_scores[el] = el < vis ? acc * ks : -INFINITY;
   }
 }
 
@@ -390,7 +361,7 @@ struct alignas(16) SelectLds {
 // three buffers (pass p zeroes the buffer of pass p+2, whose last readers finished before pass p's
 // barrier), so a pass costs one barrier.
 template <int NT, int KPT>
-__device__ uint64_t block_cut(const uint64_t (&keys)[KPT], int need, int keep_min, SelectLds &sl) {
+__device__ __forceinline__ uint64_t block_cut(const uint64_t (&keys)[KPT], int need, int keep_min, SelectLds &sl) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int i = tid; i < 768; i += NT) (&sl.hist[0][0])[i] = 0;
@@ -465,23 +436,430 @@ __device__ uint64_t block_cut(const uint64_t (&keys)[KPT], int need, int keep_mi
   }
 }
 
-// Exact rank-`need` (1 = largest) key among the block's non-zero keys.
-template <int NT, int KPT>
-__device__ __forceinline__ uint64_t block_select(const uint64_t (&keys)[KPT], int need, SelectLds &sl) {
-  return block_cut<NT, KPT>(keys, need, need, sl);
-}
+// ---- bucket select ---------------------------------------------------------------------------
+// The same threshold as block_cut, found from one histogram of the keys' scores over kBins equal
+// bins spanning [min, max].  A bin index, (s - min) * kBins / (max - min) truncated, never decreases
+// as the score grows, so every key of a higher bin is larger than every key of a lower one.  One
+// pass locates the bin where the count from the top reaches `need`; the threshold is a bin edge when
+// that leaves at least keep_min keys above, or the exact rank inside the bin when the bin holds at
+// most kSmallBucket keys (one wave ranks them); otherwise (many equal or tightly clustered scores)
+// the radix select decides.  Scores spread over many bins, so the histogram atomics seldom collide
+// (the radix passes' top digits put most keys of a tile into a handful of bins).
+constexpr int kBins = 2048;
+constexpr int kSmallBucket = 64;
+constexpr int kDummyBins = 32;                      // where keys outside the current range are counted
 
-// ---- kernel 1: scores and per-tile candidates ------------------------------------------------
-struct alignas(16) ScoreShared {
-  QueryLds ql;
-  float scores[kMaxTile];
-  SelectLds sel;
-  int tmp[16];
+struct alignas(16) BucketLds {
+  uint32_t hist[kBins + kDummyBins];
+  uint64_t list[kSmallBucket];      // keys of the crossing bin
+  uint64_t kmin[16];
+  uint32_t omin[16], omax[16];
+  int wsum[16];
+  int res[4];                       // crossing bin, keys above it, keys in it, keys listed
 };
 
-template <int FMT, int NHB, int NT, int KPT>
+// The score a key was made from (inverse of score_order).
+__device__ __forceinline__ float order_score(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ float key_score(uint64_t k) { return order_score(uint32_t(k >> 32)); }
+
+// Reductions over the wave whose result every lane holds: DPP inside rows of 16 lanes, then the
+// gfx950 half-wave and row swaps across the four rows (no readlane round trips).
+template <bool MIN>
+__device__ __forceinline__ uint32_t wave_all_u32(uint32_t v) {
+  auto pick = [](uint32_t x, uint32_t y) { return MIN ? min(x, y) : max(x, y); };
+  v = pick(v, uint32_t(dpp<kDppQuadXor1>(int(v))));
+  v = pick(v, uint32_t(dpp<kDppQuadXor2>(int(v))));
+  v = pick(v, uint32_t(dpp<kDppRowHalfMirror>(int(v))));
+  v = pick(v, uint32_t(dpp<kDppRowMirror>(int(v))));
+  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = pick(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return pick(b[0], b[1]);
+}
+__device__ __forceinline__ uint64_t wave_all_min_u64(uint64_t v) {
+  v = umin64(v, dpp64<kDppQuadXor1>(v));
+  v = umin64(v, dpp64<kDppQuadXor2>(v));
+  v = umin64(v, dpp64<kDppRowHalfMirror>(v));
+  v = umin64(v, dpp64<kDppRowMirror>(v));
+  const uint32_t lo = uint32_t(v), hi = uint32_t(v >> 32);
+  const auto a0 = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto a1 = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  v = umin64((uint64_t(a1[0]) << 32) | a0[0], (uint64_t(a1[1]) << 32) | a0[1]);
+  const uint32_t lo2 = uint32_t(v), hi2 = uint32_t(v >> 32);
+  const auto b0 = __builtin_amdgcn_permlane16_swap(lo2, lo2, false, false);
+  const auto b1 = __builtin_amdgcn_permlane16_swap(hi2, hi2, false, false);
+  return umin64((uint64_t(b1[0]) << 32) | b0[0], (uint64_t(b1[1]) << 32) | b0[1]);
+}
+// Inclusive prefix sum over the wave: DPP shifts inside rows, then the GFX9 row broadcasts of
+// lanes 15 and 31 to the rows above them.
+__device__ __forceinline__ int wave_scan_bcast(int v) {
+  v += dpp<kDppRowShr + 1>(v);
+  v += dpp<kDppRowShr + 2>(v);
+  v += dpp<kDppRowShr + 4>(v);
+  v += dpp<kDppRowShr + 8>(v);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+template <int NT, int KPT>
+__device__ __forceinline__ uint64_t block_cut_bucket(const uint64_t (&keys)[KPT], int need, int keep_min, BucketLds &bl,
+                                                     SelectLds &sl) {
+  constexpr int NW = NT / 64, BPT = kBins / NT;
+  static_assert(BPT % 4 == 0, "bins are read four at a time");
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // state of each key: 0 out, 1 undecided (inside the current score range), 2 kept
+  int st[KPT];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) st[k] = keys[k] != 0 ? 1 : 0;
+  int rneed = need, rkeep = keep_min;             // still to find among the undecided keys
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int i = tid; i < (kBins + kDummyBins) / 4; i += NT) reinterpret_cast<uint4 *>(bl.hist)[i] = make_uint4(0, 0, 0, 0);
+    if (tid == 0) bl.res[3] = 0;
+    // the undecided keys' range, in score-order bits (which order like the scores)
+    uint32_t omin = ~0u, omax = 0u;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const uint32_t o = uint32_t(keys[k] >> 32);
+      omin = min(omin, st[k] == 1 ? o : ~0u);
+      omax = max(omax, st[k] == 1 ? o : 0u);
+    }
+    omin = wave_all_u32<true>(omin);
+    omax = wave_all_u32<false>(omax);
+    if (lane == 0) { bl.omin[wave] = omin; bl.omax[wave] = omax; }
+    lds_barrier();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) { omin = min(omin, bl.omin[w]); omax = max(omax, bl.omax[w]); }
+    const float lo = order_score(omin), hi = order_score(omax);
+    const float scale = float(kBins) / (hi - lo);
+    if (!(hi > lo) || !(scale < INFINITY) || !(lo > -INFINITY) || !(hi < INFINITY)) break;   // uniform
+    int bin[KPT];
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const int bk = min(int(__fmul_rn(__fsub_rn(key_score(keys[k]), lo), scale)), kBins - 1);
+      bin[k] = st[k] == 1 ? bk : -1;
+      atomicAdd(&bl.hist[st[k] == 1 ? bk : kBins + (lane & (kDummyBins - 1))], 1u);
+    }
+    lds_barrier();
+    // this thread's BPT bins, highest first; the count of undecided keys in every higher bin
+    const int top = kBins - 1 - tid * BPT;
+    int c[BPT], sum = 0;
+#pragma unroll
+    for (int v = 0; v < BPT / 4; ++v) {
+      const uint4 x = reinterpret_cast<const uint4 *>(bl.hist)[(top - 3 - 4 * v) >> 2];
+      c[4 * v] = int(x.w); c[4 * v + 1] = int(x.z); c[4 * v + 2] = int(x.y); c[4 * v + 3] = int(x.x);
+    }
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) sum += c[j];
+    const int incl = wave_scan_bcast(sum);
+    if (lane == 63) bl.wsum[wave] = incl;
+    lds_barrier();
+    int cum = incl - sum;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) cum += w < wave ? bl.wsum[w] : 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      if (cum < rneed && rneed <= cum + c[j]) { bl.res[0] = top - j; bl.res[1] = cum; bl.res[2] = c[j]; }
+      cum += c[j];
+    }
+    lds_barrier();
+    const int bstar = bl.res[0], above = bl.res[1], cnt = bl.res[2];
+    int edge = -1;                                // undecided keys of bins >= edge are kept
+    if (above >= rkeep) edge = bstar + 1;
+    else if (above + cnt == rneed) edge = bstar;
+    if (edge >= 0) {                              // the smallest kept key
+      uint64_t mn = ~uint64_t(0);
+#pragma unroll
+      for (int k = 0; k < KPT; ++k) mn = umin64(mn, (st[k] == 2 || bin[k] >= edge) && st[k] != 0 ? keys[k] : ~uint64_t(0));
+      mn = wave_all_min_u64(mn);
+      if (lane == 0) bl.kmin[wave] = mn;
+      lds_barrier();
+      uint64_t e = ~uint64_t(0);
+#pragma unroll
+      for (int w = 0; w < NW; ++w) e = umin64(e, bl.kmin[w]);
+      lds_barrier();
+      return e;
+    }
+    if (cnt <= kSmallBucket) {                    // rank the crossing bin's keys (distinct) on one wave
+#pragma unroll
+      for (int k = 0; k < KPT; ++k)
+        if (bin[k] == bstar) bl.list[atomicAdd(&bl.res[3], 1)] = keys[k];
+      lds_barrier();
+      if (wave == 0) {
+        const uint64_t x = lane < cnt ? bl.list[lane] : 0;
+        int rank = 0;
+        for (int j = 0; j < cnt; ++j) rank += readlane64(x, j) > x;
+        if (lane < cnt && rank == rneed - above - 1) bl.kmin[0] = x;
+      }
+      lds_barrier();
+      const uint64_t e = bl.kmin[0];
+      lds_barrier();
+      return e;
+    }
+    // narrow to the crossing bin: keys above it are kept, keys below it are out
+#pragma unroll
+    for (int k = 0; k < KPT; ++k)
+      st[k] = st[k] == 1 ? (bin[k] > bstar ? 2 : (bin[k] == bstar ? 1 : 0)) : st[k];
+    rneed -= above;
+    rkeep -= above;
+  }
+  // equal or extremely clustered scores: the radix select decides (ties by index)
+  return block_cut<NT, KPT>(keys, need, keep_min, sl);
+}
+
+// Exact rank-`need` (1 = largest) key among the block's non-zero keys.
+template <int NT, int KPT>
+__device__ __forceinline__ uint64_t block_select(const uint64_t (&keys)[KPT], int need, BucketLds &bl, SelectLds &sl) {
+  return block_cut_bucket<NT, KPT>(keys, need, need, bl, sl);
+}
+
+// ---- the merge: a query's exact top-k from its tiles' candidates -----------------------------
+// Run either by the last of the query's tile workgroups to finish (one-query path: no separate
+// launch) or by a merge kernel with one workgroup per query (shared-tile path).
+template <int TILE>
+struct alignas(16) IndexSharedT {
+  QueryLds ql;                        // the query (quantised, or fp32 values and weights)
+  float scores[TILE];                 // one tile's scores
+  SelectLds sel;
+  BucketLds bl;
+  int tmp[16];
+  int flag;
+  int counts[kMaxCand / 8];           // per tile: candidates kept
+  uint64_t bounds[kMaxCand / 8];      // per tile: smallest kept key (0: the tile kept every entry)
+  uint64_t work[kMaxK + TILE];        // exact fallback: the working set
+};
+// the tile kernel (tiles of up to kMaxTile entries)
+typedef IndexSharedT<kMaxTile> IndexShared;
+
+// Sort P (a power of two) entry indices ascending in LDS.
+__device__ void bitonic_sort_u32(uint32_t *v, int P) {
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        int ixj = i ^ j;
+        if (ixj > i) {
+          uint32_t x = v[i], y = v[ixj];
+          bool up = (i & k) == 0;
+          if ((x > y) == up) { v[i] = y; v[ixj] = x; }
+        }
+      }
+      lds_barrier();
+    }
+  }
+}
+
+// The query of merge workgroup `qi` into sh.ql (fp32: values and weights; otherwise quantised).
+template <int FMT, int NT, class SH>
+__device__ __forceinline__ void load_query_lds(const IndexArgs &a, SH &sh, int64_t qi) {
+  if (FMT == 0) {
+    float *q_lds = reinterpret_cast<float *>(sh.ql.codes);    // H_I * D_I <= 2048 floats
+    const float *qsrc = static_cast<const float *>(a.q_idx) + qi * a.H_I * a.D_I;
+    for (int i = threadIdx.x; i < a.H_I * a.D_I; i += NT) q_lds[i] = qsrc[i];
+    if (int(threadIdx.x) < a.H_I) sh.ql.f[threadIdx.x] = a.w_idx[qi * a.H_I + threadIdx.x];
+  } else {
+    QueryRaw raw;
+    load_query_raw(static_cast<const uint16_t *>(a.q_idx) + qi * a.H_I * 128, a.w_idx + qi * a.H_I, a.H_I, raw);
+    prep_query_lds<FMT>(raw, a.H_I, sh.ql);
+  }
+  lds_barrier();
+}
+
+// Exact fallback: the candidate set may miss winners hidden in tiles whose kept keys all beat
+// `tau`.  Keep a working set W (the k_eff best so far) in LDS and merge in every such tile,
+// re-scored from its keys.  Writes the final selection in ascending index order.  The query must
+// be in sh.ql already.
+template <int FMT, int NHB, int NT, int KPT, class SH>
+__device__ __forceinline__ void merge_fallback(const IndexArgs &a, SH &sh, const uint64_t (&keys)[KPT], uint64_t tau,
+                               int b, int64_t n_vis, int k_eff, int32_t *out) {
+  const int tid = threadIdx.x;
+  const int tile = a.plan.tile, n_tiles = a.plan.n_tiles;
+  int wn;
+  {
+    int mine = 0;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) mine += (keys[k] != 0 && keys[k] >= tau);
+    int pos = block_excl_scan<NT>(mine, sh.tmp, wn);
+#pragma unroll
+    for (int k = 0; k < KPT; ++k)
+      if (keys[k] != 0 && keys[k] >= tau) sh.work[pos++] = keys[k];
+  }
+  lds_barrier();
+  const float *q_lds = reinterpret_cast<const float *>(sh.ql.codes);
+  constexpr int KW = int(sizeof(sh.work) / 8) / NT;          // the working set: k_eff + one tile
+  for (int tl = 0; tl < n_tiles; ++tl) {
+    const uint64_t bt = sh.bounds[tl];
+    if (bt == 0 || bt <= tau) continue;                        // complete, or cannot hold winners
+    const int64_t e_begin = int64_t(tl) * tile;
+    const int vis = int(max(int64_t(0), min(int64_t(tile), n_vis - e_begin)));
+    const int64_t row0 = int64_t(b) * a.N_cap + e_begin;
+    if (FMT == 0) {
+      score_tile_f32(q_lds, sh.ql.f, a.H_I, a.D_I, static_cast<const float *>(a.k_codes), row0, tile, vis,
+                     sh.scores);
+    } else {
+      const int rows = int(min(int64_t(tile), a.N_cap - e_begin));
+      const TileKeys<FMT> tk = make_tile_keys<FMT>(a.k_codes, a.k_scales, row0, rows, tid & 63);
+      score_tile_lean<FMT, NHB>(sh.ql, tk, tile, vis, sh.scores);
+    }
+    lds_barrier();
+    // append the tile's entries below its bound (the ones not already candidates) and above tau
+    int mine = 0;
+    for (int i = tid; i < vis; i += NT) {
+      const uint64_t key = make_key(sh.scores[i], uint32_t(e_begin + i));
+      mine += (key < bt && key > tau);
+    }
+    int total;
+    int pos = block_excl_scan<NT>(mine, sh.tmp, total) + wn;
+    for (int i = tid; i < vis; i += NT) {
+      const uint64_t key = make_key(sh.scores[i], uint32_t(e_begin + i));
+      if (key < bt && key > tau) sh.work[pos++] = key;
+    }
+    wn += total;
+    lds_barrier();
+    if (wn >= k_eff) {                                          // shrink W back to the k_eff best
+      uint64_t wk[KW];
+#pragma unroll
+      for (int k = 0; k < KW; ++k) {
+        const int i = tid * KW + k;
+        wk[k] = i < wn ? sh.work[i] : 0;
+      }
+      lds_barrier();
+      tau = block_select<NT, KW>(wk, k_eff, sh.bl, sh.sel);
+      int m2 = 0;
+#pragma unroll
+      for (int k = 0; k < KW; ++k) m2 += (wk[k] != 0 && wk[k] >= tau);
+      int tot2;
+      int p2 = block_excl_scan<NT>(m2, sh.tmp, tot2);
+#pragma unroll
+      for (int k = 0; k < KW; ++k)
+        if (wk[k] != 0 && wk[k] >= tau) sh.work[p2++] = wk[k];
+      wn = tot2;
+      lds_barrier();
+    }
+  }
+  // ascending indices
+  uint32_t *idx = reinterpret_cast<uint32_t *>(sh.work);
+  int P = 1;
+  while (P < wn) P <<= 1;
+  uint32_t tmpv[KW];
+#pragma unroll
+  for (int k = 0; k < KW; ++k) {
+    const int i = tid * KW + k;
+    tmpv[k] = i < wn ? key_index(sh.work[i]) : 0xffffffffu;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int k = 0; k < KW; ++k) {
+    const int i = tid * KW + k;
+    if (i < P) idx[i] = tmpv[k];
+  }
+  lds_barrier();
+  bitonic_sort_u32(idx, P);
+  for (int i = tid; i < a.topk; i += NT) out[i] = i < wn ? int32_t(idx[i]) : -1;
+}
+
+// Select query qi's top-k from the candidates of all its tiles (candidate slots of tile j at
+// j * cand, ascending entry order within a tile, so slot order is entry order).  `have_query`: the
+// query is already in sh.ql (the tile workgroup that scored it), needed only by the fallback.
+template <int FMT, int NHB, int NT, int KPT, class SH>
+__device__ __forceinline__ void merge_query(const IndexArgs &a, SH &sh, int64_t qi, int b, int s, bool have_query) {
+  const int tid = threadIdx.x;
+  const int cand = a.plan.cand, n_tiles = a.plan.n_tiles;
+  const int cshift = __builtin_ctz(uint32_t(cand));              // cand is a power of two
+  const int64_t n_q = int64_t(a.B) * a.Sq;
+  const uint64_t *cand_keys = static_cast<const uint64_t *>(a.workspace);
+  const uint64_t *cand_bound = cand_keys + n_q * n_tiles * cand;
+  const int *cand_count = reinterpret_cast<const int *>(cand_bound + n_q * n_tiles);
+  int32_t *out = a.topk_idx + qi * a.topk;
+
+  // candidate slots and per-tile counts are loaded together; slots past a tile's count are masked
+  uint64_t keys[KPT];
+  const int slots = n_tiles * cand;                            // a multiple of 8
+  static_assert(KPT % 2 == 0, "slots are loaded in pairs");
+  {
+    // coherent loads (the tile workgroups of this launch wrote them); slots past the region read 0
+    const __amdgpu_buffer_rsrc_t src = coherent_region(cand_keys + qi * slots, uint32_t(slots) * 8u);
+#pragma unroll
+    for (int k = 0; k < KPT; k += 2) {
+      const uint4 v = load_coherent16(src, uint32_t(tid * KPT + k) * 8u);
+      keys[k] = (uint64_t(v.y) << 32) | v.x;
+      keys[k + 1] = (uint64_t(v.w) << 32) | v.z;
+    }
+  }
+  // per-tile counts and bounds, held in registers until the position is known (loaded from a
+  // clamped slot, so no branch separates these loads from the ones above)
+  constexpr int TPT = (kMaxCand / 8 + NT - 1) / NT;
+  int cnt[TPT];
+  uint64_t bnd[TPT];
+#pragma unroll
+  for (int j = 0; j < TPT; ++j) {
+    const int i = min(tid + j * NT, n_tiles - 1);
+    cnt[j] = load_coherent(&cand_count[qi * n_tiles + i]);
+    bnd[j] = load_coherent(&cand_bound[qi * n_tiles + i]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int64_t t = a.q_pos0[b] + s;
+  const int64_t n_vis = min(a.n_entries[b], div_count(t + 1, a.m));
+  const int k_eff = int(min(int64_t(a.topk), n_vis));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < TPT; ++j) {
+    const int i = tid + j * NT;
+    if (i < n_tiles) { sh.counts[i] = cnt[j]; sh.bounds[i] = bnd[j]; }
+  }
+  if (tid == 0) sh.flag = 0;
+  lds_barrier();
+  int nvalid_local = 0;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int slot = tid * KPT + k;
+    if (slot >= slots || (slot & (cand - 1)) >= sh.counts[slot >> cshift]) keys[k] = 0;
+    nvalid_local += keys[k] != 0;
+  }
+  int nvalid;
+  (void)block_excl_scan<NT>(nvalid_local, sh.tmp, nvalid);
+  if (k_eff == 0) {
+    for (int i = tid; i < a.topk; i += NT) out[i] = -1;
+    return;
+  }
+  uint64_t tau = 0;                                            // k-th best candidate (0: need all)
+  if (nvalid >= k_eff) tau = block_select<NT, KPT>(keys, k_eff, sh.bl, sh.sel);
+  // a truncated tile whose smallest kept key beats tau may hold further winners
+  for (int i = tid; i < n_tiles; i += NT)
+    if (sh.bounds[i] != 0 && sh.bounds[i] > tau) sh.flag = 1;
+  lds_barrier();
+  if (sh.flag) {
+    if (!have_query) load_query_lds<FMT, NT>(a, sh, qi);
+    merge_fallback<FMT, NHB, NT, KPT>(a, sh, keys, tau, b, n_vis, k_eff, out);
+    return;
+  }
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) mine += (keys[k] != 0 && keys[k] >= tau);
+  int total;
+  int pos = block_excl_scan<NT>(mine, sh.tmp, total);
+#pragma unroll
+  for (int k = 0; k < KPT; ++k)
+    if (keys[k] != 0 && keys[k] >= tau) out[pos++] = int32_t(key_index(keys[k]));
+  for (int i = k_eff + tid; i < a.topk; i += NT) out[i] = -1;
+}
+
+// Arrival counters of the one-query path: one per query (kCounterStride apart), after the
+// candidate arrays.
+__host__ __device__ inline size_t arrivals_offset(int64_t n_q, const IndexPlan &p) {
+  const int64_t slots = n_q * p.n_tiles;
+  const size_t off = size_t(slots * p.cand * 8 + slots * 8 + slots * 4);
+  return (off + 255) / 256 * 256;
+}
+
+// ---- kernel 1: fp32 keys -- scores, per-tile candidates and (last tile of a query) the merge ------
+// One query and one tile of up to 2,048 entries per workgroup; one thread per entry.  Every tile
+// workgroup of a query publishes its candidates and counts itself in (arrive_last); the last one
+// runs the merge for the query and leaves the counter at zero for the next call.
+template <int NT, int KPT, int MKPT, bool FUSE>
 __global__ void __launch_bounds__(NT) index_score_kernel(IndexArgs a) {
-  __shared__ ScoreShared sh;
+  __shared__ IndexShared sh;
   const int tile_id = blockIdx.x;
   const int64_t qi = blockIdx.y;                               // query = b * Sq + s
   const int b = int(blockIdx.y / uint32_t(a.Sq)), s = int(blockIdx.y) - b * a.Sq;
@@ -493,66 +871,287 @@ __global__ void __launch_bounds__(NT) index_score_kernel(IndexArgs a) {
   uint64_t *cand_bound = cand_keys + n_q * a.plan.n_tiles * cand;
   int *cand_count = reinterpret_cast<int *>(cand_bound + n_q * a.plan.n_tiles);
   const int64_t row0 = int64_t(b) * a.N_cap + e_begin;
-  // The quantised-key loads are range-checked by their buffer resources, so they are issued
-  // before the visible count (which waits on two scalar loads and a division) is known.
-  QueryRaw raw;
-  KeyFrag<FMT> ka[batch_of<FMT>()], kb[batch_of<FMT>()];
-  TileKeys<FMT> tk;
-  if (FMT != 0) {
-    // the query's loads go first (loads complete in issue order), then two batches of keys,
-    // which stream while the query is quantised
-    load_query_raw(static_cast<const uint16_t *>(a.q_idx) + qi * a.H_I * 128, a.w_idx + qi * a.H_I, a.H_I, raw);
-    __builtin_amdgcn_sched_barrier(0);                       // keep the query loads first
-    const int rows = int(min(int64_t(tile), a.N_cap - e_begin));
-    tk = make_tile_keys<FMT>(a.k_codes, a.k_scales, row0, rows, threadIdx.x & 63);
-    const int g_first = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * batch_of<FMT>();
-    load_batch<FMT>(tk, g_first, threadIdx.x & 63, ka);
-    load_batch<FMT>(tk, g_first + (NT / 64) * batch_of<FMT>(), threadIdx.x & 63, kb);
-  }
   const int64_t t = a.q_pos0[b] + s;
   const int64_t n_vis = min(a.n_entries[b], div_count(t + 1, a.m));
   const int vis = int(max(int64_t(0), min(int64_t(tile), n_vis - e_begin)));
-
-  if (vis == 0 && a.scores == nullptr) {                      // nothing visible in this tile
-    if (threadIdx.x == 0) { cand_count[out_slot] = 0; cand_bound[out_slot] = 0; }
-    return;
+  // a tile with nothing visible publishes an empty candidate list (unless scores are asked for)
+  const bool work = vis > 0 || a.scores != nullptr;
+  if (work) {
+    load_query_lds<0, NT>(a, sh, qi);
+    score_tile_f32(reinterpret_cast<const float *>(sh.ql.codes), sh.ql.f, a.H_I, a.D_I,
+                   static_cast<const float *>(a.k_codes), row0, tile, vis, sh.scores);
+    lds_barrier();
+    if (a.scores) {
+      float *dst = a.scores + qi * a.N_cap;
+      for (int i = threadIdx.x; i < tile; i += NT)
+        if (e_begin + i < a.N_cap) dst[e_begin + i] = sh.scores[i];
+    }
+    // keys of this thread's KPT consecutive entries
+    uint64_t keys[KPT];
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const int i = threadIdx.x * KPT + k;
+      keys[k] = i < vis ? make_key(sh.scores[i], uint32_t(e_begin + i)) : 0;
+    }
+    uint64_t bound = 0;
+    // keep the tile's largest keys: all `cand` of them, or at least half as many when one histogram
+    // pass already separates them (the merge checks every truncated tile's bound against its
+    // threshold and rescans the tile when the bound is not below it)
+    if (vis > cand) bound = block_cut_bucket<NT, KPT>(keys, cand, cand / 2, sh.bl, sh.sel);
+    int mine = 0;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) mine += (keys[k] != 0 && keys[k] >= bound);
+    int total;
+    int pos = block_excl_scan<NT>(mine, sh.tmp, total);
+    // coherent stores: the merging workgroup reads them back in the same launch
+    uint64_t *dst = cand_keys + out_slot * cand;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k)
+      if (keys[k] != 0 && keys[k] >= bound) store_coherent(&dst[pos++], keys[k]);
+    if (threadIdx.x == 0) { store_coherent(&cand_count[out_slot], total); store_coherent(&cand_bound[out_slot], bound); }
+  } else if (threadIdx.x == 0) {
+    store_coherent(&cand_count[out_slot], 0);
+    store_coherent(&cand_bound[out_slot], uint64_t(0));
   }
-  if (FMT == 0) {
-    float *q_lds = reinterpret_cast<float *>(sh.ql.codes);    // H_I * D_I <= 2048 floats
-    const float *qsrc = static_cast<const float *>(a.q_idx) + qi * a.H_I * a.D_I;
-    for (int i = threadIdx.x; i < a.H_I * a.D_I; i += NT) q_lds[i] = qsrc[i];
-    if (threadIdx.x < a.H_I) sh.ql.f[threadIdx.x] = a.w_idx[qi * a.H_I + threadIdx.x];
-    lds_barrier();
-    score_tile_f32(q_lds, sh.ql.f, a.H_I, a.D_I, static_cast<const float *>(a.k_codes), row0, tile, vis,
-                   sh.scores);
-  } else {
-    prep_query_lds<FMT>(raw, a.H_I, sh.ql);
-    lds_barrier();
-    QueryFrag<NHB> qf;
-    load_query_frag<FMT, NHB>(sh.ql, threadIdx.x & 63, qf);
-    score_tile_mfma<FMT, NHB>(qf, ka, kb, tk, tile, vis, sh.scores);
+  if constexpr (FUSE) {
+    int *arrivals = reinterpret_cast<int *>(static_cast<uint8_t *>(a.workspace) + arrivals_offset(n_q, a.plan));
+    if (!arrive_last(&arrivals[qi * kCounterStride], a.plan.n_tiles, &sh.flag)) return;
+    merge_query<0, 1, NT, MKPT>(a, sh, qi, b, s, work);
+  }
+}
+
+// ---- kernel 1s: streaming scores of quantised keys, one query per workgroup ------------------
+// One 512-thread workgroup per CU owns a contiguous segment of one query's keys (up to 4,096
+// entries) and streams it through a ring of three 32 KB LDS chunks filled by direct-to-LDS
+// buffer loads (range-checked: rows past the cache read as zeros), so the HBM stream does not wait
+// for the query: the first two chunks and the query itself are requested at once, and every chunk
+// scored frees its slot for the chunk two ahead.  The loads are laid out so that lane (r, g) of a
+// scoring wave reads its MFMA key operand (entry r of a 16-entry group, K-chunk g) as one linear
+// 16-byte LDS read.  Scores (same MFMA operands and epilogue order as the tile kernel's, hence the
+// same bits) stay in LDS; the segment then keeps its best keys like a tile, and the query's last
+// segment workgroup to finish merges (FUSE).
+//
+// The LDS loads are issued from inline assembly with their LDS address in m0: the compiler then
+// knows of no vector-memory load in flight and adds no waits of its own, and every wait is an
+// explicit vmcnt count below (chunks complete in issue order; the query's loads are issued first).
+// The compiler's LDS-DMA intrinsic would serve as well, except that the compiler cannot tell the
+// ring's slots apart and waits for every chunk in flight before each LDS read.
+constexpr int kStreamThreads = 512;
+constexpr int kStreamSeg = 4096;                    // entries per workgroup, at most
+constexpr int kRingSlots = 3;
+constexpr int kChunkBytes = 32768;                  // key codes per ring slot
+template <int FMT>
+constexpr int chunk_entries() { return FMT == 1 ? 256 : 512; }
+
+__device__ __forceinline__ uint32_t lds_address(const void *p) {      // p points into LDS
+  const __attribute__((address_space(3))) void *l = (const __attribute__((address_space(3))) void *)(p);
+  return __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(l)));
+}
+// Lane l's 16 (4) bytes at byte offset voff of the buffer go to LDS address m0 + 16 l (4 l).
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(lds) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_loads() {               // at most N vector loads in flight
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+// Barrier for the ring: the wave's direct-to-LDS loads are complete already (explicit vmcnt
+// waits); its own LDS reads complete before it (lgkmcnt(0)), so a slot read before the barrier may
+// be refilled after it; the compiler-only fences keep LDS accesses from moving across it.
+__device__ __forceinline__ void ring_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+struct alignas(16) StreamShared {
+  union {
+    struct {                                        // while streaming
+      uint8_t codes[kRingSlots][kChunkBytes];
+      uint32_t scales[kRingSlots][512];
+    };
+    struct {                                        // the merge, after the stream
+      int counts[kMaxCand / 8];
+      uint64_t bounds[kMaxCand / 8];
+      uint64_t work[kMaxK + kStreamSeg];
+    };
+  };
+  QueryLds ql;
+  float scores[kStreamSeg];                         // before the scores: the raw bf16 query
+  float qw[64];                                     // the query's head weights
+  SelectLds sel;
+  BucketLds bl;
+  int tmp[16];
+  int flag;
+};
+
+template <int FMT, int NHB, bool FUSE>
+__global__ void __launch_bounds__(kStreamThreads, 1) index_stream_kernel(IndexArgs a) {
+  constexpr int NT = kStreamThreads, NW = NT / 64;
+  constexpr int CH = chunk_entries<FMT>();          // entries per chunk
+  constexpr int RB = FMT == 1 ? 128 : 64;           // code bytes per entry
+  static_assert(CH * RB == kChunkBytes, "a chunk fills one slot");
+  constexpr int CODE_I = kChunkBytes / 1024 / NW;   // 16-byte-per-lane loads per wave and chunk
+  constexpr int SCALE_I = CH / 64;                  // 4-byte-per-lane loads holding a chunk's scales
+  constexpr int P = CODE_I + 1;                     // loads per wave and chunk
+  constexpr int GPW = CH / 16 / NW;                 // 16-entry groups scored per wave and chunk
+  constexpr int KPT = kStreamSeg / NT;
+  constexpr int Q_I = 2;                            // the raw query: 16 KB of bf16 over 8 waves
+  __shared__ StreamShared sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int seg_id = blockIdx.x;
+  const int64_t qi = blockIdx.y;
+  const int b = int(blockIdx.y / uint32_t(a.Sq)), s = int(blockIdx.y) - b * a.Sq;
+  const int seg = a.plan.tile, cand = a.plan.cand;
+  const int64_t e_begin = int64_t(seg_id) * seg;
+  const int64_t out_slot = qi * a.plan.n_tiles + seg_id;
+  const int64_t n_q = int64_t(a.B) * a.Sq;
+  const int rows = int(min(int64_t(seg), a.N_cap - e_begin));
+  const int nch = (rows + CH - 1) / CH;
+  const int64_t row0 = int64_t(b) * a.N_cap + e_begin;
+  // the position and entry count first: loaded before any asm statement, they stay scalar loads
+  // (a vector load here would make the compiler wait for every direct-to-LDS load issued before
+  // its use)
+  const int64_t t = a.q_pos0[b] + s;
+  const int64_t n_ent = a.n_entries[b];
+  const __amdgpu_buffer_rsrc_t rcodes = coherent_region(static_cast<const uint8_t *>(a.k_codes) + row0 * RB,
+                                                        uint32_t(rows * RB));
+  const __amdgpu_buffer_rsrc_t rscales = coherent_region(static_cast<const uint8_t *>(a.k_scales) + row0 * 4,
+                                                         uint32_t(rows * 4));
+  // the raw query (heads x 128 bf16; heads past H_I read zeros) and its weights, first
+  {
+    const __amdgpu_buffer_rsrc_t rq = coherent_region(static_cast<const uint16_t *>(a.q_idx) + qi * a.H_I * 128,
+                                                      uint32_t(a.H_I * 256));
+    const __amdgpu_buffer_rsrc_t rw = coherent_region(a.w_idx + qi * a.H_I, uint32_t(a.H_I * 4));
+#pragma unroll
+    for (int i = 0; i < Q_I; ++i) {
+      const int blk = wave * Q_I + i;                 // 1 KB blocks of the 16 KB query
+      lds_load16(rq, uint32_t(blk * 1024 + lane * 16), lds_address(reinterpret_cast<uint8_t *>(sh.scores) + blk * 1024));
+    }
+    lds_load4(rw, uint32_t(lane * 4), lds_address(sh.qw));   // every wave: the same 256 bytes
+  }
+  // chunk c of the segment into ring slot SLOT
+  auto issue = [&](int c, uint8_t *codes, uint32_t *scales) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CODE_I; ++i) {
+      const int blk = wave * CODE_I + i;              // 1 KB block of the slot
+      uint32_t off;
+      if (FMT == 1) {                                 // block = half h of group blk / 2: bytes 16 (2 g + h)
+        const int grp = blk >> 1, h = blk & 1;
+        off = uint32_t((c * CH + grp * 16 + r16) * RB + (2 * g4 + h) * 16);
+      } else {                                        // block = group blk: bytes 16 g of each entry
+        off = uint32_t((c * CH + blk * 16 + r16) * RB + g4 * 16);
+      }
+      lds_load16(rcodes, off, lds_address(codes + blk * 1024));
+    }
+    const int j = wave % SCALE_I;                     // scale block j (fp8: two waves load each block)
+    lds_load4(rscales, uint32_t((c * CH + j * 64 + lane) * 4), lds_address(scales + j * 64));
+  };
+  // chunk 0 goes out with the query; chunks 1 and 2 only once the query is in: every load issued
+  // across the device before the query's is served before it, so the first requests are kept few
+  issue(0, sh.codes[0], sh.scales[0]);
+  const int64_t n_vis = min(n_ent, div_count(t + 1, a.m));
+  const int vis = int(max(int64_t(0), min(int64_t(seg), n_vis - e_begin)));
+  wait_loads<P>();                                  // the query (issued before chunk 0)
+  ring_barrier();
+  if (nch > 1) issue(1, sh.codes[1], sh.scales[1]);
+  if (nch > 2) issue(2, sh.codes[2], sh.scales[2]);
+  if (tid < 256) {
+    QueryRaw raw;
+    const int h = min(tid >> 2, a.H_I - 1), c = tid & 3;
+    const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(sh.scores) + h * 256 + c * 64);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint4 v = src[k];
+      raw.wv[4 * k] = v.x; raw.wv[4 * k + 1] = v.y; raw.wv[4 * k + 2] = v.z; raw.wv[4 * k + 3] = v.w;
+    }
+    raw.w = sh.qw[h];
+    prep_query_slot<FMT>(raw, tid, a.H_I, sh.ql);
+  }
+  ring_barrier();
+  QueryFrag<NHB> qf;
+  load_query_frag<FMT, NHB>(sh.ql, lane, qf);
+  constexpr int fmt = FMT == 1 ? 0 : 4;               // instruction format code: 0 = fp8 e4m3, 4 = fp4 e2m1
+  // scores of chunk c from a slot: the wave's GPW groups, MFMAs of the next group issued before the
+  // previous group's epilogue
+  auto score = [&](int c, const uint8_t *codes, const uint32_t *scales) __attribute__((always_inline)) {
+    v8i bop[GPW];
+    uint32_t ks[GPW];
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) {
+      const int grp = wave * GPW + u;
+      uint4 x0, x1 = make_uint4(0, 0, 0, 0);
+      if (FMT == 1) {
+        x0 = *reinterpret_cast<const uint4 *>(codes + (2 * grp) * 1024 + lane * 16);
+        x1 = *reinterpret_cast<const uint4 *>(codes + (2 * grp + 1) * 1024 + lane * 16);
+      } else {
+        x0 = *reinterpret_cast<const uint4 *>(codes + grp * 1024 + lane * 16);
+      }
+      bop[u] = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+      ks[u] = scales[grp * 16 + r16];
+    }
+    v4f acc4[2][NHB];
+    auto mfma = [&](int u, v4f (&cc)[NHB]) __attribute__((always_inline)) {
+      const int sb = FMT == 1 ? 127 : int((ks[u] >> (8 * g4)) & 0xff);
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
+        cc[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf.a[hb], bop[u], v4f{0.f, 0.f, 0.f, 0.f}, fmt, fmt,
+                                                                  0, qf.sa[hb], 0, sb);
+    };
+    mfma(0, acc4[0]);
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) {
+      if (u + 1 < GPW) mfma(u + 1, acc4[(u + 1) & 1]);
+      float acc = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc = fmaf(qf.f[hb][v], relu(acc4[u & 1][hb][v]), acc);
+      acc = lane_group_sum(acc);
+      const int el = c * CH + (wave * GPW + u) * 16 + r16;
+      const float kscale = FMT == 1 ? __uint_as_float(ks[u]) : 1.0f;
+      if (lane < 16) sh.scores[el] = el < vis ? acc * kscale : -INFINITY;
+    }
+  };
+  // the stream: wait for chunk c (chunks c + 1 and, for c == 0, c + 2 may be younger), then refill
+  // the slot of chunk c - 1 with chunk c + 2, then score chunk c
+  auto step = [&](int c, int cur) __attribute__((always_inline)) {
+    if (c == 0 && nch > 2) wait_loads<2 * P>();
+    else if (c + 1 < nch) wait_loads<P>();
+    else wait_loads<0>();
+    ring_barrier();
+    const int nxt = cur == 0 ? 2 : cur - 1;          // slot of chunk c + 2 = slot of chunk c - 1
+    if (c >= 1 && c + 2 < nch) issue(c + 2, sh.codes[nxt], sh.scales[nxt]);
+    score(c, sh.codes[cur], sh.scales[cur]);
+  };
+  for (int c = 0; c < nch; c += kRingSlots) {
+    step(c, 0);
+    if (c + 1 < nch) step(c + 1, 1);
+    if (c + 2 < nch) step(c + 2, 2);
   }
   lds_barrier();
   if (a.scores) {
     float *dst = a.scores + qi * a.N_cap;
-    for (int i = threadIdx.x; i < tile; i += NT)
-      if (e_begin + i < a.N_cap) dst[e_begin + i] = sh.scores[i];
+    for (int i = tid; i < rows; i += NT) dst[e_begin + i] = i < nch * CH ? sh.scores[i] : -INFINITY;
   }
-  // keys of this thread's KPT consecutive entries
+  // the segment's best keys, as a tile's
+  uint64_t *cand_keys = static_cast<uint64_t *>(a.workspace);
+  uint64_t *cand_bound = cand_keys + n_q * a.plan.n_tiles * cand;
+  int *cand_count = reinterpret_cast<int *>(cand_bound + n_q * a.plan.n_tiles);
   uint64_t keys[KPT];
-  int nvalid_local = 0;
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
-    const int i = threadIdx.x * KPT + k;
-    const bool ok = i < vis;
-    keys[k] = ok ? make_key(sh.scores[i], uint32_t(e_begin + i)) : 0;
-    nvalid_local += ok;
+    const int i = tid * KPT + k;
+    keys[k] = i < vis ? make_key(sh.scores[i], uint32_t(e_begin + i)) : 0;
   }
   uint64_t bound = 0;
-  // keep the tile's largest keys: all `cand` of them, or at least half as many when one histogram
-  // pass already separates them (the merge checks every truncated tile's bound against its
-  // threshold and rescans the tile when the bound is not below it)
-  if (vis > cand) bound = block_cut<NT, KPT>(keys, cand, cand / 2, sh.sel);
+  if (vis > cand) bound = block_cut_bucket<NT, KPT>(keys, cand, cand / 2, sh.bl, sh.sel);
   int mine = 0;
 #pragma unroll
   for (int k = 0; k < KPT; ++k) mine += (keys[k] != 0 && keys[k] >= bound);
@@ -561,9 +1160,14 @@ __global__ void __launch_bounds__(NT) index_score_kernel(IndexArgs a) {
   uint64_t *dst = cand_keys + out_slot * cand;
 #pragma unroll
   for (int k = 0; k < KPT; ++k)
-    if (keys[k] != 0 && keys[k] >= bound) dst[pos++] = keys[k];
-  if (threadIdx.x == 0) { cand_count[out_slot] = total; cand_bound[out_slot] = bound; }
-  (void)nvalid_local;
+    if (keys[k] != 0 && keys[k] >= bound) store_coherent(&dst[pos++], keys[k]);
+  if (tid == 0) { store_coherent(&cand_count[out_slot], total); store_coherent(&cand_bound[out_slot], bound); }
+  if constexpr (FUSE) {
+    int *arrivals = reinterpret_cast<int *>(static_cast<uint8_t *>(a.workspace) + arrivals_offset(n_q, a.plan));
+    if (!arrive_last(&arrivals[qi * kCounterStride], a.plan.n_tiles, &sh.flag)) return;
+    // the ring is no longer read: the merge's arrays may take its place
+    merge_query<FMT, NHB, NT, 8>(a, sh, qi, b, s, true);
+  }
 }
 
 // ---- kernel 1b (prefill): one key tile, eight queries of one sequence ------------------------
@@ -586,7 +1190,7 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
-__device__ uint64_t wave_cut(const uint64_t (&keys)[8], int need, int keep_min, uint32_t *H) {
+__device__ __forceinline__ uint64_t wave_cut(const uint64_t (&keys)[8], int need, int keep_min, uint32_t *H) {
   const int lane = threadIdx.x & 63;
   uint64_t mn = ~uint64_t(0), mx = 0;
 #pragma unroll
@@ -664,6 +1268,26 @@ __host__ __device__ inline size_t prepared_query_offset(int64_t n_q, const Index
 // Shared-tile path, step 0: every query quantised once (the same encoders, so the same bytes, as
 // the one-query kernel's) into the workspace; the tile workgroups then copy it instead of
 // re-quantising the query for each of their tiles.
+// The indexer's query encoding on its own (csa_quantize_query): one workgroup per query, the same
+// prep_query_slot as every scoring path, the image copied out field by field.
+template <int FMT>
+__global__ void __launch_bounds__(256) query_codes_kernel(const uint16_t *q, const float *w, int H_I, uint8_t *codes,
+                                                          uint8_t *scale_bytes, float *factors) {
+  __shared__ QueryLds ql;
+  const int64_t qi = blockIdx.x;
+  const int t = threadIdx.x;
+  QueryRaw raw;
+  load_query_raw(q + qi * H_I * 128, w + qi * H_I, H_I, raw, t);
+  prep_query_slot<FMT>(raw, t, H_I, ql);
+  lds_barrier();
+  constexpr int RB = FMT == 1 ? 128 : 64;                      // code bytes per head
+  for (int i = t; i < H_I * RB / 16; i += 256)
+    reinterpret_cast<uint4 *>(codes + qi * H_I * RB)[i] = reinterpret_cast<const uint4 *>(ql.codes)[i];
+  if (FMT == 2)
+    for (int i = t; i < H_I * 4; i += 256) scale_bytes[qi * H_I * 4 + i] = ql.sbytes[i];
+  if (t < H_I) factors[qi * H_I + t] = ql.f[t];
+}
+
 template <int FMT>
 __global__ void __launch_bounds__(256) index_query_prep_kernel(IndexArgs a) {
   __shared__ QueryLds ql;
@@ -701,9 +1325,9 @@ __global__ void __launch_bounds__(64 * kMultiQ, 2) index_score_multi_kernel(Inde
   uint32_t sc;
   {
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(static_cast<const uint8_t *>(a.k_codes) + row0 * RB), short(0), rows * RB, kRawBufferWord3);
+        const_cast<uint8_t *>(static_cast<const uint8_t *>(a.k_codes) + row0 * RB), short(0), rows * RB, kRawBufferDesc3);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(static_cast<const uint8_t *>(a.k_scales) + row0 * 4), short(0), rows * 4, kRawBufferWord3);
+        const_cast<uint8_t *>(static_cast<const uint8_t *>(a.k_scales) + row0 * 4), short(0), rows * 4, kRawBufferDesc3);
 #pragma unroll
     for (int l = 0; l < LPT; ++l)
       v[l] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, uint32_t((l * NT + tid) * 16), 0, 0));
@@ -790,234 +1414,13 @@ __global__ void __launch_bounds__(64 * kMultiQ, 2) index_score_multi_kernel(Inde
   if (lane == 0) { cand_count[out_slot] = base; cand_bound[out_slot] = bound; }
 }
 
-// ---- kernel 2: merge ----------------------------------------------------------------------
-struct alignas(16) MergeShared {
-  QueryLds ql;
-  float scores[kMaxTile];
-  uint64_t work[kMaxK + kMaxTile];
-  int counts[kMaxCand / 8];
-  uint64_t bounds[kMaxCand / 8];
-  SelectLds sel;
-  int tmp[16];
-  int flag;
-};
-
-// Sort P (a power of two) entry indices ascending in LDS.
-__device__ void bitonic_sort_u32(uint32_t *v, int P) {
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < P; i += blockDim.x) {
-        int ixj = i ^ j;
-        if (ixj > i) {
-          uint32_t x = v[i], y = v[ixj];
-          bool up = (i & k) == 0;
-          if ((x > y) == up) { v[i] = y; v[ixj] = x; }
-        }
-      }
-      lds_barrier();
-    }
-  }
-}
-
-// Exact fallback: the candidate set may miss winners hidden in tiles whose kept keys all beat
-// `tau`.  Keep a working set W (the k_eff best so far) in LDS and merge in every such tile,
-// re-scored from its keys.  Writes the final selection in ascending index order.
-template <int FMT, int KPT>
-__device__ void merge_fallback(const IndexArgs &a, MergeShared &sh, const uint64_t (&keys)[KPT], uint64_t tau,
-                               int64_t qi, int b, int64_t n_vis, int k_eff, int32_t *out) {
-  constexpr int NT = kMergeThreads;
-  const int tid = threadIdx.x;
-  const int tile = a.plan.tile, n_tiles = a.plan.n_tiles;
-  int wn;
-  {
-    int mine = 0;
-#pragma unroll
-    for (int k = 0; k < KPT; ++k) mine += (keys[k] != 0 && keys[k] >= tau);
-    int pos = block_excl_scan<NT>(mine, sh.tmp, wn);
-#pragma unroll
-    for (int k = 0; k < KPT; ++k)
-      if (keys[k] != 0 && keys[k] >= tau) sh.work[pos++] = keys[k];
-  }
-  lds_barrier();
-  QueryFrag<4> qf;
-  float *q_lds = reinterpret_cast<float *>(sh.ql.codes);
-  if (FMT == 0) {
-    const float *qsrc = static_cast<const float *>(a.q_idx) + qi * a.H_I * a.D_I;
-    for (int i = tid; i < a.H_I * a.D_I; i += NT) q_lds[i] = qsrc[i];
-    if (tid < a.H_I) sh.ql.f[tid] = a.w_idx[qi * a.H_I + tid];
-    lds_barrier();
-  } else {
-    QueryRaw raw;
-    load_query_raw(static_cast<const uint16_t *>(a.q_idx) + qi * a.H_I * 128, a.w_idx + qi * a.H_I, a.H_I, raw);
-    prep_query_lds<FMT>(raw, a.H_I, sh.ql);
-    lds_barrier();
-    load_query_frag<FMT, 4>(sh.ql, tid & 63, qf);
-  }
-  constexpr int KW = (kMaxK + kMaxTile) / NT;
-  for (int tl = 0; tl < n_tiles; ++tl) {
-    const uint64_t bt = sh.bounds[tl];
-    if (bt == 0 || bt <= tau) continue;                        // complete, or cannot hold winners
-    const int64_t e_begin = int64_t(tl) * tile;
-    const int vis = int(max(int64_t(0), min(int64_t(tile), n_vis - e_begin)));
-    const int64_t row0 = int64_t(b) * a.N_cap + e_begin;
-    if (FMT == 0) {
-      score_tile_f32(q_lds, sh.ql.f, a.H_I, a.D_I, static_cast<const float *>(a.k_codes), row0, tile, vis,
-                     sh.scores);
-    } else {
-      const int rows = int(min(int64_t(tile), a.N_cap - e_begin));
-      const TileKeys<FMT> tk = make_tile_keys<FMT>(a.k_codes, a.k_scales, row0, rows, tid & 63);
-      KeyFrag<FMT> ka[batch_of<FMT>()], kb[batch_of<FMT>()];
-      const int g_first = __builtin_amdgcn_readfirstlane(tid >> 6) * batch_of<FMT>();
-      load_batch<FMT>(tk, g_first, tid & 63, ka);
-      load_batch<FMT>(tk, g_first + (NT / 64) * batch_of<FMT>(), tid & 63, kb);
-      score_tile_mfma<FMT, 4>(qf, ka, kb, tk, tile, vis, sh.scores);
-    }
-    lds_barrier();
-    // append the tile's entries below its bound (the ones not already candidates) and above tau
-    int mine = 0;
-    for (int i = tid; i < vis; i += NT) {
-      const uint64_t key = make_key(sh.scores[i], uint32_t(e_begin + i));
-      mine += (key < bt && key > tau);
-    }
-    int total;
-    int pos = block_excl_scan<NT>(mine, sh.tmp, total) + wn;
-    for (int i = tid; i < vis; i += NT) {
-      const uint64_t key = make_key(sh.scores[i], uint32_t(e_begin + i));
-      if (key < bt && key > tau) sh.work[pos++] = key;
-    }
-    wn += total;
-    lds_barrier();
-    if (wn >= k_eff) {                                          // shrink W back to the k_eff best
-      uint64_t wk[KW];
-#pragma unroll
-      for (int k = 0; k < KW; ++k) {
-        const int i = tid * KW + k;
-        wk[k] = i < wn ? sh.work[i] : 0;
-      }
-      lds_barrier();
-      tau = block_select<NT, KW>(wk, k_eff, sh.sel);
-      int m2 = 0;
-#pragma unroll
-      for (int k = 0; k < KW; ++k) m2 += (wk[k] != 0 && wk[k] >= tau);
-      int tot2;
-      int p2 = block_excl_scan<NT>(m2, sh.tmp, tot2);
-#pragma unroll
-      for (int k = 0; k < KW; ++k)
-        if (wk[k] != 0 && wk[k] >= tau) sh.work[p2++] = wk[k];
-      wn = tot2;
-      lds_barrier();
-    }
-  }
-  // ascending indices
-  uint32_t *idx = reinterpret_cast<uint32_t *>(sh.work);
-  int P = 1;
-  while (P < wn) P <<= 1;
-  uint32_t tmpv[KW];
-#pragma unroll
-  for (int k = 0; k < KW; ++k) {
-    const int i = tid * KW + k;
-    tmpv[k] = i < wn ? key_index(sh.work[i]) : 0xffffffffu;
-  }
-  lds_barrier();
-#pragma unroll
-  for (int k = 0; k < KW; ++k) {
-    const int i = tid * KW + k;
-    if (i < P) idx[i] = tmpv[k];
-  }
-  lds_barrier();
-  bitonic_sort_u32(idx, P);
-  for (int i = tid; i < a.topk; i += NT) out[i] = i < wn ? int32_t(idx[i]) : -1;
-}
-
-template <int FMT, int KPT>
+// ---- kernel 2 (shared-tile path, very long caches): one workgroup per query merges -----------
+template <int FMT, int NHB>
 __global__ void __launch_bounds__(kMergeThreads) index_merge_kernel(IndexArgs a) {
-  __shared__ MergeShared sh;
-  constexpr int NT = kMergeThreads;
-  const int tid = threadIdx.x;
+  __shared__ IndexSharedT<kStreamSeg> sh;             // tiles or stream segments (the fallback rescans one)
   const int64_t qi = blockIdx.x;
   const int b = int(blockIdx.x / uint32_t(a.Sq)), s = int(blockIdx.x) - b * a.Sq;
-  const int cand = a.plan.cand, n_tiles = a.plan.n_tiles;
-  const int64_t n_q = int64_t(a.B) * a.Sq;
-  const uint64_t *cand_keys = static_cast<const uint64_t *>(a.workspace);
-  const uint64_t *cand_bound = cand_keys + n_q * n_tiles * cand;
-  const int *cand_count = reinterpret_cast<const int *>(cand_bound + n_q * n_tiles);
-  int32_t *out = a.topk_idx + qi * a.topk;
-
-  // candidate slots and per-tile counts are loaded together; slots past a tile's count are masked
-  uint64_t keys[KPT];
-  const int slots = n_tiles * cand;                            // a multiple of 8
-  if constexpr (KPT % 2 == 0) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(cand_keys + qi * slots + tid * KPT);
-#pragma unroll
-    for (int k = 0; k < KPT; k += 2) {
-      const uint4 v = tid * KPT + k < slots ? src[k / 2] : make_uint4(0, 0, 0, 0);
-      keys[k] = (uint64_t(v.y) << 32) | v.x;
-      keys[k + 1] = (uint64_t(v.w) << 32) | v.z;
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < KPT; ++k) {
-      const int slot = tid * KPT + k;
-      keys[k] = slot < slots ? cand_keys[qi * slots + slot] : 0;
-    }
-  }
-  // per-tile counts and bounds (n_tiles <= 2 NT), held in registers until the position is known
-  static_assert(kMaxCand / 8 <= 2 * NT, "two tiles' counts per thread");
-  // (loaded unconditionally from a clamped slot, so no branch separates the loads from the ones above)
-  int cnt[2];
-  uint64_t bnd[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = min(tid + j * NT, n_tiles - 1);
-    cnt[j] = cand_count[qi * n_tiles + i];
-    bnd[j] = cand_bound[qi * n_tiles + i];
-  }
-  // the query's position is read only now, while the candidate loads are in flight
-  __builtin_amdgcn_sched_barrier(0);
-  const int64_t t = a.q_pos0[b] + s;
-  const int64_t n_vis = min(a.n_entries[b], div_count(t + 1, a.m));
-  const int k_eff = int(min(int64_t(a.topk), n_vis));
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = tid + j * NT;
-    if (i < n_tiles) { sh.counts[i] = cnt[j]; sh.bounds[i] = bnd[j]; }
-  }
-  if (tid == 0) sh.flag = 0;
-  lds_barrier();
-  int nvalid_local = 0;
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const int slot = tid * KPT + k;
-    const int tl = slot / cand, j = slot - tl * cand;
-    if (slot >= slots || j >= sh.counts[tl]) keys[k] = 0;
-    nvalid_local += keys[k] != 0;
-  }
-  int nvalid;
-  (void)block_excl_scan<NT>(nvalid_local, sh.tmp, nvalid);
-  if (k_eff == 0) {
-    for (int i = tid; i < a.topk; i += NT) out[i] = -1;
-    return;
-  }
-  uint64_t tau = 0;                                            // k-th best candidate (0: need all)
-  if (nvalid >= k_eff) tau = block_select<NT, KPT>(keys, k_eff, sh.sel);
-  // a truncated tile whose smallest kept key beats tau may hold further winners
-  for (int i = tid; i < n_tiles; i += NT)
-    if (sh.bounds[i] != 0 && sh.bounds[i] > tau) sh.flag = 1;
-  lds_barrier();
-  if (sh.flag) {
-    merge_fallback<FMT, KPT>(a, sh, keys, tau, qi, b, n_vis, k_eff, out);
-    return;
-  }
-  int mine = 0;
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) mine += (keys[k] != 0 && keys[k] >= tau);
-  int total;
-  int pos = block_excl_scan<NT>(mine, sh.tmp, total);
-#pragma unroll
-  for (int k = 0; k < KPT; ++k)
-    if (keys[k] != 0 && keys[k] >= tau) out[pos++] = int32_t(key_index(keys[k]));
-  for (int i = k_eff + tid; i < a.topk; i += NT) out[i] = -1;
+  merge_query<FMT, NHB, kMergeThreads, kMaxCand / kMergeThreads>(a, sh, qi, b, s, false);
 }
 
 template <int FMT, int NHB>
@@ -1028,67 +1431,105 @@ hipError_t launch_score_t(const IndexArgs &a, hipStream_t stream) {
                stream, a);
     if (e != hipSuccess) return e;
     const dim3 mgrid(unsigned(a.plan.n_tiles), unsigned((a.Sq + kMultiQ - 1) / kMultiQ), unsigned(a.B));
-    return launch("index_score", index_score_multi_kernel<FMT, NHB>, mgrid, dim3(64 * kMultiQ), stream, a);
+    e = launch("index_score", index_score_multi_kernel<FMT, NHB>, mgrid, dim3(64 * kMultiQ), stream, a);
+    if (e != hipSuccess) return e;
+    return launch("index_merge", index_merge_kernel<FMT, NHB>, dim3(unsigned(int64_t(a.B) * a.Sq)),
+                  dim3(kMergeThreads), stream, a);
   }
-  dim3 grid(unsigned(a.plan.n_tiles), unsigned(int64_t(a.B) * a.Sq));
-  switch (a.plan.tile) {
-    case 64: case 128: case 256:
-      e = launch("index_score", index_score_kernel<FMT, NHB, 256, 1>, grid, dim3(256), stream, a); break;
-    case 512: e = launch("index_score", index_score_kernel<FMT, NHB, 256, 2>, grid, dim3(256), stream, a); break;
-    case 1024: e = launch("index_score", index_score_kernel<FMT, NHB, 512, 2>, grid, dim3(512), stream, a); break;
-    case 2048: e = launch("index_score", index_score_kernel<FMT, NHB, 512, 4>, grid, dim3(512), stream, a); break;
-    default: return hipErrorInvalidValue;
+  if (a.plan.stream) {
+    // one query segment per workgroup; the merge runs in the last segment workgroup of each query
+    // (fused), or for more than kFusedSlots candidate slots in a merge kernel after it
+    const dim3 sgrid(unsigned(a.plan.n_tiles), unsigned(int64_t(a.B) * a.Sq));
+    if constexpr (FMT != 0) {
+      if (a.plan.fused)
+        return launch("index_score", index_stream_kernel<FMT, NHB, true>, sgrid, dim3(kStreamThreads), stream, a);
+      e = launch("index_score", index_stream_kernel<FMT, NHB, false>, sgrid, dim3(kStreamThreads), stream, a);
+      if (e != hipSuccess) return e;
+      return launch("index_merge", index_merge_kernel<FMT, NHB>, dim3(unsigned(int64_t(a.B) * a.Sq)),
+                    dim3(kMergeThreads), stream, a);
+    }
+    return hipErrorInvalidValue;
   }
-  return e;
-}
-
-template <int FMT>
-hipError_t launch_merge_t(const IndexArgs &a, hipStream_t stream) {
-  hipError_t e = hipSuccess;
-  dim3 grid(unsigned(int64_t(a.B) * a.Sq));
-  const int slots = a.plan.n_tiles * a.plan.cand;
-  if (slots <= 512)
-    e = launch("index_merge", index_merge_kernel<FMT, 1>, grid, dim3(kMergeThreads), stream, a);
-  else if (slots <= 1024)
-    e = launch("index_merge", index_merge_kernel<FMT, 2>, grid, dim3(kMergeThreads), stream, a);
-  else if (slots <= 2048)
-    e = launch("index_merge", index_merge_kernel<FMT, 4>, grid, dim3(kMergeThreads), stream, a);
-  else if (slots <= 4096)
-    e = launch("index_merge", index_merge_kernel<FMT, 8>, grid, dim3(kMergeThreads), stream, a);
-  else
-    e = launch("index_merge", index_merge_kernel<FMT, 16>, grid, dim3(kMergeThreads), stream, a);
-  return e;
+  // one query per tile workgroup of 512 threads; the merge runs in the last tile workgroup of each
+  // query (fused), or for caches of more than 4,096 candidate slots in a merge kernel after it
+  if constexpr (FMT == 0) {
+    dim3 grid(unsigned(a.plan.n_tiles), unsigned(int64_t(a.B) * a.Sq));
+#define CSA_SCORE_LAUNCH(KPT, FUSE) \
+    e = launch("index_score", index_score_kernel<512, KPT, kFusedKeys, FUSE>, grid, dim3(512), stream, a)
+    const bool fuse = a.plan.fused != 0;
+    switch (a.plan.tile) {
+      case 64: case 128: case 256: case 512:
+        if (fuse) CSA_SCORE_LAUNCH(1, true); else CSA_SCORE_LAUNCH(1, false);
+        break;
+      case 1024:
+        if (fuse) CSA_SCORE_LAUNCH(2, true); else CSA_SCORE_LAUNCH(2, false);
+        break;
+      case 2048:
+        if (fuse) CSA_SCORE_LAUNCH(4, true); else CSA_SCORE_LAUNCH(4, false);
+        break;
+      default: return hipErrorInvalidValue;
+    }
+#undef CSA_SCORE_LAUNCH
+    if (e != hipSuccess || fuse) return e;
+    return launch("index_merge", index_merge_kernel<FMT, NHB>, dim3(unsigned(int64_t(a.B) * a.Sq)),
+                  dim3(kMergeThreads), stream, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
-IndexPlan plan_index(int64_t B, int64_t Sq, int64_t N_cap, int topk, int format) {
+IndexPlan plan_index(int64_t B, int64_t Sq, int64_t N_cap, int topk, int format, bool shared_tiles) {
   IndexPlan p;
   const int64_t n_queries = B * Sq;
   // many queries per sequence (a prefill chunk) with quantised keys: tiles of 512 shared by eight
   // queries (index_score_multi_kernel)
-  p.multi = (format != 0 && Sq >= kMultiQ && N_cap > kMultiTile && N_cap <= int64_t(kMaxCand / 8) * kMultiTile) ? 1 : 0;
-  int tile = kMaxTile;
-  if (p.multi) tile = kMultiTile;
-  while (!p.multi && tile > 64 && n_queries * ((N_cap + tile - 1) / tile) < 512) tile >>= 1;
-  while (!p.multi && tile > 64 && tile / 2 >= N_cap) tile >>= 1;
+  p.multi = (shared_tiles && format != 0 && Sq >= kMultiQ && N_cap > kMultiTile &&
+             N_cap <= int64_t(kMaxCand / 8) * kMultiTile) ? 1 : 0;
+  // otherwise quantised keys stream through one workgroup per segment, about one workgroup per CU
+  p.stream = (!p.multi && format != 0) ? 1 : 0;
+  int tile;
+  if (p.multi) {
+    tile = kMultiTile;
+  } else if (p.stream) {
+    const int ch = format == 1 ? chunk_entries<1>() : chunk_entries<2>();
+    const int64_t per_cu = (n_queries * N_cap + 255) / 256;
+    tile = ch;
+    while (tile < kStreamSeg && tile < per_cu && tile < N_cap) tile <<= 1;
+  } else {
+    tile = kMaxTile;
+    while (tile > 64 && n_queries * ((N_cap + tile - 1) / tile) < 512) tile >>= 1;
+    while (tile > 64 && tile / 2 >= N_cap) tile >>= 1;
+  }
   p.tile = tile;
   p.n_tiles = int((N_cap + tile - 1) / tile);
-  // keep ~4x the expected number of winners per tile, within the merge kernel's capacity
+  // keep ~4x the expected number of winners per tile, within what the merge holds: kFusedSlots in
+  // the tile workgroup that merges (kFusedKeys per thread), else kMaxCand in a merge kernel
   int64_t want = (4 * int64_t(topk) * tile + N_cap - 1) / N_cap;
   int cand = 8;
   while (cand < want && cand < tile) cand <<= 1;
   if (cand > tile) cand = tile;
-  while (int64_t(p.n_tiles) * cand > kMaxCand && cand > 8) cand >>= 1;
+  p.fused = (!p.multi && int64_t(p.n_tiles) * 8 <= kFusedSlots) ? 1 : 0;
+  const int64_t max_slots = p.fused ? kFusedSlots : kMaxCand;
+  while (int64_t(p.n_tiles) * cand > max_slots && cand > 8) cand >>= 1;
   p.cand = cand;
   return p;
 }
 
-size_t index_workspace_bytes(int64_t B, int64_t Sq, int64_t N_cap, int topk, int format) {
-  IndexPlan p = plan_index(B, Sq, N_cap, topk, format);
-  const int64_t slots = B * Sq * p.n_tiles;
+size_t index_workspace_bytes(int64_t B, int64_t Sq, int64_t N_cap, int topk, int format, bool shared_tiles) {
+  IndexPlan p = plan_index(B, Sq, N_cap, topk, format, shared_tiles);
   if (p.multi) return prepared_query_offset(B * Sq, p) + size_t(B * Sq) * sizeof(QueryLds) + 256;
-  return size_t(slots * p.cand * 8 + slots * 8 + slots * 4 + 256);
+  return arrivals_offset(B * Sq, p) + size_t(B * Sq) * kCounterStride * 4 + 256;
+}
+
+hipError_t launch_query_codes(const uint16_t *q, const float *w, int64_t n, int H_I, int format, void *codes,
+                              void *scale_bytes, float *factors, hipStream_t stream) {
+  if (format == 1)
+    return launch("query_codes", query_codes_kernel<1>, dim3(unsigned(n)), dim3(256), stream, q, w, H_I,
+                  static_cast<uint8_t *>(codes), static_cast<uint8_t *>(scale_bytes), factors);
+  return launch("query_codes", query_codes_kernel<2>, dim3(unsigned(n)), dim3(256), stream, q, w, H_I,
+                static_cast<uint8_t *>(codes), static_cast<uint8_t *>(scale_bytes), factors);
 }
 
 hipError_t launch_index_score(const IndexArgs &a, hipStream_t stream) {
@@ -1110,12 +1551,6 @@ hipError_t launch_index_score(const IndexArgs &a, hipStream_t stream) {
     }
   }
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_index_merge(const IndexArgs &a, hipStream_t stream) {
-  if (a.format == 0) return launch_merge_t<0>(a, stream);
-  if (a.format == 1) return launch_merge_t<1>(a, stream);
-  return launch_merge_t<2>(a, stream);
 }
 
 }  // namespace csa

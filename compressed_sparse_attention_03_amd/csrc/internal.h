@@ -49,16 +49,19 @@ hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t stream);
 
 // ---- lightning indexer + top-k -------------------------------------------------------------
 // The entry axis of every query is cut into tiles of `tile` entries.  The score kernel keeps, per
-// tile, the `cand` best (score, index) keys; the merge kernel selects the global top-k among all
-// tiles' candidates and re-scores any tile whose candidate list might have been too short.
+// tile, the `cand` best (score, index) keys; the merge selects the global top-k among all tiles'
+// candidates and re-scores any tile whose candidate list might have been too short.
 struct IndexPlan {
   int tile;        // entries per tile (multiple of 64)
   int cand;        // candidates kept per tile (power of two, <= tile)
   int n_tiles;     // tiles per query
   int multi;       // tiles shared by eight queries of a sequence (prefill-sized calls)
+  int stream;      // quantised keys: one workgroup streams a segment of `tile` entries of a query
+  int fused;       // one query per tile workgroup, merged by the query's last tile workgroup
 };
-IndexPlan plan_index(int64_t B, int64_t Sq, int64_t N_cap, int topk, int format);
-size_t index_workspace_bytes(int64_t B, int64_t Sq, int64_t N_cap, int topk, int format);
+// shared_tiles: allow the shared-tile path (it does not write full scores)
+IndexPlan plan_index(int64_t B, int64_t Sq, int64_t N_cap, int topk, int format, bool shared_tiles);
+size_t index_workspace_bytes(int64_t B, int64_t Sq, int64_t N_cap, int topk, int format, bool shared_tiles);
 
 struct IndexArgs {
   const void *q_idx;
@@ -72,8 +75,14 @@ struct IndexArgs {
   int64_t N_cap;
   IndexPlan plan;
 };
+// Every kernel of the call: the score kernel (which, on the one-query path, also merges each
+// query's candidates in its last tile workgroup), or on the shared-tile path the query
+// quantisation, the shared-tile score kernel and the merge kernel.  The workspace must hold zeros
+// where the arrival counters live before the first call; every call leaves them at zero.
 hipError_t launch_index_score(const IndexArgs &a, hipStream_t stream);
-hipError_t launch_index_merge(const IndexArgs &a, hipStream_t stream);
+// The indexer's query encoding alone (csa_quantize_query).
+hipError_t launch_query_codes(const uint16_t *q, const float *w, int64_t n, int H_I, int format, void *codes,
+                              void *scale_bytes, float *factors, hipStream_t stream);
 
 // ---- grouped output projection --------------------------------------------------------------
 struct ProjArgs {

@@ -27,6 +27,7 @@ I32, I64, F32, SZ = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_
 _SIGS = {
     "csa_compress": (I32, [P, P, P, P, I32, I64, I32, I32, I32, I32, I32, I64, F32, F32, P, P, P]),
     "csa_quantize_keys": (I32, [P, I64, I32, I32, P, P, P]),
+    "csa_quantize_query": (I32, [P, P, I64, I32, I32, P, P, P, P]),
     "csa_output_projection": (I32, [P, P, I32, I32, I32, I32, I32, P, P]),
     "csa_compress_index_keys": (I32, [P, P, P, I32, I64, I32, I32, I32, I32, I64, I32, P, P, P, P]),
     "csa_decode_append_index": (I32, [P, P, P, P, I32, I32, I32, I32, P, P, I64, I32, P, P, P, P]),
@@ -146,6 +147,26 @@ def csa_quantize_keys(x, fmt, codes_out=None, scales_out=None):
     st = lib().csa_quantize_keys(_ptr(x), rows, dim, f, _ptr(codes), _ptr(scales), _stream())
     _check(st, "csa_quantize_keys")
     return codes, scales
+
+
+def csa_quantize_query(q_idx, w_idx, fmt):
+    """The indexer's query encoding: q_idx bf16 [..., H_I, 128], w_idx fp32 [..., H_I] ->
+    (codes uint8 [..., H_I, 128 | 64], scale bytes uint8 [..., H_I, 4] or None, factors fp32 [..., H_I])."""
+    _dev(q_idx, "q_idx", torch.bfloat16)
+    _dev(w_idx, "w_idx", torch.float32)
+    H_I = q_idx.shape[-2]
+    if q_idx.shape[-1] != 128 or tuple(w_idx.shape) != tuple(q_idx.shape[:-1]):
+        raise ValueError("q_idx must be [..., H_I, 128] and w_idx [..., H_I]")
+    lead = tuple(q_idx.shape[:-2])
+    n = q_idx.numel() // (H_I * 128)
+    f = KEY_FORMATS[fmt]
+    codes = torch.empty(lead + (H_I, 128 if f == KEY_FP8_E4M3 else 64), dtype=torch.uint8, device=q_idx.device)
+    sb = torch.empty(lead + (H_I, 4), dtype=torch.uint8, device=q_idx.device) if f == KEY_MXFP4 else None
+    factors = torch.empty(lead + (H_I,), dtype=torch.float32, device=q_idx.device)
+    st = lib().csa_quantize_query(_ptr(q_idx), _ptr(w_idx), n, H_I, f, _ptr(codes), _ptr(sb), _ptr(factors),
+                                  _stream())
+    _check(st, "csa_quantize_query")
+    return codes, sb, factors
 
 
 def _key_cache_shapes(lead, D_I, f):
@@ -277,7 +298,7 @@ def csa_decode_append(c_new, z_new, pos, bias, *, m, overlap, rope_dim, tok_c, t
 
 def index_topk_workspace(B, Sq, N_cap, topk, device="cuda"):
     n = lib().csa_index_topk_workspace_bytes(B, Sq, N_cap, topk)
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)     # zero once: it holds counters
 
 
 def csa_index_topk(q_idx, w_idx, k_codes, k_scales, *, key_format, n_entries, q_pos0, m, topk,
@@ -309,12 +330,12 @@ def csa_index_topk(q_idx, w_idx, k_codes, k_scales, *, key_format, n_entries, q_
 
 def attend_workspace(B, Sq, H, D, topk, window, device="cuda"):
     n = lib().csa_attend_workspace_bytes(B, Sq, H, D, topk, window)
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)     # zero once: it holds counters
 
 
 def hca_workspace(B, Sq, H, D, N_cap, window, device="cuda"):
     n = lib().hca_attend_workspace_bytes(B, Sq, H, D, N_cap, window)
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)     # zero once: it holds counters
 
 
 def _attend_common(q, entries, win_rows, win_pos0, q_pos0, q_norm_w):

@@ -29,6 +29,10 @@
  *     without a synchronisation; out-of-range values are undefined behaviour.
  *   - Workspace is caller-provided device memory of at least the size the matching
  *     *_workspace_bytes() function returns; two calls that run concurrently must not share it.
+ *     It must be zero-filled once before its first use: it holds counters through which the
+ *     last workgroup of a query learns that the others are done, and every completed call leaves
+ *     them at zero again (a call that was launched but did not complete -- a fault -- may leave
+ *     them non-zero: zero the workspace again before reusing it).
  *   - Results are deterministic: fixed reduction orders, no floating-point atomics.
  */
 #ifndef CSA_H
@@ -178,6 +182,24 @@ csa_status csa_quantize_keys(const uint16_t *x, int64_t rows, int dim, int forma
                              void *scales, void *stream);
 
 /*
+ * csa_quantize_query -- the lightning indexer's query encoding on its own: what csa_index_topk
+ * scores with, exposed so that it can be checked bit for bit.
+ * [DEVTO] "Two Compression Strategies": the indexer runs in low precision (FP4); the query is put
+ * in the keys' format so the products run on the low-precision matrix units.
+ *
+ *   q_idx     bf16 [n, H_I, 128] query heads; w_idx fp32 [n, H_I] head weights.
+ *   key_format CSA_KEY_FP8_E4M3: codes uint8 [n, H_I, 128] by csa_quantize_keys's row rule (one
+ *             power-of-two scale 2^e per head row); scale_bytes unused (may be NULL);
+ *             factors fp32 [n, H_I] = w * 2^e.
+ *             CSA_KEY_MXFP4: codes uint8 [n, H_I, 64] (two e2m1 codes per byte, element 2j in the
+ *             low nibble) by csa_quantize_keys's MX rule; scale_bytes uint8 [n, H_I, 4] (e8m0 per 32
+ *             values); factors fp32 [n, H_I] = w.
+ * Limits: H_I in {16, 32, 48, 64}; 0 <= n <= 65535.
+ */
+csa_status csa_quantize_query(const uint16_t *q_idx, const float *w_idx, int64_t n, int H_I, int key_format,
+                              void *codes, void *scale_bytes, float *factors, void *stream);
+
+/*
  * csa_index_topk -- lightning-indexer scores and per-query top-k selection.
  * [EXPLAINER] CSA walk-through: a lightweight scoring head rates each compressed block for the
  * present query and only the k highest-rated blocks are kept; [RABBIT] indexer paragraph: of some
@@ -201,6 +223,9 @@ csa_status csa_quantize_keys(const uint16_t *x, int64_t rows, int dim, int forma
  *              the rest -inf (for inspection; it adds traffic).
  * Limits: 1 <= topk <= 2048; fp8/MXFP4 need D_I == 128 and H_I in {16, 32, 48, 64}; fp32 needs
  * H_I * D_I <= 2048 with D_I % 4 == 0; 1 <= N_cap <= 2^21; m >= 1.
+ * Kernels: one launch per call on the one-query-per-workgroup path (scores per tile, and the
+ * top-k merge in the last tile workgroup of each query to finish); three when many queries share a
+ * sequence (prefill) or a cache holds more than about a million entries.
  */
 csa_status csa_index_topk(const void *q_idx, const float *w_idx, const void *k_codes,
                           const void *k_scales, int key_format, int B, int Sq, int H_I, int D_I,

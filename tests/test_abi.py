@@ -218,3 +218,13 @@ def test_stream_read_rejects_bad_arguments():
     assert L.csa_measure_stream_read(None, 1024, v, None) == 1
     assert L.csa_measure_stream_read(ctypes.c_void_p(8), 1024, v, None) == 1   # src misaligned
     assert L.csa_measure_stream_read(v, 1024, None, None) == 1
+
+
+def test_quantize_query_rejects_bad_arguments():
+    L = ops.lib()
+    v = ctypes.c_void_p(16)
+    assert L.csa_quantize_query(v, v, 4, 64, 0, v, v, v, None) == 1       # fp32 is not a code format
+    assert L.csa_quantize_query(v, v, 4, 40, 1, v, None, v, None) == 1    # H_I not a multiple of 16
+    assert L.csa_quantize_query(v, v, 4, 64, 2, v, None, v, None) == 1    # MXFP4 needs scale bytes
+    assert L.csa_quantize_query(None, v, 4, 64, 1, v, None, v, None) == 1
+    assert L.csa_quantize_query(None, None, 0, 64, 1, None, None, None, None) == 0

@@ -1,6 +1,7 @@
 """bench.py's host side, on the CPU: a request for more than one GPU exits with a message; the
 algorithmic byte counts are the sums of what one step must touch; the committed traffic summary is
 used only while it matches the kernel source; the trace and MFMA summarisers read rocprofv3 tables."""
+import hashlib
 import os
 import shutil
 import sqlite3
@@ -40,22 +41,22 @@ def test_algorithmic_bytes_of_the_decode_steps():
 
 
 def test_traffic_summary_follows_the_kernel_source(tmp_path, monkeypatch):
+    # a summary taken on the current kernel source is used; the same summary beside a source that
+    # differs from the one it was taken on is ignored
     name = "index_score_csa_decode_1m_b4_mxfp4_pmc.txt"
-    if not os.path.exists(os.path.join(ROOT, "profiles", name)):
-        pytest.skip("no committed traffic summary")
-    assert bench.profile_traffic("index_score", "csa_decode_1m_b4_mxfp4") > bench.index_score_bytes(
-        gen.CSA_DECODE_1M) * 0.9
-    # the same summary beside a kernel source that differs from the one it was taken on
+    src = open(os.path.join(ROOT, "compressed_sparse_attention_03_amd", "csrc", "indexer.hip")).read()
+    sha = hashlib.sha256(src.encode()).hexdigest()[:16]
     (tmp_path / "profiles").mkdir()
-    shutil.copy(os.path.join(ROOT, "profiles", name), tmp_path / "profiles" / name)
+    (tmp_path / "profiles" / name).write_text(
+        f"kernel = index_score_kernel\nsource = indexer.hip\nsource_sha256_16 = {sha}\n"
+        "traffic_bytes_per_dispatch = 72306425\n")
     csrc = tmp_path / "compressed_sparse_attention_03_amd" / "csrc"
     csrc.mkdir(parents=True)
-    src = open(os.path.join(ROOT, "compressed_sparse_attention_03_amd", "csrc", "indexer.hip")).read()
-    (csrc / "indexer.hip").write_text(src + "\n// changed\n")
-    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    assert bench.profile_traffic("index_score", "csa_decode_1m_b4_mxfp4") is None
     (csrc / "indexer.hip").write_text(src)
-    assert bench.profile_traffic("index_score", "csa_decode_1m_b4_mxfp4") is not None
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.profile_traffic("index_score", "csa_decode_1m_b4_mxfp4") == 72306425.0
+    (csrc / "indexer.hip").write_text(src + "\n// changed\n")
+    assert bench.profile_traffic("index_score", "csa_decode_1m_b4_mxfp4") is None
 
 
 def test_summarize_trace_reads_a_kernel_table(tmp_path):

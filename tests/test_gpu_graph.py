@@ -1,6 +1,8 @@
 """The decode step replayed from a captured HIP graph (as the benchmark times it): every replay,
 with eager library calls and poisoned outputs in between, gives the bits of the eager call.  The
-library records no memset nodes; its workspaces carry nothing from one call to the next."""
+library records no memset nodes; the only state its workspaces carry from one call to the next
+are the arrival counters, which every completed call leaves at zero (so replays, which share the
+eager calls' workspace here, must keep working)."""
 import numpy as np
 import pytest
 import torch

@@ -69,7 +69,7 @@ def test_tiny_fp32_all_queries():
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
-@pytest.mark.parametrize("H_I", [64, 32, 16])
+@pytest.mark.parametrize("H_I", [64, 48, 32, 16])
 def test_small_shapes_ragged(fmt, H_I):
     B, N = 2, 1000                       # N not a multiple of the tile or of 16
     q = gen.normal_bf16(60, 0, (B * H_I, 128)).reshape(B, 1, H_I, 128)
@@ -103,7 +103,8 @@ def _both_paths(q, w, k, fmt, m, topk, t_first, n_entries, tag, sample=None):
     return sel_shared
 
 
-@pytest.mark.parametrize("fmt,H_I", [("fp8", 64), ("mxfp4", 64), ("fp8", 16), ("mxfp4", 32)])
+@pytest.mark.parametrize("fmt,H_I", [("fp8", 64), ("mxfp4", 64), ("fp8", 16), ("mxfp4", 32), ("fp8", 48),
+                                     ("mxfp4", 48)])
 def test_shared_key_tiles_for_many_queries(fmt, H_I):
     # 37 queries per sequence (not a multiple of 8), causal visibility from 25 entries up, a cache
     # that ends inside a tile and a sequence with fewer valid entries than its capacity
@@ -158,29 +159,36 @@ def test_long_cache_with_few_visible_takes_the_fallback():
     run_quantised(q, w, k, "fp8", 4, 1024, [4 * 3000 - 1], tag="long-few", check_scores=False)
 
 
-def _decode_case(wl, n_seq=None):
+def _decode_case(wl, n_seq=None, scores=True):
     n_seq = wl.B if n_seq is None else n_seq
     x = gen.decode_inputs(wl, 0, n_seq, parts=("index",))
     planted = gen.planted_indices(wl)[:n_seq] if wl.n_planted else None
     return run_quantised(x["q_idx"], x["w_idx"], x["k_idx"], wl.key_format, wl.m, wl.topk,
-                         x["t"], n_entries=x["n_entries"], tag=wl.name, check_scores=True, planted=planted)
+                         x["t"], n_entries=x["n_entries"], tag=wl.name + ("" if scores else " (no scores)"),
+                         check_scores=scores, planted=planted)
 
 
-def test_csa_decode_32k_full():
-    _decode_case(gen.CSA_DECODE_32K)
+# Each decode configuration twice: with the scores written (compared with the oracle's element by
+# element) and without (the call the benchmark times), its selection held to the oracle's scores.
+@pytest.mark.parametrize("scores", [True, False])
+def test_csa_decode_32k_full(scores):
+    _decode_case(gen.CSA_DECODE_32K, scores=scores)
 
 
-def test_csa_decode_128k_full():
-    _decode_case(gen.CSA_DECODE_128K)
+@pytest.mark.parametrize("scores", [True, False])
+def test_csa_decode_128k_full(scores):
+    _decode_case(gen.CSA_DECODE_128K, scores=scores)
 
 
-def test_csa_decode_1m_mxfp4_planted_full():
-    _decode_case(gen.CSA_DECODE_1M)
+@pytest.mark.parametrize("scores", [True, False])
+def test_csa_decode_1m_mxfp4_planted_full(scores):
+    _decode_case(gen.CSA_DECODE_1M, scores=scores)
 
 
-def test_csa_decode_1m_flash_topk512_full():
+@pytest.mark.parametrize("scores", [True, False])
+def test_csa_decode_1m_flash_topk512_full(scores):
     # the Flash configuration: attention top-k 512 at the maximum context
-    _decode_case(gen.CSA_DECODE_1M_FLASH)
+    _decode_case(gen.CSA_DECODE_1M_FLASH, scores=scores)
 
 
 def test_prefill_chunk_full_size_sampled():
