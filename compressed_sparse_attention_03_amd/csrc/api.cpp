@@ -423,6 +423,34 @@ csa_status csa_attend(const uint16_t *q, const uint16_t *q_norm_w, const uint16_
   return run_attend(a, stream);
 }
 
+csa_status csa_attend_noalloc(const uint16_t *q, const uint16_t *q_norm_w, const uint16_t *entries,
+                              int64_t N_cap, const int32_t *topk_idx, int topk, const uint16_t *win_rows,
+                              int64_t W_cap, const int64_t *win_pos0, const int64_t *q_pos0, int B, int Sq,
+                              int H, int D, int rope_dim, int window, float softmax_scale, float rope_base,
+                              float eps, uint16_t *out, float *lse, void *stream) {
+  csa_status s = check_attend_common(q, q_norm_w, entries, N_cap, win_rows, W_cap, win_pos0, q_pos0, B,
+                                     Sq, H, D, rope_dim, window, softmax_scale, rope_base, eps, out, lse);
+  if (s != CSA_OK || B == 0 || Sq == 0) return s;
+  REQUIRE(topk >= 1 && topk <= 2048, "topk must be in [1, 2048]");
+  REQUIRE_PTR(topk_idx);
+  const size_t need = csa::attend_workspace_bytes(int64_t(B) * Sq, H, D, topk, window);
+  if (need > csa::attend_scratch_bytes())
+    return fail(CSA_ERR_WORKSPACE, "csa_attend_noalloc needs %zu scratch bytes for this shape; its scratch holds %zu",
+                need, csa::attend_scratch_bytes());
+  void *ws = nullptr;
+  hipError_t e = csa::attend_scratch(&ws);
+  if (e != hipSuccess) return fail(CSA_ERR_HIP, "scratch address: %s", hipGetErrorString(e));
+  csa::AttendArgs a{};
+  a.q = q; a.q_norm_w = q_norm_w; a.entries = entries; a.win_rows = win_rows; a.topk_idx = topk_idx;
+  a.n_entries = nullptr; a.win_pos0 = win_pos0; a.q_pos0 = q_pos0; a.out = out; a.lse = lse;
+  a.workspace = ws; a.N_cap = N_cap; a.W_cap = W_cap; a.n_sel = topk; a.B = B; a.Sq = Sq;
+  a.H = H; a.D = D; a.rope_dim = rope_dim; a.window = window; a.m = 1;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f; a.log2_base = std::log2(double(rope_base));
+  a.eps = eps;
+  a.plan = csa::plan_attend(int64_t(B) * Sq, H, topk, window, D);
+  return run_attend(a, stream);
+}
+
 csa_status hca_attend(const uint16_t *q, const uint16_t *q_norm_w, const uint16_t *entries,
                       int64_t N_cap, const int64_t *n_entries, int m, const uint16_t *win_rows,
                       int64_t W_cap, const int64_t *win_pos0, const int64_t *q_pos0, int B, int Sq,

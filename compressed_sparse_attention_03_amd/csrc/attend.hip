@@ -20,6 +20,8 @@
 //                                                   transposing LDS read of the staged rows
 // Each wave writes its channels of the slice's normalised fp32 partial; wave 0 writes the slice's
 // log2-sum-exp, and a combine kernel merges the slices in a fixed order.
+#include <mutex>
+
 #include "common.h"
 #include "internal.h"
 
@@ -551,6 +553,36 @@ size_t attend_workspace_bytes(int64_t n_queries, int H, int D, int64_t n_sel, in
   AttendPlan p = plan_attend(n_queries, H, n_sel, window, D);
   if (p.n_splits == 1 || p.fused) return 256;
   return size_t(n_queries * H * p.n_splits * (int64_t(D) + 1) * 4 + 256);
+}
+
+// ---- the library's own scratch for csa_attend_noalloc -------------------------------------------
+// One file-scope device array (each GPU the library runs on holds its own copy from module load to
+// process exit).  Host code never passes the array's name to a kernel: its device address on the
+// current device comes from hipGetSymbolAddress, taken once per device and kept.
+namespace {
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+size_t attend_scratch_bytes() { return kScratchBytes; }
+
+hipError_t attend_scratch(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream) {

@@ -122,6 +122,10 @@ struct AttendArgs {
 };
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream);
 hipError_t launch_combine(const AttendArgs &a, hipStream_t stream);
+// The library's scratch array for csa_attend_noalloc: its size, and its device address on the
+// current device (looked up once per device).
+size_t attend_scratch_bytes();
+hipError_t attend_scratch(void **ptr);
 
 // Plain streaming read of `bytes` (a positive multiple of 16) at `src` (measure.hip).
 hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t stream);

@@ -38,6 +38,8 @@ _SIGS = {
     "csa_attend": (I32, [P, P, P, I64, P, I32, P, I64, P, P, I32, I32, I32, I32, I32, I32, F32, F32,
                          F32, P, P, P, SZ, P]),
     "csa_attend_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
+    "csa_attend_noalloc": (I32, [P, P, P, I64, P, I32, P, I64, P, P, I32, I32, I32, I32, I32, I32, F32, F32,
+                                 F32, P, P, P]),
     "hca_attend": (I32, [P, P, P, I64, P, I32, P, I64, P, P, I32, I32, I32, I32, I32, I32, F32, F32,
                          F32, P, P, P, SZ, P]),
     "hca_attend_workspace_bytes": (SZ, [I32, I32, I32, I32, I64, I32]),
@@ -369,6 +371,28 @@ def csa_attend(q, entries, topk_idx, win_rows, win_pos0, q_pos0, *, rope_dim, wi
                           _stream())
     _check(st, "csa_attend")
     return o, ls
+
+
+def csa_attend_noalloc(q, entries, topk_idx, win_rows, win_pos0, q_pos0, *, rope_dim, window, q_norm_w=None,
+                       softmax_scale=None, rope_base=10000.0, eps=1e-6, out, lse=None):
+    """csa_attend with the library's own scratch (no workspace): ``out`` (and ``lse`` if wanted)
+    must be given, so the call itself allocates nothing."""
+    B, Sq, H, D = _attend_common(q, entries, win_rows, win_pos0, q_pos0, q_norm_w)
+    _dev(topk_idx, "topk_idx", torch.int32, 3)
+    _dev(out, "out", torch.bfloat16, 4)
+    if tuple(out.shape) != (B, Sq, H, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, Sq, H, D] tensor")
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, 3)
+        if tuple(lse.shape) != (B, Sq, H) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous [B, Sq, H] tensor")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
+    st = lib().csa_attend_noalloc(_ptr(q), _ptr(q_norm_w), _ptr(entries), entries.shape[1], _ptr(topk_idx),
+                                  topk_idx.shape[2], _ptr(win_rows), win_rows.shape[1], _ptr(win_pos0), _ptr(q_pos0),
+                                  B, Sq, H, D, rope_dim, window, scale, rope_base, eps, _ptr(out), _ptr(lse),
+                                  _stream())
+    _check(st, "csa_attend_noalloc")
+    return out, lse
 
 
 def hca_attend(q, entries, n_entries, win_rows, win_pos0, q_pos0, *, m, rope_dim, window, q_norm_w=None,

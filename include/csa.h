@@ -270,6 +270,23 @@ csa_status csa_attend(const uint16_t *q, const uint16_t *q_norm_w, const uint16_
 size_t csa_attend_workspace_bytes(int B, int Sq, int H, int D, int topk, int window);
 
 /*
+ * csa_attend_noalloc -- csa_attend for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same kernels, with the
+ * split-K partials in a scratch array the library holds on each GPU (32 MiB, from module load until
+ * the process ends) instead of a caller workspace.  Arguments and results as csa_attend.
+ * The call allocates nothing.  Shapes whose partials need more than the scratch holds
+ * (csa_attend_workspace_bytes() > 32 MiB) return CSA_ERR_WORKSPACE before any HIP call.  Every
+ * call on a GPU uses that GPU's one scratch array: calls that overlap on one GPU (concurrent
+ * streams or threads) race and must be serialised by the caller.  A call rewrites every scratch
+ * byte it reads, so nothing needs clearing between calls.
+ */
+csa_status csa_attend_noalloc(const uint16_t *q, const uint16_t *q_norm_w, const uint16_t *entries,
+                              int64_t N_cap, const int32_t *topk_idx, int topk, const uint16_t *win_rows,
+                              int64_t W_cap, const int64_t *win_pos0, const int64_t *q_pos0, int B, int Sq,
+                              int H, int D, int rope_dim, int window, float softmax_scale, float rope_base,
+                              float eps, uint16_t *out, float *lse, void *stream);
+
+/*
  * hca_attend -- HCA core attention: dense over every visible compressed entry plus the window.
  * [EXPLAINER] HCA walk-through: no selection step -- each query sees every compressed entry
  * (ordinary multi-query attention, over a far shorter sequence) together with a short window of

@@ -228,3 +228,17 @@ def test_quantize_query_rejects_bad_arguments():
     assert L.csa_quantize_query(v, v, 4, 64, 2, v, None, v, None) == 1    # MXFP4 needs scale bytes
     assert L.csa_quantize_query(None, v, 4, 64, 1, v, None, v, None) == 1
     assert L.csa_quantize_query(None, None, 0, 64, 1, None, None, None, None) == 0
+
+
+def test_attend_noalloc_rejects_shapes_beyond_its_scratch():
+    # 16 decode queries of 128 heads x 512 over 2,048 + 128 rows run split-K with 56 MiB of
+    # partials, more than the 32 MiB scratch; the check happens on the host before any HIP call
+    # (nothing is launched, no device needed)
+    L = ops.lib()
+    v = ctypes.c_void_p(16)
+    need = L.csa_attend_workspace_bytes(16, 1, 128, 512, 2048, 128)
+    assert need > (32 << 20)
+    st = L.csa_attend_noalloc(v, None, v, 8192, v, 2048, v, 128, v, v, 16, 1, 128, 512, 64, 128,
+                              ctypes.c_float(0.044), ctypes.c_float(10000.0), ctypes.c_float(1e-6), v, None, None)
+    assert st == 3
+    assert b"scratch" in L.csa_last_error()
