@@ -19,6 +19,16 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// A workgroup barrier after which every wave's LDS writes are visible, without waiting for the
+// wave's global loads still in flight (the memory-model fence of lds_barrier makes the compiler
+// wait for those as well): each wave's LDS operations have completed (lgkmcnt 0) when it arrives.
+__device__ __forceinline__ void lds_sync() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---- hand-over between the workgroups of one launch -------------------------------------------
 // Several kernels let the last of a group of workgroups to finish (decided by a device-scope atomic
 // counter) combine what the others produced.  The handed-over values are written and read with the

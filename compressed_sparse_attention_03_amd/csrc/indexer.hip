@@ -609,6 +609,134 @@ __device__ __forceinline__ uint64_t block_cut_bucket(const uint64_t (&keys)[KPT]
   return block_cut<NT, KPT>(keys, need, keep_min, sl);
 }
 
+// ---- tile cut from the score distribution --------------------------------------------------
+// z with P(Z > z) = p for a standard normal Z, 0 < p <= 1/2: the rational approximation of
+// Abramowitz and Stegun, Handbook of Mathematical Functions, formula 26.2.23 (|error| < 4.5e-4).
+__device__ __forceinline__ float normal_upper_quantile(float p) {
+  const float t = sqrtf(-2.0f * __logf(p));
+  return t - (2.515517f + t * (0.802853f + t * 0.010328f)) / (1.0f + t * (1.432788f + t * (0.189269f + t * 0.001308f)));
+}
+
+// Sum over the wave's 64 lanes, in lane 63 (inclusive DPP scan, then the row broadcasts).
+__device__ __forceinline__ float wave_total_f32(float v) {
+  v += __int_as_float(dpp<kDppRowShr + 1>(__float_as_int(v)));
+  v += __int_as_float(dpp<kDppRowShr + 2>(__float_as_int(v)));
+  v += __int_as_float(dpp<kDppRowShr + 4>(__float_as_int(v)));
+  v += __int_as_float(dpp<kDppRowShr + 8>(__float_as_int(v)));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
+  return v;
+}
+
+// A tile's candidates: its entries whose scores reach a cut that keeps between cand / 2 and cand
+// of them (all of them when at most cand are visible), written in entry order as keys to `dst`
+// with coherent stores, then their count and the cut (0: nothing cut) for the merge.  The tile's
+// scores are sums over many heads, so their upper tail is close to normal: each wave's mean and
+// mean absolute deviation about it (a spread one extreme score -- a planted or duplicated key --
+// barely moves) place the score ranked 3 cand / 4 near mean + z sd, sd = sqrt(pi / 2) x deviation;
+// four thresholds from 0.15 sd below to 0.45 sd above it (the ReLU sums' tail is heavier than a
+// normal one with the same deviation, so the range leans upward) are counted in one pass, with the
+// positions every kept entry takes, and the highest threshold that keeps between cand / 2 and
+// cand entries is the cut: two barriers in all.  When none does (a tail far from normal), the histogram cut decides.  Which threshold is
+// taken changes only how many candidates the tile hands to the merge, never which entries win.
+// Scores: KPT consecutive entries per thread in `scores` (LDS); entries past vis are ignored.
+template <int NT, int KPT>
+__device__ __forceinline__ void publish_candidates(const float *scores, int vis, int64_t e_begin, int cand,
+                                                   uint64_t *dst, int *count_out, uint64_t *bound_out, BucketLds &bl,
+                                                   SelectLds &sl, int *tmp) {
+  constexpr int NW = NT / 64;
+  static_assert(NW <= 8 && NT * KPT < 65536, "per-wave sums in bl.wsum, 16-bit counts");
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int keep_min = cand / 2;
+  float x[KPT];
+  uint32_t o[KPT];                                 // score order; 0 for an entry past vis
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int i = tid * KPT + k;
+    x[k] = scores[i];
+    o[k] = i < vis ? score_order(x[k]) : 0u;
+  }
+  auto key_of = [&](int k) { return (uint64_t(o[k]) << 32) | uint64_t(~uint32_t(e_begin + tid * KPT + k)); };
+  uint64_t bound = 0;                              // keep the entries whose keys reach it
+  int pos = 0, total = 0;
+  bool done = false;
+  if (vis > cand) {
+    // this wave's mean, then its summed absolute deviation about that mean
+    const int n_w = min(max(vis - wave * 64 * KPT, 0), 64 * KPT);
+    float s1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) s1 += o[k] != 0 ? x[k] : 0.f;
+    s1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_total_f32(s1)), 63));
+    const float m_w = n_w > 0 ? s1 / float(n_w) : 0.f;
+    float d1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) d1 += o[k] != 0 ? fabsf(x[k] - m_w) : 0.f;
+    d1 = wave_total_f32(d1);
+    if (lane == 63) bl.kmin[wave] = (uint64_t(__float_as_uint(d1)) << 32) | __float_as_uint(s1);
+    lds_barrier();
+    float sum = 0.f, dev = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint64_t v = bl.kmin[w];
+      sum += __uint_as_float(uint32_t(v));
+      dev += __uint_as_float(uint32_t(v >> 32));
+    }
+    const float inv_n = 1.0f / float(vis);
+    const float mean = sum * inv_n, sd = 1.2533141f * dev * inv_n;
+    const float z = normal_upper_quantile(fminf(0.5f, 0.5f * float(cand + keep_min) * inv_n));
+    uint32_t th[4];
+    const float dz[4] = {0.45f, 0.25f, 0.05f, -0.15f};         // highest threshold first
+#pragma unroll
+    for (int j = 0; j < 4; ++j) th[j] = score_order(fmaf(z + dz[j], sd, mean));
+    // the four counts in two words (16 bits each), their wave prefixes and totals
+    uint32_t c01 = 0, c23 = 0;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      c01 += (o[k] >= th[0] ? 1u : 0u) + (o[k] >= th[1] ? 0x10000u : 0u);
+      c23 += (o[k] >= th[2] ? 1u : 0u) + (o[k] >= th[3] ? 0x10000u : 0u);
+    }
+    const uint32_t i01 = uint32_t(wave_scan_bcast(int(c01))), i23 = uint32_t(wave_scan_bcast(int(c23)));
+    if (lane == 63) { bl.wsum[wave] = int(i01); bl.wsum[8 + wave] = int(i23); }
+    lds_barrier();
+    uint32_t t01 = 0, t23 = 0, p01 = 0, p23 = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t v01 = uint32_t(bl.wsum[w]), v23 = uint32_t(bl.wsum[8 + w]);
+      t01 += v01; t23 += v23;
+      if (w < wave) { p01 += v01; p23 += v23; }
+    }
+    const uint32_t tot[4] = {t01 & 0xffffu, t01 >> 16, t23 & 0xffffu, t23 >> 16};
+    int pick = -1;
+#pragma unroll
+    for (int j = 3; j >= 0; --j)
+      if (int(tot[j]) >= keep_min) pick = j;                   // the highest threshold keeping enough
+    if (pick >= 0 && int(tot[pick]) <= cand && th[pick] != 0) {
+      const uint32_t pre01 = p01 + i01 - c01, pre23 = p23 + i23 - c23;   // entries kept before mine
+      const uint32_t pre = pick == 0 ? (pre01 & 0xffffu) : pick == 1 ? (pre01 >> 16)
+                         : pick == 2 ? (pre23 & 0xffffu) : (pre23 >> 16);
+      bound = uint64_t(th[pick]) << 32;                       // keys >= it: orders >= th[pick]
+      pos = int(pre);
+      total = int(tot[pick]);
+      done = true;
+    } else {
+      uint64_t keys[KPT];
+#pragma unroll
+      for (int k = 0; k < KPT; ++k) keys[k] = o[k] != 0 ? key_of(k) : 0;
+      bound = block_cut_bucket<NT, KPT>(keys, cand, keep_min, bl, sl);
+    }
+  }
+  if (!done) {                                     // positions by a block scan
+    int mine = 0;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) mine += (o[k] != 0 && key_of(k) >= bound);
+    pos = block_excl_scan<NT>(mine, tmp, total);
+  }
+#pragma unroll
+  for (int k = 0; k < KPT; ++k)
+    if (o[k] != 0 && key_of(k) >= bound) store_coherent(&dst[pos++], key_of(k));
+  if (tid == 0) { store_coherent(count_out, total); store_coherent(bound_out, bound); }
+}
+
 // Exact rank-`need` (1 = largest) key among the block's non-zero keys.
 template <int NT, int KPT>
 __device__ __forceinline__ uint64_t block_select(const uint64_t (&keys)[KPT], int need, BucketLds &bl, SelectLds &sl) {
@@ -886,29 +1014,8 @@ __global__ void __launch_bounds__(NT) index_score_kernel(IndexArgs a) {
       for (int i = threadIdx.x; i < tile; i += NT)
         if (e_begin + i < a.N_cap) dst[e_begin + i] = sh.scores[i];
     }
-    // keys of this thread's KPT consecutive entries
-    uint64_t keys[KPT];
-#pragma unroll
-    for (int k = 0; k < KPT; ++k) {
-      const int i = threadIdx.x * KPT + k;
-      keys[k] = i < vis ? make_key(sh.scores[i], uint32_t(e_begin + i)) : 0;
-    }
-    uint64_t bound = 0;
-    // keep the tile's largest keys: all `cand` of them, or at least half as many when one histogram
-    // pass already separates them (the merge checks every truncated tile's bound against its
-    // threshold and rescans the tile when the bound is not below it)
-    if (vis > cand) bound = block_cut_bucket<NT, KPT>(keys, cand, cand / 2, sh.bl, sh.sel);
-    int mine = 0;
-#pragma unroll
-    for (int k = 0; k < KPT; ++k) mine += (keys[k] != 0 && keys[k] >= bound);
-    int total;
-    int pos = block_excl_scan<NT>(mine, sh.tmp, total);
-    // coherent stores: the merging workgroup reads them back in the same launch
-    uint64_t *dst = cand_keys + out_slot * cand;
-#pragma unroll
-    for (int k = 0; k < KPT; ++k)
-      if (keys[k] != 0 && keys[k] >= bound) store_coherent(&dst[pos++], keys[k]);
-    if (threadIdx.x == 0) { store_coherent(&cand_count[out_slot], total); store_coherent(&cand_bound[out_slot], bound); }
+    publish_candidates<NT, KPT>(sh.scores, vis, e_begin, cand, cand_keys + out_slot * cand, &cand_count[out_slot],
+                                &cand_bound[out_slot], sh.bl, sh.sel, sh.tmp);
   } else if (threadIdx.x == 0) {
     store_coherent(&cand_count[out_slot], 0);
     store_coherent(&cand_bound[out_slot], uint64_t(0));
@@ -962,12 +1069,7 @@ __device__ __forceinline__ void wait_loads() {               // at most N vector
 // Barrier for the ring: the wave's direct-to-LDS loads are complete already (explicit vmcnt
 // waits); its own LDS reads complete before it (lgkmcnt(0)), so a slot read before the barrier may
 // be refilled after it; the compiler-only fences keep LDS accesses from moving across it.
-__device__ __forceinline__ void ring_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
+__device__ __forceinline__ void ring_barrier() { lds_sync(); }
 
 struct alignas(16) StreamShared {
   union {
@@ -1144,24 +1246,8 @@ __global__ void __launch_bounds__(kStreamThreads, 1) index_stream_kernel(IndexAr
   uint64_t *cand_keys = static_cast<uint64_t *>(a.workspace);
   uint64_t *cand_bound = cand_keys + n_q * a.plan.n_tiles * cand;
   int *cand_count = reinterpret_cast<int *>(cand_bound + n_q * a.plan.n_tiles);
-  uint64_t keys[KPT];
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const int i = tid * KPT + k;
-    keys[k] = i < vis ? make_key(sh.scores[i], uint32_t(e_begin + i)) : 0;
-  }
-  uint64_t bound = 0;
-  if (vis > cand) bound = block_cut_bucket<NT, KPT>(keys, cand, cand / 2, sh.bl, sh.sel);
-  int mine = 0;
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) mine += (keys[k] != 0 && keys[k] >= bound);
-  int total;
-  int pos = block_excl_scan<NT>(mine, sh.tmp, total);
-  uint64_t *dst = cand_keys + out_slot * cand;
-#pragma unroll
-  for (int k = 0; k < KPT; ++k)
-    if (keys[k] != 0 && keys[k] >= bound) store_coherent(&dst[pos++], keys[k]);
-  if (tid == 0) { store_coherent(&cand_count[out_slot], total); store_coherent(&cand_bound[out_slot], bound); }
+  publish_candidates<NT, KPT>(sh.scores, vis, e_begin, cand, cand_keys + out_slot * cand, &cand_count[out_slot],
+                              &cand_bound[out_slot], sh.bl, sh.sel, sh.tmp);
   if constexpr (FUSE) {
     int *arrivals = reinterpret_cast<int *>(static_cast<uint8_t *>(a.workspace) + arrivals_offset(n_q, a.plan));
     if (!arrive_last(&arrivals[qi * kCounterStride], a.plan.n_tiles, &sh.flag)) return;
