@@ -437,20 +437,23 @@ __device__ __forceinline__ uint64_t block_cut(const uint64_t (&keys)[KPT], int n
 }
 
 // ---- bucket select ---------------------------------------------------------------------------
-// The same threshold as block_cut, found from one histogram of the keys' scores over kBins equal
-// bins spanning [min, max].  A bin index, (s - min) * kBins / (max - min) truncated, never decreases
-// as the score grows, so every key of a higher bin is larger than every key of a lower one.  One
-// pass locates the bin where the count from the top reaches `need`; the threshold is a bin edge when
-// that leaves at least keep_min keys above, or the exact rank inside the bin when the bin holds at
-// most kSmallBucket keys (one wave ranks them); otherwise (many equal or tightly clustered scores)
-// the radix select decides.  Scores spread over many bins, so the histogram atomics seldom collide
-// (the radix passes' top digits put most keys of a tile into a handful of bins).
+// The same cut as block_cut, found from histograms of the keys' score orders (the high words, which
+// order like the scores) over kBins bins: bin = (o - base) >> shift, with the shift that fits the
+// orders' span into kBins bins.  The bin never decreases as the score grows, so every key of a
+// higher bin is larger than every key of a lower one.  Binning the order bits is binning the scores
+// on a scale that is linear inside each binade and doubles its step per binade: a few extreme
+// scores (planted keys, ten times the rest) widen the span by a few binades instead of squeezing
+// every other key into a handful of bins.  A pass locates the bin where the count from the top
+// reaches `need`; the result is that bin's edge when it leaves at least keep_min keys above (or
+// exactly `need` from it down), the exact key of rank `need` when the bin holds at most
+// kSmallBucket keys (one wave ranks them), or else a second pass over the crossing bin alone;
+// equal or extremely clustered scores fall to the radix select.  A bin edge is a threshold key
+// (low word 0): the keys >= it are exactly the keys of the bins above, as with any other cut.
 constexpr int kBins = 2048;
 constexpr int kSmallBucket = 64;
-constexpr int kDummyBins = 32;                      // where keys outside the current range are counted
 
 struct alignas(16) BucketLds {
-  uint32_t hist[kBins + kDummyBins];
+  uint32_t hist[kBins];
   uint64_t list[kSmallBucket];      // keys of the crossing bin
   uint64_t kmin[16];
   uint32_t omin[16], omax[16];
@@ -508,100 +511,91 @@ template <int NT, int KPT>
 __device__ __forceinline__ uint64_t block_cut_bucket(const uint64_t (&keys)[KPT], int need, int keep_min, BucketLds &bl,
                                                      SelectLds &sl) {
   constexpr int NW = NT / 64, BPT = kBins / NT;
-  static_assert(BPT % 4 == 0, "bins are read four at a time");
+  static_assert(BPT == 4, "four bins per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // state of each key: 0 out, 1 undecided (inside the current score range), 2 kept
-  int st[KPT];
+  uint32_t omin = ~0u, omax = 0u;
 #pragma unroll
-  for (int k = 0; k < KPT; ++k) st[k] = keys[k] != 0 ? 1 : 0;
-  int rneed = need, rkeep = keep_min;             // still to find among the undecided keys
+  for (int k = 0; k < KPT; ++k) {
+    const uint32_t o = uint32_t(keys[k] >> 32);
+    omin = min(omin, keys[k] != 0 ? o : ~0u);
+    omax = max(omax, o);                                      // an empty key's order is 0
+  }
+  reinterpret_cast<uint4 *>(bl.hist)[tid] = make_uint4(0, 0, 0, 0);   // NT x 4 bins = kBins
+  if (tid == 0) bl.res[3] = 0;
+  omin = wave_all_u32<true>(omin);
+  omax = wave_all_u32<false>(omax);
+  if (lane == 0) { bl.omin[wave] = omin; bl.omax[wave] = omax; }
+  lds_barrier();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) { omin = min(omin, bl.omin[w]); omax = max(omax, bl.omax[w]); }
+  if (omin == omax) return block_cut<NT, KPT>(keys, need, keep_min, sl);    // one score: by index
+  uint32_t base = omin, span = omax - omin;                   // the undecided keys' orders
+  int rneed = need, rkeep = keep_min;                          // still to find among them
   for (int pass = 0; pass < 2; ++pass) {
-    for (int i = tid; i < (kBins + kDummyBins) / 4; i += NT) reinterpret_cast<uint4 *>(bl.hist)[i] = make_uint4(0, 0, 0, 0);
-    if (tid == 0) bl.res[3] = 0;
-    // the undecided keys' range, in score-order bits (which order like the scores)
-    uint32_t omin = ~0u, omax = 0u;
-#pragma unroll
-    for (int k = 0; k < KPT; ++k) {
-      const uint32_t o = uint32_t(keys[k] >> 32);
-      omin = min(omin, st[k] == 1 ? o : ~0u);
-      omax = max(omax, st[k] == 1 ? o : 0u);
-    }
-    omin = wave_all_u32<true>(omin);
-    omax = wave_all_u32<false>(omax);
-    if (lane == 0) { bl.omin[wave] = omin; bl.omax[wave] = omax; }
-    lds_barrier();
-#pragma unroll
-    for (int w = 0; w < NW; ++w) { omin = min(omin, bl.omin[w]); omax = max(omax, bl.omax[w]); }
-    const float lo = order_score(omin), hi = order_score(omax);
-    const float scale = float(kBins) / (hi - lo);
-    if (!(hi > lo) || !(scale < INFINITY) || !(lo > -INFINITY) || !(hi < INFINITY)) break;   // uniform
+    const int shift = max(0, 32 - __clz(span) - 11);          // span >> shift < kBins
     int bin[KPT];
 #pragma unroll
     for (int k = 0; k < KPT; ++k) {
-      const int bk = min(int(__fmul_rn(__fsub_rn(key_score(keys[k]), lo), scale)), kBins - 1);
-      bin[k] = st[k] == 1 ? bk : -1;
-      atomicAdd(&bl.hist[st[k] == 1 ? bk : kBins + (lane & (kDummyBins - 1))], 1u);
+      const uint32_t d = uint32_t(keys[k] >> 32) - base;
+      bin[k] = (keys[k] != 0 && d <= span) ? int(d >> shift) : -1;
+      if (bin[k] >= 0) atomicAdd(&bl.hist[bin[k]], 1u);
     }
     lds_barrier();
-    // this thread's BPT bins, highest first; the count of undecided keys in every higher bin
+    // this thread's four bins, highest first, and the undecided keys in every higher bin
     const int top = kBins - 1 - tid * BPT;
-    int c[BPT], sum = 0;
-#pragma unroll
-    for (int v = 0; v < BPT / 4; ++v) {
-      const uint4 x = reinterpret_cast<const uint4 *>(bl.hist)[(top - 3 - 4 * v) >> 2];
-      c[4 * v] = int(x.w); c[4 * v + 1] = int(x.z); c[4 * v + 2] = int(x.y); c[4 * v + 3] = int(x.x);
-    }
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) sum += c[j];
+    const uint4 x = reinterpret_cast<const uint4 *>(bl.hist)[(top - 3) >> 2];
+    const int c0 = int(x.w), c1 = int(x.z), c2 = int(x.y), c3 = int(x.x);
+    const int sum = c0 + c1 + c2 + c3;
     const int incl = wave_scan_bcast(sum);
     if (lane == 63) bl.wsum[wave] = incl;
     lds_barrier();
     int cum = incl - sum;
 #pragma unroll
     for (int w = 0; w < NW; ++w) cum += w < wave ? bl.wsum[w] : 0;
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-      if (cum < rneed && rneed <= cum + c[j]) { bl.res[0] = top - j; bl.res[1] = cum; bl.res[2] = c[j]; }
-      cum += c[j];
+    {
+      const int a0 = cum, a1 = a0 + c0, a2 = a1 + c1, a3 = a2 + c2;
+      const int hit = (a0 < rneed && rneed <= a1) ? 0 : (a1 < rneed && rneed <= a2) ? 1
+                    : (a2 < rneed && rneed <= a3) ? 2 : (a3 < rneed && rneed <= a3 + c3) ? 3 : -1;
+      if (hit >= 0) {
+        bl.res[0] = top - hit;
+        bl.res[1] = hit == 0 ? a0 : hit == 1 ? a1 : hit == 2 ? a2 : a3;
+        bl.res[2] = hit == 0 ? c0 : hit == 1 ? c1 : hit == 2 ? c2 : c3;
+      }
     }
+    // the histogram is read: its readers clear their own bins for a second pass
+    reinterpret_cast<uint4 *>(bl.hist)[(top - 3) >> 2] = make_uint4(0, 0, 0, 0);
     lds_barrier();
     const int bstar = bl.res[0], above = bl.res[1], cnt = bl.res[2];
-    int edge = -1;                                // undecided keys of bins >= edge are kept
-    if (above >= rkeep) edge = bstar + 1;
-    else if (above + cnt == rneed) edge = bstar;
-    if (edge >= 0) {                              // the smallest kept key
-      uint64_t mn = ~uint64_t(0);
+    if (above >= rkeep)                                        // the bins above keep enough
+      return uint64_t(base + (uint32_t(bstar + 1) << shift)) << 32;
+    if (above + cnt == rneed) return uint64_t(base + (uint32_t(bstar) << shift)) << 32;
+    if (cnt <= kSmallBucket) {                                 // rank the crossing bin's keys (distinct)
 #pragma unroll
-      for (int k = 0; k < KPT; ++k) mn = umin64(mn, (st[k] == 2 || bin[k] >= edge) && st[k] != 0 ? keys[k] : ~uint64_t(0));
-      mn = wave_all_min_u64(mn);
-      if (lane == 0) bl.kmin[wave] = mn;
-      lds_barrier();
-      uint64_t e = ~uint64_t(0);
-#pragma unroll
-      for (int w = 0; w < NW; ++w) e = umin64(e, bl.kmin[w]);
-      lds_barrier();
-      return e;
-    }
-    if (cnt <= kSmallBucket) {                    // rank the crossing bin's keys (distinct) on one wave
-#pragma unroll
-      for (int k = 0; k < KPT; ++k)
-        if (bin[k] == bstar) bl.list[atomicAdd(&bl.res[3], 1)] = keys[k];
-      lds_barrier();
-      if (wave == 0) {
-        const uint64_t x = lane < cnt ? bl.list[lane] : 0;
-        int rank = 0;
-        for (int j = 0; j < cnt; ++j) rank += readlane64(x, j) > x;
-        if (lane < cnt && rank == rneed - above - 1) bl.kmin[0] = x;
+      for (int k = 0; k < KPT; ++k) {
+        const bool m = bin[k] == bstar;
+        const uint64_t bal = __ballot(m);
+        if (bal) {
+          const int first = __ffsll((unsigned long long)bal) - 1;
+          int wb = 0;
+          if (lane == first) wb = atomicAdd(&bl.res[3], __popcll(bal));
+          wb = __builtin_amdgcn_readlane(wb, first);
+          const int r = __builtin_amdgcn_mbcnt_hi(uint32_t(bal >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(bal), 0));
+          if (m) bl.list[wb + r] = keys[k];
+        }
       }
       lds_barrier();
-      const uint64_t e = bl.kmin[0];
+      if (wave == 0) {
+        const uint64_t v = lane < cnt ? bl.list[lane] : 0;
+        int rank = 0;
+        for (int j = 0; j < cnt; ++j) rank += readlane64(v, j) > v;
+        if (lane < cnt && rank == rneed - above - 1) bl.kmin[0] = v;
+      }
       lds_barrier();
-      return e;
+      return bl.kmin[0];
     }
-    // narrow to the crossing bin: keys above it are kept, keys below it are out
-#pragma unroll
-    for (int k = 0; k < KPT; ++k)
-      st[k] = st[k] == 1 ? (bin[k] > bstar ? 2 : (bin[k] == bstar ? 1 : 0)) : st[k];
+    if (shift == 0) break;                                     // one score in the bin: by index
+    base += uint32_t(bstar) << shift;                          // narrow to the crossing bin
+    span = (1u << shift) - 1;
     rneed -= above;
     rkeep -= above;
   }
