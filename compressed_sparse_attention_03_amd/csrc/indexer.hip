@@ -449,6 +449,7 @@ __device__ __forceinline__ uint64_t block_cut(const uint64_t (&keys)[KPT], int n
 // kSmallBucket keys (one wave ranks them), or else a second pass over the crossing bin alone;
 // equal or extremely clustered scores fall to the radix select.  A bin edge is a threshold key
 // (low word 0): the keys >= it are exactly the keys of the bins above, as with any other cut.
+// With fewer than `need` non-zero keys the result is 0 (every key is kept).
 constexpr int kBins = 2048;
 constexpr int kSmallBucket = 64;
 
@@ -514,20 +515,25 @@ __device__ __forceinline__ uint64_t block_cut_bucket(const uint64_t (&keys)[KPT]
   static_assert(BPT == 4, "four bins per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint32_t omin = ~0u, omax = 0u;
+  int nk = 0;
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
     const uint32_t o = uint32_t(keys[k] >> 32);
     omin = min(omin, keys[k] != 0 ? o : ~0u);
     omax = max(omax, o);                                      // an empty key's order is 0
+    nk += keys[k] != 0;
   }
   reinterpret_cast<uint4 *>(bl.hist)[tid] = make_uint4(0, 0, 0, 0);   // NT x 4 bins = kBins
   if (tid == 0) bl.res[3] = 0;
   omin = wave_all_u32<true>(omin);
   omax = wave_all_u32<false>(omax);
-  if (lane == 0) { bl.omin[wave] = omin; bl.omax[wave] = omax; }
+  nk = wave_scan_bcast(nk);
+  if (lane == 63) { bl.omin[wave] = omin; bl.omax[wave] = omax; bl.wsum[8 + wave] = nk; }
   lds_barrier();
+  nk = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) { omin = min(omin, bl.omin[w]); omax = max(omax, bl.omax[w]); }
+  for (int w = 0; w < NW; ++w) { omin = min(omin, bl.omin[w]); omax = max(omax, bl.omax[w]); nk += bl.wsum[8 + w]; }
+  if (nk < need) return 0;                                     // fewer keys than asked: keep them all
   if (omin == omax) return block_cut<NT, KPT>(keys, need, keep_min, sl);    // one score: by index
   uint32_t base = omin, span = omax - omin;                   // the undecided keys' orders
   int rneed = need, rkeep = keep_min;                          // still to find among them
@@ -731,7 +737,8 @@ __device__ __forceinline__ void publish_candidates(const float *scores, int vis,
   if (tid == 0) { store_coherent(count_out, total); store_coherent(bound_out, bound); }
 }
 
-// Exact rank-`need` (1 = largest) key among the block's non-zero keys.
+// A key E such that exactly `need` of the block's non-zero keys are >= E (the rank-`need` key,
+// 1 = largest, or a bin edge just below it), or 0 when there are fewer than `need` keys.
 template <int NT, int KPT>
 __device__ __forceinline__ uint64_t block_select(const uint64_t (&keys)[KPT], int need, BucketLds &bl, SelectLds &sl) {
   return block_cut_bucket<NT, KPT>(keys, need, need, bl, sl);
@@ -932,35 +939,31 @@ __device__ __forceinline__ void merge_query(const IndexArgs &a, SH &sh, int64_t 
   }
   if (tid == 0) sh.flag = 0;
   lds_barrier();
-  int nvalid_local = 0;
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
     const int slot = tid * KPT + k;
     if (slot >= slots || (slot & (cand - 1)) >= sh.counts[slot >> cshift]) keys[k] = 0;
-    nvalid_local += keys[k] != 0;
   }
-  int nvalid;
-  (void)block_excl_scan<NT>(nvalid_local, sh.tmp, nvalid);
   if (k_eff == 0) {
     for (int i = tid; i < a.topk; i += NT) out[i] = -1;
     return;
   }
-  uint64_t tau = 0;                                            // k-th best candidate (0: need all)
-  if (nvalid >= k_eff) tau = block_select<NT, KPT>(keys, k_eff, sh.bl, sh.sel);
-  // a truncated tile whose smallest kept key beats tau may hold further winners
+  // the k-th best candidate (0 when fewer than k_eff candidates: every one is kept)
+  const uint64_t tau = block_select<NT, KPT>(keys, k_eff, sh.bl, sh.sel);
+  // a truncated tile whose cut beats tau may hold further winners (the flag is read after the
+  // output positions' scan, whose barrier publishes it)
   for (int i = tid; i < n_tiles; i += NT)
     if (sh.bounds[i] != 0 && sh.bounds[i] > tau) sh.flag = 1;
-  lds_barrier();
-  if (sh.flag) {
-    if (!have_query) load_query_lds<FMT, NT>(a, sh, qi);
-    merge_fallback<FMT, NHB, NT, KPT>(a, sh, keys, tau, b, n_vis, k_eff, out);
-    return;
-  }
   int mine = 0;
 #pragma unroll
   for (int k = 0; k < KPT; ++k) mine += (keys[k] != 0 && keys[k] >= tau);
   int total;
   int pos = block_excl_scan<NT>(mine, sh.tmp, total);
+  if (sh.flag) {
+    if (!have_query) load_query_lds<FMT, NT>(a, sh, qi);
+    merge_fallback<FMT, NHB, NT, KPT>(a, sh, keys, tau, b, n_vis, k_eff, out);
+    return;
+  }
 #pragma unroll
   for (int k = 0; k < KPT; ++k)
     if (keys[k] != 0 && keys[k] >= tau) out[pos++] = int32_t(key_index(keys[k]));
