@@ -126,12 +126,12 @@ class Leg:
     def step(self, i):
         w, c = self.w, i % self.ncopies
         if w.kind == "csa_decode" and self.append:
-            ops.csa_decode_append(self.c_new[c], self.z_new[c], self.t, self.bias, m=w.m, overlap=w.overlap,
-                                  rope_dim=w.rope_dim, tok_c=self.tok_c[c], tok_z=self.tok_z[c], win_ring=self.win[c],
-                                  entries=self.ent[c], n_entries=self.n_app)
-            ops.csa_decode_append_index(self.c_i_new[c], self.z_i_new[c], self.t, self.bias_i, m=w.m,
-                                        overlap=w.overlap, tok_c=self.tok_ci[c], tok_z=self.tok_zi[c],
-                                        key_format=w.key_format, k_codes=self.codes[c], k_scales=self.scales[c])
+            ops.csa_decode_append_step(self.c_new[c], self.z_new[c], self.t, self.bias, m=w.m, overlap=w.overlap,
+                                       rope_dim=w.rope_dim, tok_c=self.tok_c[c], tok_z=self.tok_z[c],
+                                       win_ring=self.win[c], entries=self.ent[c], n_entries=self.n_app,
+                                       c_i_new=self.c_i_new[c], z_i_new=self.z_i_new[c], bias_i=self.bias_i,
+                                       tok_ci=self.tok_ci[c], tok_zi=self.tok_zi[c], key_format=w.key_format,
+                                       k_codes=self.codes[c], k_scales=self.scales[c])
             ops.csa_index_topk(self.q_idx[c], self.w_idx[c], self.codes[c], self.scales[c], key_format=w.key_format,
                                n_entries=self.n_app, q_pos0=self.t, m=w.m, topk=w.topk, workspace=self.ws_i,
                                topk_out=self.sel[c])
@@ -158,7 +158,7 @@ class Leg:
             self.step(i)
         torch.cuda.synchronize()
         res = {}
-        for k in ("decode_append", "decode_append_keys", "index_score", "index_merge", "attend_split",
+        for k in ("decode_append_step", "decode_append", "decode_append_keys", "index_score", "index_merge", "attend_split",
                   "attend_combine"):
             ms, cnt = ops.timing_read(k)
             if cnt:

@@ -250,6 +250,46 @@ csa_status csa_decode_append_index(const uint16_t *c_i_new, const uint16_t *z_i_
   return launched(e, "decode_append_index launch");
 }
 
+csa_status csa_decode_append_step(const uint16_t *c_new, const uint16_t *z_new, const int64_t *pos,
+                                  const uint16_t *bias, const uint16_t *norm_w, int B, int d, int m, int overlap,
+                                  int rope_dim, float rope_base, float eps, uint16_t *tok_c, uint16_t *tok_z,
+                                  uint16_t *win_ring, int64_t W_cap, uint16_t *entries, int64_t N_cap,
+                                  int64_t *n_entries, const uint16_t *c_i_new, const uint16_t *z_i_new,
+                                  const uint16_t *bias_i, int D_I, uint16_t *tok_ci, uint16_t *tok_zi,
+                                  int key_format, uint16_t *keys_out, void *k_codes, void *k_scales, void *stream) {
+  REQUIRE(B >= 0 && B <= 65535, "B must be in [0, 65535]");
+  if (!(d == 128 || d == 256 || d == 512 || d == 1024))
+    return fail(CSA_ERR_UNSUPPORTED, "d must be one of 128, 256, 512, 1024 (got %d)", d);
+  REQUIRE(m >= 1 && m <= 1024, "m must be in [1, 1024]");
+  REQUIRE(overlap == 0 || overlap == 1, "overlap must be 0 or 1");
+  REQUIRE(rope_dim >= 0 && rope_dim <= d && rope_dim % 4 == 0, "rope_dim must be a multiple of 4 in [0, d]");
+  REQUIRE(eps > 0.f && std::isfinite(eps), "eps must be positive");
+  REQUIRE(rope_base > 1.f && std::isfinite(rope_base), "rope_base must be > 1");
+  REQUIRE(W_cap >= 1 && W_cap < (int64_t(1) << 31), "W_cap must be in [1, 2^31)");
+  REQUIRE(N_cap >= 1 && N_cap < (int64_t(1) << 31), "N_cap must be in [1, 2^31)");
+  if (B == 0) return CSA_OK;
+  csa_status s = check_key_cache(D_I, key_format, k_codes, k_scales);
+  if (s != CSA_OK) return s;
+  REQUIRE_PTR(c_new); REQUIRE_PTR(z_new); REQUIRE_PTR(pos); REQUIRE_PTR(bias); REQUIRE_PTR_OR_NULL(norm_w);
+  REQUIRE_PTR(tok_c); REQUIRE_PTR(tok_z); REQUIRE_PTR(win_ring); REQUIRE_PTR(entries); REQUIRE_PTR(n_entries);
+  REQUIRE_PTR(c_i_new); REQUIRE_PTR(z_i_new); REQUIRE_PTR(bias_i); REQUIRE_PTR(tok_ci); REQUIRE_PTR(tok_zi);
+  REQUIRE_PTR_OR_NULL(keys_out);
+  csa::AppendArgs a{};
+  a.c_new = c_new; a.z_new = z_new; a.k_new = nullptr; a.bias = bias; a.norm_w = norm_w; a.pos = pos;
+  a.tok_c = tok_c; a.tok_z = tok_z; a.win_ring = win_ring; a.entries = entries; a.k_codes = nullptr;
+  a.k_scales = nullptr; a.n_entries = n_entries; a.W_cap = W_cap; a.N_cap = N_cap; a.B = B; a.d = d; a.m = m;
+  a.overlap = overlap; a.rope_dim = rope_dim; a.key_format = key_format; a.D_I = D_I;
+  a.log2_base = std::log2(double(rope_base)); a.eps = eps;
+  csa::AppendArgs ai{};
+  ai.c_new = c_i_new; ai.z_new = z_i_new; ai.k_new = nullptr; ai.bias = bias_i; ai.norm_w = nullptr; ai.pos = pos;
+  ai.tok_c = tok_ci; ai.tok_z = tok_zi; ai.win_ring = nullptr; ai.entries = keys_out; ai.k_codes = k_codes;
+  ai.k_scales = k_scales; ai.n_entries = nullptr; ai.W_cap = 1; ai.N_cap = N_cap; ai.B = B; ai.d = D_I; ai.m = m;
+  ai.overlap = overlap; ai.rope_dim = 0; ai.key_format = key_format; ai.D_I = D_I; ai.log2_base = 1.0;
+  ai.eps = 1e-6f;
+  hipError_t e = csa::launch_append_step(a, ai, static_cast<hipStream_t>(stream));
+  return launched(e, "decode_append_step launch");
+}
+
 csa_status csa_output_projection(const uint16_t *o, const uint16_t *w, int M, int H, int D, int G, int N_g,
                                  uint16_t *y, void *stream) {
   REQUIRE(M >= 0 && M <= (1 << 24), "M must be in [0, 2^24]");

@@ -19,6 +19,14 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Orders one wave's LDS accesses: its writes before the call are seen by its reads after it (a
+// wave's LDS operations complete in order; the fences keep the compiler from moving them across).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 // A workgroup barrier after which every wave's LDS writes are visible, without waiting for the
 // wave's global loads still in flight (the memory-model fence of lds_barrier makes the compiler
 // wait for those as well): each wave's LDS operations have completed (lgkmcnt 0) when it arrives.
@@ -185,6 +193,18 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// The same sum in every lane by DPP inside rows of 16 lanes and the gfx950 half-wave and row swaps
+// across them (a fixed order; no LDS round trips).
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false));   // quad [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false));   // quad [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));  // row half mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false));  // row mirror
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -198,12 +218,20 @@ __device__ __forceinline__ float wave_max(float v) {
 // the reduced angle); the hardware sine and cosine (v_sin_f32 / v_cos_f32, whose argument is in
 // turns) take the fp32 fraction.
 __device__ __forceinline__ double rope_rate(int r, double log2_base) { return -2.0 * log2_base / double(r); }
-__device__ __forceinline__ void rope_cos_sin(int64_t pos, int u, double rate, float *c, float *s) {
+// pair u's turns per position, base^(-2u/r) / (2 pi): independent of the position, so it can be
+// formed before the position is known
+__device__ __forceinline__ double rope_turns_per_pos(int u, double rate) {
   constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
-  const double turns = double(pos) * (exp2(double(u) * rate) * kInvTwoPi);
+  return exp2(double(u) * rate) * kInvTwoPi;
+}
+__device__ __forceinline__ void rope_cos_sin_f(int64_t pos, double turns_per_pos, float *c, float *s) {
+  const double turns = double(pos) * turns_per_pos;
   const float f = float(turns - rint(turns));                   // in [-1/2, 1/2]
   *s = __builtin_amdgcn_sinf(f);
   *c = __builtin_amdgcn_cosf(f);
+}
+__device__ __forceinline__ void rope_cos_sin(int64_t pos, int u, double rate, float *c, float *s) {
+  rope_cos_sin_f(pos, rope_turns_per_pos(u, rate), c, s);
 }
 
 }  // namespace csa

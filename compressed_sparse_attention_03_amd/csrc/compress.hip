@@ -173,6 +173,57 @@ __device__ __forceinline__ void norm_rope(float (&v)[CPL], const NormWeights<CPL
   }
 }
 
+// The rotation's per-lane pair frequencies (turns per position), formed before the position is
+// known: lane l's pair p is channels l CPL + 2p, 2p + 1 (0 for the channels below d - r).
+template <int CPL>
+struct RopeFreq {
+  double f[(CPL + 1) / 2];
+};
+template <int CPL>
+__device__ __forceinline__ RopeFreq<CPL> rope_freqs(int d, int r, double log2_base, int lane, double *s_f) {
+  // each lane forms one pair's frequency (a double-precision exp2: a long chain) into the wave's LDS
+  // row s_f[d / 2], then every lane reads its own pairs'
+  RopeFreq<CPL> q;
+  const int rope0 = d - r, c0 = lane * CPL;
+  const double rate = rope_rate(r > 0 ? r : 2, log2_base);
+  for (int u = lane; u < r / 2; u += 64) s_f[u] = rope_turns_per_pos(u, rate);
+  wave_lds_sync();
+#pragma unroll
+  for (int p = 0; p < CPL / 2; ++p) {
+    const int ch = c0 + 2 * p;
+    q.f[p] = ch >= rope0 ? s_f[(ch - rope0) >> 1] : 0.0;
+  }
+  return q;
+}
+
+// norm_rope with the frequencies formed beforehand and the wave's sum of squares by DPP: the
+// arithmetic of norm_rope but for the order of that sum.
+template <int CPL>
+__device__ __forceinline__ void norm_rope_f(float (&v)[CPL], const NormWeights<CPL> &gw, int d, int r, int64_t pos,
+                                            const RopeFreq<CPL> &q, float eps, int lane) {
+  static_assert(CPL >= 2, "pairs within a lane");
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) ss += v[j] * v[j];
+  ss = wave_sum_dpp(ss);
+  const float inv = rsqrtf(ss / float(d) + eps);
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) v[j] *= inv * (gw.has ? gw.w.at(j) : 1.0f);
+  const int rope0 = d - r, c0 = lane * CPL;
+  if (c0 + CPL > rope0) {
+#pragma unroll
+    for (int p = 0; p < CPL / 2; ++p) {
+      if (c0 + 2 * p >= rope0) {
+        float cs, sn;
+        rope_cos_sin_f(pos, q.f[p], &cs, &sn);
+        const float a = v[2 * p], b = v[2 * p + 1];
+        v[2 * p] = a * cs - b * sn;
+        v[2 * p + 1] = a * sn + b * cs;
+      }
+    }
+  }
+}
+
 template <int CPL, int U, bool WIN, bool KEYS>
 __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
   const int d = a.d, m = a.m;
@@ -290,12 +341,16 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
 // paragraph: the newest tokens are kept as separate rows, and a group becomes an entry once it is
 // complete; indexer paragraph: the indexer keys are stored in low precision.
 //
-// One workgroup per sequence.  The token's raw c, z rows go into the sequence's ring of the last
-// (1+overlap) m tokens (slot = position mod ring size); its window row (RMSNorm, RoPE at its own
-// position) into the window ring (slot = position mod W_cap).  When the token closes a group the
-// entry is pooled exactly as the batch compressor pools it -- from the ring, with the new token
-// taken from registers -- normalised, rotated at i m and written; the entry's indexer key is
-// quantised into the key cache (the encoders of csa_quantize_keys) and n_entries is advanced.
+// One workgroup per sequence (and stream: the fused launch runs the KV stream's and the indexer
+// stream's workgroups side by side).  The token's raw c, z rows go into the sequence's ring of the
+// last (1+overlap) m tokens (slot = position mod ring size); its window row (RMSNorm, RoPE at its
+// own position) into the window ring (slot = position mod W_cap).  When the token closes a group
+// the entry is pooled from the ring, with the new token taken from registers -- the same tokens,
+// bias rows and softmax as the batch compressor, accumulated in ring-slot order -- normalised,
+// rotated at i m and written; the entry's indexer key is quantised into the key cache (the
+// encoders of csa_quantize_keys) and n_entries is advanced.  A closing group's tokens fill the
+// whole ring, so the waves load their ring slots, and both bias rows a slot can take, before the
+// position arrives: the position only decides which rows take part and with which bias row.
 
 // Quantise-on-write of one indexer key row (one wave; D_I % 32 == 0, <= 1024): lane l holds the
 // value pairs l, l + 64, ... (all loaded before any store).  fp32 copy, fp8 e4m3 with a
@@ -346,64 +401,112 @@ __device__ void store_key_row(const AppendArgs &a, const uint16_t *x, int64_t ro
   }
 }
 
+// Rings of at most kSmallRing rows (CSA: 2 m = 8) are pooled by waves 0 and 1 over half the slots
+// each while waves 2 and 3 write the token's window row and ring rows; longer rings (HCA:
+// m' = 128) by all four waves over their shares of the slots.  The partial softmax states meet in
+// LDS and wave 0 merges them in wave order.
+constexpr int kSmallRing = 8;
+
 template <int CPL, bool KEYS>
-__global__ void __launch_bounds__(256) decode_append_kernel(AppendArgs a) {
+__device__ __forceinline__ void append_sequence(const AppendArgs &a, int b) {
   const int d = a.d, m = a.m;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int b = blockIdx.x;
-  const int64_t t = a.pos[b];
-  if (t < 0) return;
   const int R = (1 + a.overlap) * m;                           // ring rows per sequence
   const int64_t ring0 = int64_t(b) * R;
+  const int npw = R <= kSmallRing ? 2 : 4;                     // pooling waves
+  const bool pools = wave < npw;
+  // everything that does not need the position first: the token's rows, the norm weights, the
+  // rotation's frequencies, and the ring slots with both of their candidate bias rows
   RawRow<CPL> rc, rz;
   load_raw<CPL>(a.c_new + int64_t(b) * d + lane * CPL, rc);
   load_raw<CPL>(a.z_new + int64_t(b) * d + lane * CPL, rz);
   const NormWeights<CPL> gw = load_norm_weights<CPL>(a.norm_w, a.bias, lane);
+  constexpr int U = 4;                                         // slots held in registers at once
+  const int per = (R + npw - 1) / npw;                         // ring slots per pooling wave
+  const int s0 = pools ? wave * per : 0, s1 = pools ? min(R, s0 + per) : 0;
+  RawRow<CPL> xc[U], xz[U], xa[U], xb[U];
+  auto load_slots = [&](int k) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sl = min(k + u, max(s1 - 1, 0));              // past the wave's slots: repeat (in bounds)
+      load_raw<CPL>(a.tok_c + (ring0 + sl) * d + lane * CPL, xc[u]);
+      load_raw<CPL>(a.tok_z + (ring0 + sl) * d + lane * CPL, xz[u]);
+      load_raw<CPL>(a.bias + int64_t(sl) * d + lane * CPL, xa[u]);
+      if (a.overlap) load_raw<CPL>(a.bias + int64_t((sl + m) % R) * d + lane * CPL, xb[u]);
+      else xb[u] = xa[u];
+    }
+  };
+  if (s0 < s1) load_slots(s0);
+  __shared__ float s_state[3][4][64 * CPL];
+  __shared__ double s_freq[2][32 * CPL];                       // waves 0 and 2: d / 2 pair frequencies
+  RopeFreq<CPL> rq;                                            // (one channel per lane: formed at use)
+  if constexpr (!KEYS && CPL >= 2) {
+    if (wave == 0 || wave == 2) rq = rope_freqs<CPL>(d, a.rope_dim, a.log2_base, lane, s_freq[wave >> 1]);
+  }
+  const int64_t t = a.pos[b];
+  if (t < 0) return;
   const int64_t i = (t + 1) / m - 1;                           // the entry this token closes, if any
   const bool closes = (t + 1) % m == 0 && i < a.N_cap;         // uniform over the workgroup
 
-  __shared__ float s_state[3][4][64 * CPL];
-  if (closes) {
-    // pooling first (its loads are the longest chain); the four waves split the entry's tokens
-    const bool has_prev = a.overlap && i > 0;
-    const int nt = has_prev ? 2 * m : m;
-    const int64_t p_first = has_prev ? (i - 1) * m : i * m;
-    const int slot_first = has_prev ? 0 : (a.overlap ? m : 0); // bias row of the first token
-    float mx[CPL], sm[CPL], acc[CPL];
+  // the token's own rows: the window row (RMSNorm, RoPE at t) and the raw rows into the ring
+  auto token_jobs = [&]() __attribute__((always_inline)) {
+    if (wave == 2) {
+      if constexpr (!KEYS) {
+        float v[CPL];
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) { mx[j] = -INFINITY; sm[j] = 0.f; acc[j] = 0.f; }
-    const int per = (nt + 3) >> 2;
-    const int k0 = wave * per, k1 = min(nt, k0 + per);
-    const int ring_first = int(p_first % R);                   // ring slot of the entry's first token
-    // groups of 4 tokens, their loads in flight together; the token at t comes from registers
-    // (its ring row is written by this launch), and past the wave's last token the loads repeat
-    // that token (in bounds) with logit -inf
-    constexpr int U = 4;
-    for (int k = k0; k < k1; k += U) {
-      RawRow<CPL> xc[U], xz[U], xb[U];
+        for (int j = 0; j < CPL; ++j) v[j] = rc.at(j);
+        if constexpr (CPL >= 2) norm_rope_f<CPL>(v, gw, d, a.rope_dim, t, rq, a.eps, lane);
+        else norm_rope<CPL>(v, gw, d, a.rope_dim, t, a.log2_base, a.eps, lane);
+        store_row<CPL>(a.win_ring + (int64_t(b) * a.W_cap + t % a.W_cap) * d + lane * CPL, v);
+      }
+    } else if (wave == 3) {
+      store_raw<CPL>(a.tok_c + (ring0 + t % R) * d + lane * CPL, rc);
+      store_raw<CPL>(a.tok_z + (ring0 + t % R) * d + lane * CPL, rz);
+    }
+  };
+  if (!closes) {
+    token_jobs();
+    return;
+  }
+
+  // the entry's tokens: positions p_first .. p_first + nt - 1, token kk in ring slot
+  // (p_first + kk) mod R with bias row slot_first + kk; a slot's token is (slot - ring_first) mod R
+  const bool has_prev = a.overlap && i > 0;
+  const int nt = has_prev ? 2 * m : m;
+  const int64_t p_first = has_prev ? (i - 1) * m : i * m;
+  const int slot_first = has_prev ? 0 : (a.overlap ? m : 0);
+  const int ring_first = int(p_first % R);
+  const int slot_t = int(t % R);                               // the new token: from registers
+  float mx[CPL], sm[CPL], acc[CPL];                            // this wave's online softmax
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) { mx[j] = -INFINITY; sm[j] = 0.f; acc[j] = 0.f; }
+  if (pools) {
+    for (int k = s0; k < s1; k += U) {
+      if (k != s0) load_slots(k);
+      bool use_b[U], valid[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int kk = min(k + u, k1 - 1);
-        const int slot = (ring_first + kk) % R;
-        load_raw<CPL>(a.tok_c + (ring0 + slot) * d + lane * CPL, xc[u]);
-        load_raw<CPL>(a.tok_z + (ring0 + slot) * d + lane * CPL, xz[u]);
-        load_raw<CPL>(a.bias + int64_t(slot_first + kk) * d + lane * CPL, xb[u]);
-        if (p_first + kk == t) { xc[u] = rc; xz[u] = rz; }
+        const int sl = k + u;
+        const int kk = (sl - ring_first + R) % R;
+        valid[u] = sl < s1 && kk < nt;
+        use_b[u] = a.overlap && valid[u] && slot_first + kk != sl;   // then it is (sl + m) mod R
+        if (sl == slot_t) { xc[u] = rc; xz[u] = rz; }
       }
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         float l[U], gm = -INFINITY;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          l[u] = k + u < k1 ? (xz[u].at(j) + xb[u].at(j)) * kLog2e : -INFINITY;
+          const float bj = use_b[u] ? xb[u].at(j) : xa[u].at(j);
+          l[u] = valid[u] ? (xz[u].at(j) + bj) * kLog2e : -INFINITY;
           gm = fmaxf(gm, l[u]);
         }
         const float nm = fmaxf(mx[j], gm);
-        const float sc = exp2f(mx[j] - nm);
+        const float sc = nm == -INFINITY ? 0.f : exp2f(mx[j] - nm);
         float es = 0.f, ea = 0.f;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const float e = exp2f(l[u] - nm);
+          const float e = nm == -INFINITY ? 0.f : exp2f(l[u] - nm);
           es += e;
           ea += e * xc[u].at(j);
         }
@@ -412,70 +515,66 @@ __global__ void __launch_bounds__(256) decode_append_kernel(AppendArgs a) {
         mx[j] = nm;
       }
     }
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      s_state[0][wave][lane * CPL + j] = mx[j];
-      s_state[1][wave][lane * CPL + j] = sm[j];
-      s_state[2][wave][lane * CPL + j] = acc[j];
-    }
-    lds_barrier();
-  }
-  // then one job per wave: the entry, its key, the token's window row, the token's ring rows
-  if (wave == 0) {
-    if (!closes) return;
-    if constexpr (KEYS) {
-      // the indexer stream: the pooled key, rounded to bf16 and quantised into the key cache
-      float kv[CPL];
+    if (wave > 0) {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
-        const int ch = lane * CPL + j;
-        float M = fmaxf(fmaxf(s_state[0][0][ch], s_state[0][1][ch]), fmaxf(s_state[0][2][ch], s_state[0][3][ch]));
-        float S = 0.f, A = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float mw = s_state[0][w][ch];
-          const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-          S += s_state[1][w][ch] * f;
-          A += s_state[2][w][ch] * f;
-        }
-        kv[j] = bf16_to_f32(f32_to_bf16(A / S));
+        s_state[0][wave][lane * CPL + j] = mx[j];
+        s_state[1][wave][lane * CPL + j] = sm[j];
+        s_state[2][wave][lane * CPL + j] = acc[j];
       }
-      const int64_t row = int64_t(b) * a.N_cap + i;
-      if (a.entries) store_row<CPL>(a.entries + row * d + lane * CPL, kv);
-      encode_key_lanes<CPL>(kv, a.key_format, d, a.k_codes, a.k_scales, row, lane);
-      return;
     }
+  } else {
+    token_jobs();                                              // meanwhile
+  }
+  lds_barrier();
+  if (wave == 0) {
+    // merge the pooling waves' states in wave order (wave 0's own from registers)
     float pv[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int ch = lane * CPL + j;
-      float M = fmaxf(fmaxf(s_state[0][0][ch], s_state[0][1][ch]), fmaxf(s_state[0][2][ch], s_state[0][3][ch]));
+      float M = mx[j];
+      for (int w = 1; w < npw; ++w) M = fmaxf(M, s_state[0][w][ch]);
       float S = 0.f, A = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = s_state[0][w][ch];
+      for (int w = 0; w < npw; ++w) {
+        const float mw = w == 0 ? mx[j] : s_state[0][w][ch];
         const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-        S += s_state[1][w][ch] * f;
-        A += s_state[2][w][ch] * f;
+        S += (w == 0 ? sm[j] : s_state[1][w][ch]) * f;
+        A += (w == 0 ? acc[j] : s_state[2][w][ch]) * f;
       }
       pv[j] = A / S;
     }
-    norm_rope<CPL>(pv, gw, d, a.rope_dim, i * m, a.log2_base, a.eps, lane);
-    store_row<CPL>(a.entries + (int64_t(b) * a.N_cap + i) * d + lane * CPL, pv);
-    if (lane == 0) a.n_entries[b] = i + 1;
-  } else if (wave == 1) {
-    if (!KEYS && closes && a.k_new) store_key_row(a, a.k_new + int64_t(b) * a.D_I, int64_t(b) * a.N_cap + i, lane);
-  } else if (wave == 2) {
-    if (KEYS) return;
-    float v[CPL];
+    const int64_t row = int64_t(b) * a.N_cap + i;
+    if constexpr (KEYS) {
+      // the indexer stream: the pooled key, rounded to bf16 and quantised into the key cache
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) v[j] = rc.at(j);
-    norm_rope<CPL>(v, gw, d, a.rope_dim, t, a.log2_base, a.eps, lane);
-    store_row<CPL>(a.win_ring + (int64_t(b) * a.W_cap + t % a.W_cap) * d + lane * CPL, v);
-  } else {
-    store_raw<CPL>(a.tok_c + (ring0 + t % R) * d + lane * CPL, rc);
-    store_raw<CPL>(a.tok_z + (ring0 + t % R) * d + lane * CPL, rz);
+      for (int j = 0; j < CPL; ++j) pv[j] = bf16_to_f32(f32_to_bf16(pv[j]));
+      if (a.entries) store_row<CPL>(a.entries + row * d + lane * CPL, pv);
+      encode_key_lanes<CPL>(pv, a.key_format, d, a.k_codes, a.k_scales, row, lane);
+    } else {
+      if constexpr (CPL >= 2) norm_rope_f<CPL>(pv, gw, d, a.rope_dim, i * m, rq, a.eps, lane);
+      else norm_rope<CPL>(pv, gw, d, a.rope_dim, i * m, a.log2_base, a.eps, lane);
+      store_row<CPL>(a.entries + row * d + lane * CPL, pv);
+      if (lane == 0) a.n_entries[b] = i + 1;
+    }
+  } else if (wave == 1) {
+    if (!KEYS && a.k_new) store_key_row(a, a.k_new + int64_t(b) * a.D_I, int64_t(b) * a.N_cap + i, lane);
+  } else if (pools) {
+    token_jobs();                                              // long rings: after the pooling
   }
+}
+
+template <int CPL, bool KEYS>
+__global__ void __launch_bounds__(256) decode_append_kernel(AppendArgs a) {
+  append_sequence<CPL, KEYS>(a, blockIdx.x);
+}
+
+// Both streams of one decode step in one launch: workgroups (b, 0) maintain the KV stream, (b, 1)
+// the indexer stream.
+template <int CPL, int CPLI>
+__global__ void __launch_bounds__(256) decode_append_step_kernel(AppendArgs a, AppendArgs ai) {
+  if (blockIdx.y == 0) append_sequence<CPL, false>(a, blockIdx.x);
+  else append_sequence<CPLI, true>(ai, blockIdx.x);
 }
 
 template <int CPL, bool WIN>
@@ -530,6 +629,26 @@ hipError_t launch_append_keys(const AppendArgs &a, hipStream_t stream) {
     case 16: return launch("decode_append_keys", decode_append_kernel<16, true>, grid, block, stream, a);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_append_step(const AppendArgs &a, const AppendArgs &ai, hipStream_t stream) {
+  const dim3 grid(unsigned(a.B), 2), block(256);
+#define CSA_STEP_CASES(C)                                                                                      \
+  switch (ai.d / 64) {                                                                                        \
+    case 2: return launch("decode_append_step", decode_append_step_kernel<C, 2>, grid, block, stream, a, ai);  \
+    case 4: return launch("decode_append_step", decode_append_step_kernel<C, 4>, grid, block, stream, a, ai);  \
+    case 8: return launch("decode_append_step", decode_append_step_kernel<C, 8>, grid, block, stream, a, ai);  \
+    case 16: return launch("decode_append_step", decode_append_step_kernel<C, 16>, grid, block, stream, a, ai); \
+    default: return hipErrorInvalidValue;                                                                     \
+  }
+  switch (a.d / 64) {
+    case 2: CSA_STEP_CASES(2)
+    case 4: CSA_STEP_CASES(4)
+    case 8: CSA_STEP_CASES(8)
+    case 16: CSA_STEP_CASES(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef CSA_STEP_CASES
 }
 
 hipError_t launch_compress_keys(const CompressArgs &a, hipStream_t stream) {

@@ -1267,11 +1267,6 @@ constexpr int kMultiTile = 512;         // entries per tile
 // exactly `need` keys, or between keep_min and need - 1 when one histogram pass separates them --
 // on one wave, with the wave's own 256-bin histogram in LDS and no workgroup barrier (a wave's
 // LDS accesses complete in order; the fences keep the compiler from reordering them).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-}
 
 __device__ __forceinline__ uint64_t wave_cut(const uint64_t (&keys)[8], int need, int keep_min, uint32_t *H) {
   const int lane = threadIdx.x & 63;

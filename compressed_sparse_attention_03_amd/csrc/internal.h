@@ -38,6 +38,8 @@ struct AppendArgs {
 hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
 // the indexer stream's ring and keys (d = D_I; entries: optional bf16 keys [B, N_cap, D_I])
 hipError_t launch_append_keys(const AppendArgs &a, hipStream_t stream);
+// both streams in one launch (a: the KV stream, d in 128..1024; ai: the indexer stream)
+hipError_t launch_append_step(const AppendArgs &a, const AppendArgs &ai, hipStream_t stream);
 
 struct QuantizeArgs {
   const uint16_t *x;

@@ -31,6 +31,8 @@ _SIGS = {
     "csa_output_projection": (I32, [P, P, I32, I32, I32, I32, I32, P, P]),
     "csa_compress_index_keys": (I32, [P, P, P, I32, I64, I32, I32, I32, I32, I64, I32, P, P, P, P]),
     "csa_decode_append_index": (I32, [P, P, P, P, I32, I32, I32, I32, P, P, I64, I32, P, P, P, P]),
+    "csa_decode_append_step": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, F32, F32, P, P, P, I64, P, I64, P,
+                                     P, P, P, I32, P, P, I32, P, P, P, P]),
     "csa_decode_append": (I32, [P, P, P, P, P, P, I32, I32, I32, I32, I32, F32, F32, P, P, P, I64, P, I64,
                                 I32, I32, P, P, P, P]),
     "csa_index_topk": (I32, [P, P, P, P, I32, I32, I32, I32, I32, I64, P, P, I32, I32, P, P, P, SZ, P]),
@@ -296,6 +298,57 @@ def csa_decode_append(c_new, z_new, pos, bias, *, m, overlap, rope_dim, tok_c, t
                                  win_ring.shape[1], _ptr(entries), N_cap, f, D_I, _ptr(k_codes), _ptr(k_scales),
                                  _ptr(n_entries), _stream())
     _check(st, "csa_decode_append")
+
+
+def csa_decode_append_step(c_new, z_new, pos, bias, *, m, overlap, rope_dim, tok_c, tok_z, win_ring, entries,
+                           n_entries, c_i_new, z_i_new, bias_i, tok_ci, tok_zi, key_format, k_codes, k_scales=None,
+                           keys_out=None, norm_w=None, rope_base=10000.0, eps=1e-6):
+    """A decode step's whole cache maintenance in one launch: csa_decode_append's KV stream
+    (without k_new) and csa_decode_append_index's indexer stream, in place on the caches."""
+    _dev(c_new, "c_new", torch.bfloat16, 2)
+    _dev(z_new, "z_new", torch.bfloat16, 2)
+    B, d = c_new.shape
+    if tuple(z_new.shape) != (B, d):
+        raise ValueError("z_new must have the shape of c_new")
+    _i64(pos, "pos", B)
+    _i64(n_entries, "n_entries", B)
+    _dev(bias, "bias", torch.bfloat16, 2)
+    R = (1 + overlap) * m
+    for name, t in (("tok_c", tok_c), ("tok_z", tok_z)):
+        _dev(t, name, torch.bfloat16, 3)
+        if tuple(t.shape) != (B, R, d):
+            raise ValueError(f"{name} must be [{B}, {R}, {d}]")
+    _dev(win_ring, "win_ring", torch.bfloat16, 3)
+    _dev(entries, "entries", torch.bfloat16, 3)
+    if win_ring.shape[0] != B or win_ring.shape[2] != d or entries.shape[0] != B or entries.shape[2] != d:
+        raise ValueError("win_ring / entries must be [B, rows, d]")
+    if norm_w is not None:
+        _dev(norm_w, "norm_w", torch.bfloat16, 1)
+    N_cap = entries.shape[1]
+    _dev(c_i_new, "c_i_new", torch.bfloat16, 2)
+    _dev(z_i_new, "z_i_new", torch.bfloat16, 2)
+    D_I = c_i_new.shape[1]
+    if c_i_new.shape[0] != B or tuple(z_i_new.shape) != (B, D_I):
+        raise ValueError("c_i_new / z_i_new must be [B, D_I]")
+    _dev(bias_i, "bias_i", torch.bfloat16, 2)
+    for name, t in (("tok_ci", tok_ci), ("tok_zi", tok_zi)):
+        _dev(t, name, torch.bfloat16, 3)
+        if tuple(t.shape) != (B, R, D_I):
+            raise ValueError(f"{name} must be [{B}, {R}, {D_I}]")
+    f = KEY_FORMATS[key_format]
+    if k_codes.shape[1] != N_cap:
+        raise ValueError("k_codes must have N_cap rows per sequence, as entries")
+    _check_key_cache(k_codes, k_scales, (B, N_cap), D_I, f)
+    if keys_out is not None:
+        _dev(keys_out, "keys_out", torch.bfloat16, 3)
+        if tuple(keys_out.shape) != (B, N_cap, D_I):
+            raise ValueError(f"keys_out must be [{B}, {N_cap}, {D_I}]")
+    st = lib().csa_decode_append_step(_ptr(c_new), _ptr(z_new), _ptr(pos), _ptr(bias), _ptr(norm_w), B, d, m, overlap,
+                                      rope_dim, rope_base, eps, _ptr(tok_c), _ptr(tok_z), _ptr(win_ring),
+                                      win_ring.shape[1], _ptr(entries), N_cap, _ptr(n_entries), _ptr(c_i_new),
+                                      _ptr(z_i_new), _ptr(bias_i), D_I, _ptr(tok_ci), _ptr(tok_zi), f, _ptr(keys_out),
+                                      _ptr(k_codes), _ptr(k_scales), _stream())
+    _check(st, "csa_decode_append_step")
 
 
 def index_topk_workspace(B, Sq, N_cap, topk, device="cuda"):

@@ -164,6 +164,26 @@ csa_status csa_decode_append_index(const uint16_t *c_i_new, const uint16_t *z_i_
                                    void *k_codes, void *k_scales, void *stream);
 
 /*
+ * csa_decode_append_step -- a decode step's whole cache maintenance in one launch: the KV
+ * stream's part of csa_decode_append and the indexer stream's csa_decode_append_index, side by
+ * side (one workgroup per sequence and stream).  [EXPLAINER] CSA walk-through: one new entry per
+ * m tokens, and its indexer key, which the lightning indexer rates; [RABBIT] sliding-window and
+ * indexer paragraphs.
+ * The KV-stream arguments are csa_decode_append's (with no k_new: the closed entry's indexer key
+ * is the indexer stream's pooled key); c_i_new, z_i_new, bias_i, D_I, tok_ci, tok_zi, key_format,
+ * keys_out, k_codes, k_scales are csa_decode_append_index's (tok_c, tok_z there).  The results are
+ * those of the two calls.  pos, m, overlap and N_cap are shared by both streams.
+ * Limits: d in {128, 256, 512, 1024}; D_I in {128, 256, 512, 1024}; others as the two calls.
+ */
+csa_status csa_decode_append_step(const uint16_t *c_new, const uint16_t *z_new, const int64_t *pos,
+                                  const uint16_t *bias, const uint16_t *norm_w, int B, int d, int m, int overlap,
+                                  int rope_dim, float rope_base, float eps, uint16_t *tok_c, uint16_t *tok_z,
+                                  uint16_t *win_ring, int64_t W_cap, uint16_t *entries, int64_t N_cap,
+                                  int64_t *n_entries, const uint16_t *c_i_new, const uint16_t *z_i_new,
+                                  const uint16_t *bias_i, int D_I, uint16_t *tok_ci, uint16_t *tok_zi,
+                                  int key_format, uint16_t *keys_out, void *k_codes, void *k_scales, void *stream);
+
+/*
  * csa_quantize_keys -- quantise lightning-indexer keys to their storage format (quantise on write).
  * [DEVTO] "Two Compression Strategies": the indexer runs in FP4; [RABBIT] indexer paragraph:
  * the indexer works on compact, low-precision operands.

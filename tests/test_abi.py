@@ -242,3 +242,19 @@ def test_attend_noalloc_rejects_shapes_beyond_its_scratch():
                               ctypes.c_float(0.044), ctypes.c_float(10000.0), ctypes.c_float(1e-6), v, None, None)
     assert st == 3
     assert b"scratch" in L.csa_last_error()
+
+
+def test_append_step_rejects_bad_arguments():
+    L = ops.lib()
+    v = ctypes.c_void_p(16)
+    f = lambda x: ctypes.c_float(x)
+    # d = 64 is not offered by the fused launch; D_I = 96 is no key-cache width; m = 0
+    args = dict(d=512, D_I=128, m=4, fmt=2)
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.csa_decode_append_step(v, v, v, v, None, 4, a["d"], a["m"], 1, 64, f(10000.0), f(1e-6), v, v, v,
+                                        128, v, 64, v, v, v, v, a["D_I"], v, v, a["fmt"], None, v, v, None)
+    assert call(d=64) == 2 and b"d must be" in L.csa_last_error()
+    assert call(D_I=96) == 2
+    assert call(m=0) == 1
+    assert call(fmt=7) == 1
