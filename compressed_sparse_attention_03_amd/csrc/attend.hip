@@ -171,11 +171,13 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
   constexpr int QS = D + 8;           // q^ row stride (bf16), padded likewise
   constexpr int BUF = (16 * QS * 2 > NW * 32 * RS) ? 16 * QS * 2 : NW * 32 * RS;
   static_assert(QCH * 16 <= NT, "the q prologue needs one thread per 32 channels of a head");
+  static_assert(QCH >= 2 && QCH <= 16, "a head's prologue threads share one row of 16 lanes");
+  static_assert(D / 2 <= NT, "one rotary pair per thread");
   // LDS: q^ during the prologue, then (same bytes) every wave's staging of its current pair of
   // chunks (their row slices) for the transposing V reads; the waves' S partials (two pairs of chunks, double-buffered); row
   // codes; rotary angles.
   __shared__ __align__(16) unsigned char s_buf[BUF];
-  __shared__ __align__(16) float4 s_part[2][2][NW][64];
+  __shared__ __align__(16) float4 s_part[3][2][NW][64];
   __shared__ int s_row[kMaxRowsPerSplit];
   __shared__ float s_cs[256], s_sn[256];
   uint16_t *s_q = reinterpret_cast<uint16_t *>(s_buf);
@@ -206,11 +208,13 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
     for (int k = 0; k < 4; ++k) { qraw[k] = src[k]; wraw[k] = wsrc[k]; }
   }
   __builtin_amdgcn_sched_barrier(0);             // keep the q loads ahead of the position wait
+  // the rotary frequencies do not need the position: thread u forms pair u's (rope_dim / 2 <= D / 2
+  // <= NT pairs) while the position is on its way
+  const int npairs = a.rope_dim / 2;
+  const double rf = tid < npairs ? rope_turns_per_pos(tid, rope_rate(a.rope_dim, a.log2_base)) : 0.0;
   const int64_t t = a.q_pos0[b] + s_idx;
   const int64_t n_vis = a.topk_idx ? 0 : min(a.n_entries[b], div_count(t + 1, a.m));
-  const int npairs = a.rope_dim / 2;
-  const double rate = rope_rate(a.rope_dim, a.log2_base);
-  for (int u = tid; u < npairs; u += NT) rope_cos_sin(t, u, rate, &s_cs[u], &s_sn[u]);
+  if (tid < npairs) rope_cos_sin_f(t, rf, &s_cs[tid], &s_sn[tid]);
   const uint16_t *ent_b = a.entries + int64_t(b) * a.N_cap * D + C * wave;
   const uint16_t *win_b = a.win_rows + int64_t(b) * a.W_cap * D + C * wave;
   // the fused path's running merge of the slices (per head r; lane's channels as in O^T below)
@@ -266,8 +270,11 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
         ss += x * x;
       }
     }
-#pragma unroll
-    for (int o = 1; o < QCH; o <<= 1) ss += __shfl_xor(ss, o, 64);   // the head's QCH threads
+    // over the head's QCH (2 to 16) consecutive threads, inside one row of 16 lanes: DPP
+    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0xb1, 0xf, 0xf, false));
+    if constexpr (QCH >= 4) ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x4e, 0xf, 0xf, false));
+    if constexpr (QCH >= 8) ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x141, 0xf, 0xf, false));
+    if constexpr (QCH >= 16) ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x140, 0xf, 0xf, false));
     const float inv = qhead < a.H ? rsqrtf(ss / float(D) + a.eps) * a.scale_log2 : 0.f;
     const bool has_w = a.q_norm_w != nullptr;
     const int rope0 = D - a.rope_dim;
@@ -327,9 +334,18 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
   //   for the 32 rows (every wave runs the same arithmetic on the same logits, so m and l agree
   //   across the waves); the rows go to the wave's staging area and two transposing LDS reads give
   //   the A operand V^T[16 channels x 32 rows] of O^T += V^T P^T.
-  auto pair = [&](int slot0, int parity) __attribute__((always_inline)) {
-    // The V^T fragments do not depend on P: the rows are staged and read back first, so the LDS
-    // round trip overlaps the S^T products, the exchange and the softmax.
+  // A pair is taken in two halves, software-pipelined one pair apart: half A stages the pair's
+  // rows, reads its V^T fragments back and forms this wave's S^T partial (MFMAs), which it leaves
+  // in LDS; half B sums the waves' partials (the exchange, one barrier) and runs the softmax and
+  // O^T += V^T P^T.  After pair p's exchange, half A of pair p + 1 is issued before the rest of
+  // pair p's half B, so the next pair's LDS traffic and products run through this pair's softmax
+  // chain.  The arithmetic of each pair is unchanged (the same bits as taking the halves back to
+  // back).  Partial buffers rotate (pair p uses p mod 3): pair p + 1's are written after the
+  // barrier of pair p, which no wave passes before every wave has read pair p - 1's.
+  Frag8 vtp[2][NB];                               // V^T fragments of the pairs in flight (by parity)
+  v4f spp[2][2];                                  // their S^T (this wave's partial, then the sum)
+  uint64_t vmp[2][2];                             // their rows' validity masks
+  auto pair_a = [&](int slot0, int par, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -339,36 +355,46 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
     // V^T fragment of block nb: lane (n, g) reads row 4g + n/4, channels 16 nb + 4(n%4) .. +3;
     // the transposing read hands lane (n, g) rows 4g .. 4g+3 of channel 16 nb + n
     const unsigned char *vbase = stage + (4 * g + (r >> 2)) * RS + 8 * (r & 3);
-    Frag8 vt[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      vt[nb].h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vbase + 32 * nb));
-      vt[nb].h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vbase + 16 * RS + 32 * nb));
+      vtp[par][nb].h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vbase + 32 * nb));
+      vtp[par][nb].h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vbase + 16 * RS + 32 * nb));
     }
-    v4f sp[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      sp[c] = v4f{0.f, 0.f, 0.f, 0.f};
+      spp[par][c] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        sp[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[slot0 + c][s].b, qf[s].b, sp[c], 0, 0, 0);
+        spp[par][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[slot0 + c][s].b, qf[s].b, spp[par][c], 0, 0, 0);
     }
     if constexpr (NW > 1) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) s_part[parity][c][wave][lane] = make_float4(sp[c][0], sp[c][1], sp[c][2], sp[c][3]);
+      for (int c = 0; c < 2; ++c)
+        s_part[buf][c][wave][lane] = make_float4(spp[par][c][0], spp[par][c][1], spp[par][c][2], spp[par][c][3]);
+    }
+    vmp[par][0] = __ballot(codes[slot0] >= 0);
+    vmp[par][1] = __ballot(codes[slot0 + 1] >= 0);
+  };
+  // half B, first the exchange: the waves' partials of the pair summed in wave order
+  auto pair_x = [&](int par, int buf) __attribute__((always_inline)) {
+    if constexpr (NW > 1) {
       lds_barrier();
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        float4 x = s_part[parity][c][0][lane];
+        float4 x = s_part[buf][c][0][lane];
 #pragma unroll
         for (int w = 1; w < NW; ++w) {
-          const float4 y = s_part[parity][c][w][lane];
+          const float4 y = s_part[buf][c][w][lane];
           x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
         }
-        sp[c] = v4f{x.x, x.y, x.z, x.w};
+        spp[par][c] = v4f{x.x, x.y, x.z, x.w};
       }
     }
-    const uint64_t vm0 = __ballot(codes[slot0] >= 0), vm1 = __ballot(codes[slot0 + 1] >= 0);
+  };
+  // then the softmax and O^T += V^T P^T
+  auto pair_b = [&](int par) __attribute__((always_inline)) {
+    const v4f sp[2] = {spp[par][0], spp[par][1]};
+    const uint64_t vm0 = vmp[par][0], vm1 = vmp[par][1];
     float sv[8], cmax = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -400,7 +426,7 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
     pf.h[0] = pack4(p[0], p[1], p[2], p[3]);
     pf.h[1] = pack4(p[4], p[5], p[6], p[7]);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[nb].b, pf.b, o[nb], 0, 0, 0);
+    for (int nb = 0; nb < NB; ++nb) o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vtp[par][nb].b, pf.b, o[nb], 0, 0, 0);
   };
   // ---- end of a slice: this wave's channels of O / l and the slice's log2-sum-exp ------------
   auto end_slice = [&]() __attribute__((always_inline)) {
@@ -448,22 +474,38 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
       lds_barrier();                              // the previous segment's readers of the row codes are done
       begin_segment(seg);
     }
-    for (int j0 = 0; j0 < n_chunks; j0 += RING) {
+    // pair q uses ring slots 2 (q mod 2) and +1 and partial buffer q mod 3; its slots are refilled
+    // (with pair q + 2's chunks) once its half A has read them
+    // (the fused kernel, short of registers for two pairs in flight, takes the halves back to back)
+    const int np = (n_chunks + 1) >> 1;
+    if constexpr (!FUSED) pair_a(0, 0, 0);
+    for (int q0 = 0; q0 < np; q0 += 2) {
 #pragma unroll
-      for (int h = 0; h < RING / 2; ++h) {
-        const int j = j0 + 2 * h;
-        if (j < n_chunks) {
-          pair(2 * h, h & 1);
+      for (int h = 0; h < 2; ++h) {
+        const int q = q0 + h;
+        if (q < np) {
+          const int j = 2 * q;
           if constexpr (FUSED) {
+            pair_a(2 * h, 0, q % 3);
+            issue(j + RING, 2 * h);               // pair q's slots: pair q + 2
+            issue(j + 1 + RING, 2 * h + 1);
+            pair_x(0, q % 3);
+            pair_b(0);
             if ((j + 2) % cps == 0 && j + 2 < n_chunks) {   // a slice ends inside the stream
               end_slice();
               ++split;
               reset_slice();
             }
+          } else {
+            // pair q's exchange first (its partials were written an iteration ago), then pair
+            // q + 1's half A, whose LDS traffic and products overlap pair q's softmax
+            pair_x(h, q % 3);
+            issue(j + RING, 2 * h);               // pair q's slots: pair q + 2
+            issue(j + 1 + RING, 2 * h + 1);
+            if (q + 1 < np) pair_a(2 * (h ^ 1), h ^ 1, (q + 1) % 3);
+            pair_b(h);
           }
         }
-        issue(j + RING, 2 * h);                  // refill the pair's slots
-        issue(j + 1 + RING, 2 * h + 1);
       }
     }
     end_slice();
