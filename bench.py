@@ -637,9 +637,11 @@ def main():
         else:
             ab = leg.step_bytes
             dur = (kt.get("attend_split", 0.0) + kt.get("attend_combine", 0.0)) * 1e-6
+            ts, tc = profile_traffic("attend_split", w.name), profile_traffic("attend_combine", w.name)
             r["roofline"] = {"kernel": "attend_split+attend_combine", "bound": "hbm", "achieved": ab / dur / 1e9,
                              "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ab / dur / 1e9 / PEAK_HBM_GBS,
-                             "traffic": None, "algorithmic_bytes": ab, "avg_us": kt.get("attend_split")}
+                             "traffic": None if ts is None or tc is None else ts + tc,
+                             "algorithmic_bytes": ab, "avg_us": kt.get("attend_split")}
         results[name] = r
         log(json.dumps(r))
         leg.free()

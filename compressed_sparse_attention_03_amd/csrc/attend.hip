@@ -108,10 +108,14 @@ __device__ __forceinline__ AttendTile attend_tile(const AttendArgs &a, int64_t n
 }
 
 // The merge of slice partials, shared by the combine kernel and the fused path so that both give
-// the same bits: a slice's partial is x = O / l with log2-sum-exp m + log2 l; slices are merged in
-// order with a running maximum M and sum L (explicit roundings: no contraction choices).
+// the same bits: a slice's partial is x = O / l, rounded to bf16 (the split-K path stores it so:
+// half the bytes of fp32 through HBM and back, and a rounding like the output's own), with
+// log2-sum-exp m + log2 l in fp32; slices are merged in order with a running maximum M and sum L
+// (explicit roundings: no contraction choices).
 __device__ __forceinline__ float slice_scale(float l) { return l > 0.f ? 1.0f / l : 0.f; }
-__device__ __forceinline__ float slice_value(float o, float inv) { return __fmul_rn(o, inv); }
+__device__ __forceinline__ float slice_value(float o, float inv) {
+  return float(__bf16(__fmul_rn(o, inv)));                    // v_cvt_pk_bf16_f32: round to nearest even
+}
 __device__ __forceinline__ float slice_lse2(float m, float l) { return l > 0.f ? m + log2f(l) : -INFINITY; }
 struct MergeWeights {
   float c, w;   // factor of the running sums, weight of the slice
@@ -451,13 +455,14 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
                                                        slice_value(o[nb][2], inv), slice_value(o[nb][3], inv));
       if (a.lse && wave == 0 && g == 0) a.lse[qi * a.H + gh] = ls * 0.6931471805599453f;
     } else {
-      float *po = static_cast<float *>(a.workspace);
-      float *plse = po + n_queries * a.H * a.plan.n_splits * D;
-      float *dst = po + ((qi * a.H + gh) * a.plan.n_splits + split) * int64_t(D) + c0;
+      // workspace: bf16 partials [query, head, slice, D], then fp32 log2-sum-exps [query, head, slice]
+      uint16_t *po = static_cast<uint16_t *>(a.workspace);
+      float *plse = reinterpret_cast<float *>(po + n_queries * a.H * a.plan.n_splits * D);
+      uint16_t *dst = po + ((qi * a.H + gh) * a.plan.n_splits + split) * int64_t(D) + c0;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        *reinterpret_cast<float4 *>(dst + 16 * nb) = make_float4(slice_value(o[nb][0], inv), slice_value(o[nb][1], inv),
-                                                                 slice_value(o[nb][2], inv), slice_value(o[nb][3], inv));
+        *reinterpret_cast<v4s *>(dst + 16 * nb) = pack4(slice_value(o[nb][0], inv), slice_value(o[nb][1], inv),
+                                                       slice_value(o[nb][2], inv), slice_value(o[nb][3], inv));
       if (wave == 0 && g == 0) plse[(qi * a.H + gh) * a.plan.n_splits + split] = ls;
     }
   }
@@ -534,8 +539,9 @@ __global__ void __launch_bounds__(D / 4) attend_combine_kernel(AttendArgs a, int
   constexpr int kBatch = 8;                       // slices whose loads are in flight together
   const int64_t qh = blockIdx.x;                  // query * H + head
   const int ns = a.plan.n_splits;
-  const float *po = static_cast<const float *>(a.workspace) + qh * ns * int64_t(D);
-  const float *plse = static_cast<const float *>(a.workspace) + n_queries * a.H * ns * int64_t(D) + qh * ns;
+  const uint16_t *po = static_cast<const uint16_t *>(a.workspace) + qh * ns * int64_t(D);
+  const float *plse = reinterpret_cast<const float *>(static_cast<const uint16_t *>(a.workspace) +
+                                                      n_queries * a.H * ns * int64_t(D)) + qh * ns;
   const int ch = threadIdx.x * 4;
   // every slice's log2-sum-exp and partial are loaded before any is used (one round trip per
   // batch of slices), then merged in slice order with a running maximum
@@ -548,7 +554,8 @@ __global__ void __launch_bounds__(D / 4) attend_combine_kernel(AttendArgs a, int
     for (int j = 0; j < kBatch; ++j) {
       const int s = s0 + j < ns ? s0 + j : ns - 1;
       ls[j] = plse[s];
-      x[j] = *reinterpret_cast<const float4 *>(po + s * int64_t(D) + ch);
+      const uint2 w = *reinterpret_cast<const uint2 *>(po + s * int64_t(D) + ch);
+      x[j] = make_float4(bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y));
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
@@ -594,7 +601,7 @@ AttendPlan plan_attend(int64_t n_queries, int H, int64_t n_sel, int window, int 
 size_t attend_workspace_bytes(int64_t n_queries, int H, int D, int64_t n_sel, int window) {
   AttendPlan p = plan_attend(n_queries, H, n_sel, window, D);
   if (p.n_splits == 1 || p.fused) return 256;
-  return size_t(n_queries * H * p.n_splits * (int64_t(D) + 1) * 4 + 256);
+  return size_t(n_queries * H * p.n_splits * (int64_t(D) * 2 + 4) + 256);   // bf16 partials, fp32 lse
 }
 
 // ---- the library's own scratch for csa_attend_noalloc -------------------------------------------

@@ -231,14 +231,14 @@ def test_quantize_query_rejects_bad_arguments():
 
 
 def test_attend_noalloc_rejects_shapes_beyond_its_scratch():
-    # 16 decode queries of 128 heads x 512 over 2,048 + 128 rows run split-K with 56 MiB of
-    # partials, more than the 32 MiB scratch; the check happens on the host before any HIP call
-    # (nothing is launched, no device needed)
+    # 16 decode queries of 128 heads x 512 over 2,048 + 512 rows run split-K (16 slices) with
+    # 32.1 MiB of partials, more than the 32 MiB scratch; the check happens on the host before any
+    # HIP call (nothing is launched, no device needed)
     L = ops.lib()
     v = ctypes.c_void_p(16)
-    need = L.csa_attend_workspace_bytes(16, 1, 128, 512, 2048, 128)
+    need = L.csa_attend_workspace_bytes(16, 1, 128, 512, 2048, 512)
     assert need > (32 << 20)
-    st = L.csa_attend_noalloc(v, None, v, 8192, v, 2048, v, 128, v, v, 16, 1, 128, 512, 64, 128,
+    st = L.csa_attend_noalloc(v, None, v, 8192, v, 2048, v, 512, v, v, 16, 1, 128, 512, 64, 512,
                               ctypes.c_float(0.044), ctypes.c_float(10000.0), ctypes.c_float(1e-6), v, None, None)
     assert st == 3
     assert b"scratch" in L.csa_last_error()

@@ -41,7 +41,7 @@ def _both(args, rope, W):
 
 
 def test_noalloc_matches_csa_attend_on_two_calls_the_second_smaller():
-    # first: 8 decode queries of 64 x 512 heads over 1,024 + 128 rows, split-K (8.4 MB of partials);
+    # first: 8 decode queries of 64 x 512 heads over 1,024 + 128 rows, split-K (4.2 MB of partials);
     # second: 2 queries of 16 x 128 heads over 256 + 64 rows, split-K into far less of the scratch
     cases = [(dict(B=8, H=64, D=512, N=20000, k=1024, W=128), 64),
              (dict(B=2, H=16, D=128, N=3000, k=256, W=64), 32)]
@@ -60,8 +60,9 @@ def test_noalloc_without_split_and_rejection_of_oversized_shapes():
     say("case: csa_attend_noalloc fused plan B=512 H=16 D=128 k=512 W=64")
     ref_o, ref_l, out, lse = _both(_case(93, B=512, H=16, D=128, N=2000, k=512, W=64), 32, 64)
     assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
-    say("case: csa_attend_noalloc oversized B=16 H=128 D=512 k=2048 W=128")
-    args = _case(94, B=16, H=128, D=512, N=4000, k=2048, W=128)
+    say("case: csa_attend_noalloc oversized B=16 H=128 D=512 k=2048 W=512")
+    assert ops.lib().csa_attend_workspace_bytes(16, 1, 128, 512, 2048, 512) > (32 << 20)
+    args = _case(94, B=16, H=128, D=512, N=4000, k=2048, W=512)
     out = torch.empty_like(args[0])
     with pytest.raises(RuntimeError, match="scratch"):
-        ops.csa_attend_noalloc(*args, rope_dim=64, window=128, out=out)
+        ops.csa_attend_noalloc(*args, rope_dim=64, window=512, out=out)
