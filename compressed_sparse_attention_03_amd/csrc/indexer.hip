@@ -8,18 +8,41 @@
 //
 // score[i] = sum_h w[h] * max(0, <q~_h, k~_i>)  (the form stated in csa.h).
 //
-// Kernel 1 (index_score): grid (tiles, queries).  The query's [H_I x 128] head matrix is quantised
-// once per workgroup into LDS and held as MFMA A-operands; key tiles stream from HBM in groups of
-// 16 entries, each group costing one v_mfma_scale_f32_16x16x128_f8f6f4 per 16 heads (fp8 e4m3,
-// or MXFP4 with its e8m0 block scales applied by the instruction).  The tile's scores stay in LDS;
-// a block radix select keeps the tile's `cand` best (score, index) keys, written in ascending
-// index order together with the smallest kept key.
-// Kernel 1b (index_score_multi_kernel, calls with eight or more queries per sequence): a tile of
-// 512 keys is loaded into LDS once and scored against eight queries, one per wave, each wave
-// keeping its own candidates (same scores, same candidate layout).
-// Kernel 2 (index_merge): one workgroup per query selects the k best keys among all candidates.
-// A tile whose smallest kept key beats the k-th best may hide further winners; such tiles are
-// re-scored in the merge workgroup (exact, slow, rare).
+// With quantised keys every path first encodes the query's [H_I x 128] head matrix like the keys
+// (prep_query_slot: fp8 e4m3 with a per-head scale, or MXFP4 with e8m0 block scales; the head
+// weight and scale are folded into one factor per head) and holds it as MFMA A-operands.  A group
+// of 16 entries then costs one v_mfma_scale_f32_16x16x128_f8f6f4 per 16 heads, the block scales
+// applied by the instruction.  fp32 keys are scored by plain fp32 dot products.
+// Which kernels run is fixed by plan_index:
+//
+//   quantised keys, fewer than eight queries per sequence or the raw scores asked for (the
+//   streaming path): index_stream_kernel, grid (segments, queries).
+//     A segment of up to 4,096 entries per workgroup streams through a ring of LDS chunks filled by
+//     direct-to-LDS buffer loads; its scores stay in LDS and its best keys are published as
+//     candidates.  The last segment workgroup of a query to finish merges them into the query's
+//     top-k (arrive_last; index_merge_kernel after it when the candidates exceed what one workgroup
+//     holds).
+//   quantised keys, eight or more queries per sequence (a prefill chunk, the shared-tile path):
+//     index_query_prep_kernel encodes every query once into the workspace, index_score_multi_kernel
+//     scores one 512-entry tile against eight queries (one per wave), index_merge_kernel merges.
+//   fp32 keys: index_score_kernel, one tile of up to 2,048 entries per workgroup, with the merge in
+//     each query's last tile workgroup.
+//
+// Keeping a segment's candidates: an estimate of the score distribution (per-wave mean and mean
+// absolute deviation) places four trial thresholds at normal quantiles around the wanted count;
+// one pass counts the entries above each, and the kept entries' output positions come from the
+// same pass.  When no threshold lands in the accepted band the bucket select over the score keys'
+// order bits decides instead.  The merge selects the exact k-th best key over all candidates; a
+// segment whose smallest kept key beats it may hide further winners and is re-scored by the
+// merging workgroup (exact, slow, rare).
+//
+// Workspace (bytes, from the start; n_q = queries, S = segments or tiles per query):
+//   candidate keys  n_q * S * cand * 8   (score order bits << 32 | entry index, ascending index)
+//   smallest kept   n_q * S * 8
+//   counts          n_q * S * 4
+//   then, 256-aligned, either the arrival counters (n_q * kCounterStride ints; every merge leaves
+//   its counter at zero, so a zeroed workspace stays valid across calls) or, on the shared-tile
+//   path, every query's encoded image (n_q * sizeof(QueryLds)).
 #include "common.h"
 #include "internal.h"
 
@@ -1257,8 +1280,9 @@ __global__ void __launch_bounds__(kStreamThreads, 1) index_stream_kernel(IndexAr
 // For calls with many queries per sequence (a prefill chunk) the same keys are scored against
 // consecutive queries.  Workgroup = (tile of 512 entries, 8 consecutive queries, sequence): the
 // tile's quantised keys are loaded into LDS once and every wave scores them against its own query
-// (quantised straight into MFMA operands, no LDS), then selects its candidates with a wave-local
-// radix select -- no workgroup barrier after the tile is loaded.  Scores are bit-identical to
+// (encoded once per call by index_query_prep_kernel; each wave copies the image into its LDS slot
+// before the tile arrives and reads its MFMA operands from there), then selects its candidates
+// with a wave-local radix select -- no workgroup barrier after the tile is loaded.  Scores are bit-identical to
 // index_score_kernel's (the same MFMA operands and epilogue order), so the selection is too.
 constexpr int kMultiQ = 8;              // queries per workgroup, one per wave
 constexpr int kMultiTile = 512;         // entries per tile

@@ -32,7 +32,10 @@
  *     It must be zero-filled once before its first use: it holds counters through which the
  *     last workgroup of a query learns that the others are done, and every completed call leaves
  *     them at zero again (a call that was launched but did not complete -- a fault -- may leave
- *     them non-zero: zero the workspace again before reusing it).
+ *     them non-zero: zero the workspace again before reusing it).  csa_index_topk keeps its
+ *     counters after its candidate arrays, at an offset that depends on B * Sq, N_cap, topk and
+ *     key_format (and on whether scores are asked for): zero its workspace again before a call
+ *     that differs in any of these.
  *   - Results are deterministic: fixed reduction orders, no floating-point atomics.
  */
 #ifndef CSA_H
