@@ -3,7 +3,7 @@ the dominant kernel and the CPU oracle timed beside it.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--legs main,d128,c32k,hca,flash,append,prefill,compress,oproj]
-                    [--mode bench|copy|summarize-trace|summarize-traffic]
+                    [--mode bench|copy|summarize-trace|summarize-traffic|summarize-mfma|summarize-counters]
 
 One step = one decode pass of the whole hot path over one batch: csa_index_topk (lightning-indexer
 scores + top-k) then csa_attend (shared-KV attention over the selected entries + window) for CSA;
@@ -539,6 +539,46 @@ def summarize_traffic(fetch_db: str, write_db: str, copy_fetch_db: str, copy_wri
         f"traffic_bytes_per_dispatch = {traffic:.0f}"])
 
 
+def summarize_counters(dbs, kernels) -> str:
+    """Per-kernel averages per dispatch (summed over the GPU's instances of each counter) of every
+    counter in one or more `rocprofv3 --pmc` databases, and the ratios that share a unit: the share
+    of wave cycles spent waiting (on anything; on an instruction's dependency), issuing (any
+    instruction; VALU; LDS; vector memory), LDS bank-conflict cycles per LDS-active cycle and the
+    L2 hit rate."""
+    import sqlite3
+    vals = {k: {} for k in kernels}
+    for db in dbs:
+        cur = sqlite3.connect(db).cursor()
+        names = [r[0] for r in cur.execute("select distinct counter_name from pmc_events")]
+        for k in kernels:
+            for c in names:
+                r = cur.execute("select avg(v), count(*) from (select sum(counter_value) as v from pmc_events where "
+                                "counter_name = ? and name like ? group by dispatch_id)", (c, f"%{k}%")).fetchone()
+                if r and r[1]:
+                    vals[k][c] = (r[0], r[1])
+    out = []
+    for k in kernels:
+        v = {c: x[0] for c, x in vals[k].items()}
+        n = max([x[1] for x in vals[k].values()] + [0])
+        out.append(f"{k} ({n} dispatches)")
+        for c in sorted(v):
+            out.append(f"  {c} = {v[c]:.4g}")
+        ratio = lambda a, b: (v[a] / v[b]) if a in v and b in v and v[b] else None
+        derived = [("wave cycles waiting (any)", ratio("SQ_WAIT_ANY", "SQ_WAVE_CYCLES")),
+                   ("wave cycles waiting on a dependency", ratio("SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES")),
+                   ("wave cycles issuing (any)", ratio("SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES")),
+                   ("wave cycles issuing VALU", ratio("SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES")),
+                   ("wave cycles issuing LDS", ratio("SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES")),
+                   ("wave cycles issuing vector memory", ratio("SQ_ACTIVE_INST_VMEM", "SQ_WAVE_CYCLES")),
+                   ("LDS bank-conflict cycles per LDS-active cycle", ratio("SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS"))]
+        if "TCC_HIT_sum" in v and "TCC_MISS_sum" in v and v["TCC_HIT_sum"] + v["TCC_MISS_sum"]:
+            derived.append(("L2 hit rate", v["TCC_HIT_sum"] / (v["TCC_HIT_sum"] + v["TCC_MISS_sum"])))
+        for name, x in derived:
+            if x is not None:
+                out.append(f"  [{name}] = {x:.3f}")
+    return "\n".join(out)
+
+
 MFMA_COUNTERS = ("MfmaUtil", "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_F6F4",
                  "SQ_INSTS_VALU_MFMA_MOPS_BF16")
 
@@ -572,7 +612,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--legs", default="main,d128,c32k,hca,flash,append,prefill,compress,oproj")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy", "summarize-trace", "summarize-traffic",
-                                                        "summarize-mfma"])
+                                                        "summarize-mfma", "summarize-counters"])
     ap.add_argument("--db", nargs="*", default=[], help="rocprofv3 databases for the summarize modes: one "
                     "kernel-trace db; or FETCH, WRITE, copy-FETCH, copy-WRITE dbs")
     ap.add_argument("--kernel", default="index_score_kernel")
@@ -594,6 +634,9 @@ def main():
         return
     if args.mode == "summarize-traffic":
         print(summarize_traffic(*args.db[:4], kernel=args.kernel, source=args.source))
+        return
+    if args.mode == "summarize-counters":
+        print(summarize_counters(args.db, args.kernel.split(",")))
         return
     legs = args.legs.split(",")
     table = {"main": gen.CSA_DECODE_1M, "d128": gen.CSA_DECODE_128K, "c32k": gen.CSA_DECODE_32K,

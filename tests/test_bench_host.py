@@ -89,3 +89,23 @@ def test_summarize_mfma_sums_shader_engines_per_dispatch(tmp_path):
     con.close()
     out = bench.summarize_mfma(str(db), ["k<1>"]).splitlines()
     assert out[2] == "| k<1> | 2 | 21.5 | 0.5 | 0.0 | 0.0 |"      # 1e6 x 512 ops = 0.512 GFLOP
+
+
+def test_summarize_counters_sums_instances_and_forms_ratios(tmp_path):
+    # two databases (counter sets of separate runs), two dispatches, two instances per counter
+    a, b = tmp_path / "a.db", tmp_path / "b.db"
+    for db, rows in ((a, [("SQ_WAVE_CYCLES", 100.0), ("SQ_WAIT_INST_ANY", 30.0)]),
+                     (b, [("TCC_HIT_sum", 3.0), ("TCC_MISS_sum", 1.0)])):
+        con = sqlite3.connect(db)
+        con.execute("create table pmc_events (name text, dispatch_id int, counter_name text, counter_value real)")
+        for d in (1, 2):
+            for c, v in rows:
+                con.executemany("insert into pmc_events values (?, ?, ?, ?)",
+                                [("void csa::attend_split_kernel<512, false>(...)", d, c, v / 2)] * 2)
+        con.commit()
+        con.close()
+    out = bench.summarize_counters([str(a), str(b)], ["attend_split_kernel"])
+    assert "attend_split_kernel (2 dispatches)" in out
+    assert "SQ_WAVE_CYCLES = 100" in out and "SQ_WAIT_INST_ANY = 30" in out
+    assert "[wave cycles waiting on a dependency] = 0.300" in out
+    assert "[L2 hit rate] = 0.750" in out
