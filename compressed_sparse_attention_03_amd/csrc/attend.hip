@@ -282,6 +282,19 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
     const float inv = qhead < a.H ? rsqrtf(ss / float(D) + a.eps) * a.scale_log2 : 0.f;
     const bool has_w = a.q_norm_w != nullptr;
     const int rope0 = D - a.rope_dim;
+    // the rotary pairs of this thread's 32 channels (pair u = (ch - rope0) / 2 = u0 + p), read from
+    // LDS together so that one wait covers them all; reads below the rotated part are clamped
+    // to pair 0 and not used
+    float rcs[16], rsn[16];
+    {
+      const int u0 = (32 * qc - rope0) >> 1;       // rope0 is even: exact
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        const int u = max(u0 + p, 0);
+        rcs[p] = s_cs[u];
+        rsn[p] = s_sn[u];
+      }
+    }
     uint4 *dst = reinterpret_cast<uint4 *>(s_q + qh * QS + 32 * qc);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -294,8 +307,7 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
         for (int e = 0; e < 8; e += 2) {
           const int ch = ch0 + e;
           if (ch >= rope0) {
-            const int u = (ch - rope0) >> 1;
-            const float cs = s_cs[u], sn = s_sn[u], x0 = v[e], x1 = v[e + 1];
+            const float cs = rcs[(8 * k + e) >> 1], sn = rsn[(8 * k + e) >> 1], x0 = v[e], x1 = v[e + 1];
             v[e] = x0 * cs - x1 * sn;
             v[e + 1] = x0 * sn + x1 * cs;
           }
