@@ -60,20 +60,10 @@ __device__ __forceinline__ float elem8(const uint4 &w, int e) {
 constexpr int kMaxRowsPerSplit = 2048;
 
 // Row code of slot `ri` of the query's row list: an entry index (< N_cap), N_cap + window row, or
-// -1 when the slot is empty.
-__device__ __forceinline__ int row_code(const AttendArgs &a, int64_t qi, int b, int64_t t, int64_t n_vis,
-                                        int64_t ri) {
-  if (ri < a.n_sel) {
-    int64_t e;
-    if (a.topk_idx) {
-      e = a.topk_idx[qi * a.n_sel + ri];
-      if (e < 0 || e >= a.N_cap) return -1;
-    } else {
-      e = ri;
-      if (e >= n_vis) return -1;
-    }
-    return int(e);
-  }
+// -1 when the slot is empty.  Slots below n_sel: selected entry e (SEL; e read from topk_idx) or
+// entry ri (HCA, visible when below n_vis); then the window.
+__device__ __forceinline__ int selected_code(const AttendArgs &a, int e) { return (e < 0 || e >= a.N_cap) ? -1 : e; }
+__device__ __forceinline__ int window_code(const AttendArgs &a, int b, int64_t t, int64_t ri) {
   const int64_t w = ri - a.n_sel;
   if (w >= a.window) return -1;
   const int64_t p = t - a.window + 1 + w;                  // window position
@@ -82,6 +72,13 @@ __device__ __forceinline__ int row_code(const AttendArgs &a, int64_t qi, int b, 
   const int64_t wr = p - a.win_pos0[b];
   if (wr < 0 || wr >= a.W_cap) return -1;
   return int(a.N_cap + wr);
+}
+template <bool SEL>
+__device__ __forceinline__ int row_code(const AttendArgs &a, int64_t qi, int b, int64_t t, int64_t n_vis,
+                                        int64_t ri) {
+  if (ri >= a.n_sel) return window_code(a, b, t, ri);
+  if constexpr (SEL) return selected_code(a, a.topk_idx[qi * a.n_sel + ri]);
+  return ri < n_vis ? int(ri) : -1;
 }
 
 // Workgroup -> (query, split, head block).  Workgroups are dispatched to the 8 XCDs round-robin by
@@ -163,7 +160,7 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 // FUSED: one workgroup per (query, head block) takes every slice in order and merges them in
 // registers exactly as the combine kernel does (for calls with many queries: no workspace, same
 // bits as the split-K path).
-template <int D, bool FUSED>
+template <int D, bool FUSED, bool SEL>
 __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(AttendArgs a, int64_t n_queries) {
   constexpr int C = slice_of<D>(), NW = waves_of<D>(), NT = 64 * NW;
   constexpr int NS = C / 32;          // 32-channel steps of the wave's slice (QK^T)
@@ -196,9 +193,27 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
   const int split_first = FUSED ? 0 : tl.split;
   const int split_end = FUSED ? a.plan.n_splits : tl.split + 1;
 
-  // ---- prologue.  The raw q chunk (and norm weights) of this thread are loaded first -- before
-  // the query's position is read, whose round trip they do not need -- and loads complete in
+  // A segment of the row list -- one slice, or in the fused path every slice when the whole list
+  // fits the row-code buffer (one continuous stream of chunks, no restart between slices) --
+  // begins with its row codes in LDS and its first chunks' loads in flight.
+  const bool stream = FUSED && a.plan.n_rows <= kMaxRowsPerSplit;
+  const int n_seg = stream ? 1 : split_end - split_first;
+  // ---- prologue.  The selection behind the first segment's row-code table (thread tid: rows
+  // tid + k NT) is read first of all: it needs no position, so its round trip runs beside the
+  // position's instead of after it.  Reads are clamped to the query's selection; a clamped value
+  // is not used.  Then the raw q chunk (and norm weights) of this thread -- loads complete in
   // issue order, so anything issued later (the row prefetch) does not delay them.
+  const int64_t r0_first = stream ? 0 : int64_t(split_first) * a.plan.rows_per_split;
+  const int nr_first = int((stream ? int64_t(a.plan.n_rows)
+                                   : min(int64_t(a.plan.n_rows), r0_first + a.plan.rows_per_split)) - r0_first);
+  constexpr int KP = 4;
+  int pre_e[KP];
+  if constexpr (SEL) {
+    const int32_t *sel = a.topk_idx + qi * a.n_sel;
+    const int64_t last = a.n_sel - 1;
+#pragma unroll
+    for (int k = 0; k < KP; ++k) pre_e[k] = sel[min(r0_first + min(tid + k * NT, nr_first - 1), last)];
+  }
   const bool qthread = tid < 16 * QCH;
   const int qh = tid / QCH, qc = tid % QCH;
   const int qhead = hb * 16 + qh;
@@ -217,7 +232,7 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
   const int npairs = a.rope_dim / 2;
   const double rf = tid < npairs ? rope_turns_per_pos(tid, rope_rate(a.rope_dim, a.log2_base)) : 0.0;
   const int64_t t = a.q_pos0[b] + s_idx;
-  const int64_t n_vis = a.topk_idx ? 0 : min(a.n_entries[b], div_count(t + 1, a.m));
+  const int64_t n_vis = SEL ? 0 : min(a.n_entries[b], div_count(t + 1, a.m));
   if (tid < npairs) rope_cos_sin_f(t, rf, &s_cs[tid], &s_sn[tid]);
   const uint16_t *ent_b = a.entries + int64_t(b) * a.N_cap * D + C * wave;
   const uint16_t *win_b = a.win_rows + int64_t(b) * a.W_cap * D + C * wave;
@@ -245,17 +260,25 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
 #pragma unroll
     for (int s = 0; s < NS; ++s) ring[slot][s].u = *reinterpret_cast<const uint4 *>(rp + 32 * s + 8 * g);
   };
-  // A segment of the row list -- one slice, or in the fused path every slice when the whole list
-  // fits the row-code buffer (one continuous stream of chunks, no restart between slices) --
-  // begins with its row codes in LDS and its first chunks' loads in flight.
-  const bool stream = FUSED && a.plan.n_rows <= kMaxRowsPerSplit;
-  const int n_seg = stream ? 1 : split_end - split_first;
+  // (the first segment's table takes the selection read at the start)
   auto begin_segment = [&](int seg) __attribute__((always_inline)) {
     const int64_t r0 = stream ? 0 : int64_t(split_first + seg) * a.plan.rows_per_split;
     const int64_t r1 = stream ? a.plan.n_rows : min(int64_t(a.plan.n_rows), r0 + a.plan.rows_per_split);
     nr = int(r1 - r0);
     n_chunks = (nr + 15) >> 4;
-    for (int i = tid; i < nr; i += NT) s_row[i] = row_code(a, qi, b, t, n_vis, r0 + i);
+    int i0 = tid;
+    if (seg == 0) {
+#pragma unroll
+      for (int k = 0; k < KP; ++k) {
+        const int i = tid + k * NT;
+        if (i < nr) {
+          const int64_t ri = r0 + i;
+          s_row[i] = (SEL && ri < a.n_sel) ? selected_code(a, pre_e[k]) : row_code<SEL>(a, qi, b, t, n_vis, ri);
+        }
+      }
+      i0 = tid + KP * NT;
+    }
+    for (int i = i0; i < nr; i += NT) s_row[i] = row_code<SEL>(a, qi, b, t, n_vis, r0 + i);
     lds_barrier();
 #pragma unroll
     for (int j = 0; j < RING; ++j) issue(j, j);
@@ -652,8 +675,12 @@ hipError_t launch_attend(const AttendArgs &a, hipStream_t stream) {
   const int64_t pairs = nq * (a.plan.fused ? 1 : a.plan.n_splits);
   dim3 grid(unsigned(((pairs + 7) / 8) * 8 * a.plan.n_hb));
 #define CSA_ATTEND_LAUNCH(DD)                                                                          \
-  e = a.plan.fused ? launch("attend_split", attend_split_kernel<DD, true>, grid, dim3(64 * waves_of<DD>()), stream, a, nq) \
-                   : launch("attend_split", attend_split_kernel<DD, false>, grid, dim3(64 * waves_of<DD>()), stream, a, nq)
+  if (a.topk_idx)                                                                                      \
+    e = a.plan.fused ? launch("attend_split", attend_split_kernel<DD, true, true>, grid, dim3(64 * waves_of<DD>()), stream, a, nq) \
+                     : launch("attend_split", attend_split_kernel<DD, false, true>, grid, dim3(64 * waves_of<DD>()), stream, a, nq); \
+  else                                                                                                 \
+    e = a.plan.fused ? launch("attend_split", attend_split_kernel<DD, true, false>, grid, dim3(64 * waves_of<DD>()), stream, a, nq) \
+                     : launch("attend_split", attend_split_kernel<DD, false, false>, grid, dim3(64 * waves_of<DD>()), stream, a, nq)
   switch (a.D) {
     case 64: CSA_ATTEND_LAUNCH(64); break;
     case 128: CSA_ATTEND_LAUNCH(128); break;
