@@ -424,7 +424,9 @@ __device__ __forceinline__ void append_sequence(const AppendArgs &a, int b) {
   constexpr int U = 4;                                         // slots held in registers at once
   const int per = (R + npw - 1) / npw;                         // ring slots per pooling wave
   const int s0 = pools ? wave * per : 0, s1 = pools ? min(R, s0 + per) : 0;
-  RawRow<CPL> xc[U], xz[U], xa[U], xb[U];
+  // (xb, the other bias row, is read only with overlap: without it the zeros stay unused -- a copy
+  // of xa here would make the loads wait for one another)
+  RawRow<CPL> xc[U], xz[U], xa[U], xb[U] = {};
   auto load_slots = [&](int k) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -433,7 +435,6 @@ __device__ __forceinline__ void append_sequence(const AppendArgs &a, int b) {
       load_raw<CPL>(a.tok_z + (ring0 + sl) * d + lane * CPL, xz[u]);
       load_raw<CPL>(a.bias + int64_t(sl) * d + lane * CPL, xa[u]);
       if (a.overlap) load_raw<CPL>(a.bias + int64_t((sl + m) % R) * d + lane * CPL, xb[u]);
-      else xb[u] = xa[u];
     }
   };
   if (s0 < s1) load_slots(s0);
