@@ -63,20 +63,22 @@ constexpr int kMaxRowsPerSplit = 2048;
 // -1 when the slot is empty.  Slots below n_sel: selected entry e (SEL; e read from topk_idx) or
 // entry ri (HCA, visible when below n_vis); then the window.
 __device__ __forceinline__ int selected_code(const AttendArgs &a, int e) { return (e < 0 || e >= a.N_cap) ? -1 : e; }
-__device__ __forceinline__ int window_code(const AttendArgs &a, int b, int64_t t, int64_t ri) {
+// wp0: win_pos0[b] when the window rows are stored from a position on (read once, with the query's
+// position), unused for a ring.
+__device__ __forceinline__ int window_code(const AttendArgs &a, int64_t wp0, int64_t t, int64_t ri) {
   const int64_t w = ri - a.n_sel;
   if (w >= a.window) return -1;
   const int64_t p = t - a.window + 1 + w;                  // window position
   if (p < 0) return -1;
   if (a.win_pos0 == nullptr) return int(a.N_cap + p % a.W_cap);   // ring: row of p at p mod W_cap
-  const int64_t wr = p - a.win_pos0[b];
+  const int64_t wr = p - wp0;
   if (wr < 0 || wr >= a.W_cap) return -1;
   return int(a.N_cap + wr);
 }
 template <bool SEL>
-__device__ __forceinline__ int row_code(const AttendArgs &a, int64_t qi, int b, int64_t t, int64_t n_vis,
+__device__ __forceinline__ int row_code(const AttendArgs &a, int64_t qi, int64_t wp0, int64_t t, int64_t n_vis,
                                         int64_t ri) {
-  if (ri >= a.n_sel) return window_code(a, b, t, ri);
+  if (ri >= a.n_sel) return window_code(a, wp0, t, ri);
   if constexpr (SEL) return selected_code(a, a.topk_idx[qi * a.n_sel + ri]);
   return ri < n_vis ? int(ri) : -1;
 }
@@ -232,6 +234,7 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
   const int npairs = a.rope_dim / 2;
   const double rf = tid < npairs ? rope_turns_per_pos(tid, rope_rate(a.rope_dim, a.log2_base)) : 0.0;
   const int64_t t = a.q_pos0[b] + s_idx;
+  const int64_t wp0 = a.win_pos0 ? a.win_pos0[b] : 0;
   const int64_t n_vis = SEL ? 0 : min(a.n_entries[b], div_count(t + 1, a.m));
   if (tid < npairs) rope_cos_sin_f(t, rf, &s_cs[tid], &s_sn[tid]);
   const uint16_t *ent_b = a.entries + int64_t(b) * a.N_cap * D + C * wave;
@@ -273,12 +276,12 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
         const int i = tid + k * NT;
         if (i < nr) {
           const int64_t ri = r0 + i;
-          s_row[i] = (SEL && ri < a.n_sel) ? selected_code(a, pre_e[k]) : row_code<SEL>(a, qi, b, t, n_vis, ri);
+          s_row[i] = (SEL && ri < a.n_sel) ? selected_code(a, pre_e[k]) : row_code<SEL>(a, qi, wp0, t, n_vis, ri);
         }
       }
       i0 = tid + KP * NT;
     }
-    for (int i = i0; i < nr; i += NT) s_row[i] = row_code<SEL>(a, qi, b, t, n_vis, r0 + i);
+    for (int i = i0; i < nr; i += NT) s_row[i] = row_code<SEL>(a, qi, wp0, t, n_vis, r0 + i);
     lds_barrier();
 #pragma unroll
     for (int j = 0; j < RING; ++j) issue(j, j);
