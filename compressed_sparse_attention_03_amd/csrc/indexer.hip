@@ -962,10 +962,14 @@ __device__ __forceinline__ void merge_query(const IndexArgs &a, SH &sh, int64_t 
   }
   if (tid == 0) sh.flag = 0;
   lds_barrier();
+  // (every count read first, from a clamped slot, so that one wait covers them all)
+  int kc[KPT];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) kc[k] = sh.counts[min(tid * KPT + k, slots - 1) >> cshift];
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
     const int slot = tid * KPT + k;
-    if (slot >= slots || (slot & (cand - 1)) >= sh.counts[slot >> cshift]) keys[k] = 0;
+    if (slot >= slots || (slot & (cand - 1)) >= kc[k]) keys[k] = 0;
   }
   if (k_eff == 0) {
     for (int i = tid; i < a.topk; i += NT) out[i] = -1;
