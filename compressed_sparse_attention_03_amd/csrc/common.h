@@ -205,10 +205,25 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+// Maximum over aligned groups of LANES (1, 2, 4, 8 or 16) consecutive lanes, in every lane of the
+// group: quad swaps, then the half-row and row mirrors (DPP, no LDS round trip; a maximum does not
+// depend on the order it is taken in).
+template <int LANES>
+__device__ __forceinline__ float group_max_dpp(float v) {
+  static_assert(LANES == 1 || LANES == 2 || LANES == 4 || LANES == 8 || LANES == 16, "a power of two up to 16");
+  if constexpr (LANES >= 2) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false)));
+  if constexpr (LANES >= 4) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false)));
+  if constexpr (LANES >= 8) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false)));
+  if constexpr (LANES >= 16) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false)));
   return v;
+}
+// The maximum over the wave, in every lane (rows of 16 by DPP, then the half-wave and row swaps).
+__device__ __forceinline__ float wave_max(float v) {
+  v = group_max_dpp<16>(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // ---- rotary angles ---------------------------------------------------------------------------

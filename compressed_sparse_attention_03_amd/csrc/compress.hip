@@ -123,8 +123,7 @@ __device__ __forceinline__ void encode_key_lanes(const float (&v)[CPL], int fmt,
     float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) amax = fmaxf(amax, fabsf(v[j]));
-#pragma unroll
-    for (int o = 1; o < LB; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    amax = group_max_dpp<LB>(amax);
     const uint32_t sb = mx_scale_byte(amax);
     const float inv = ldexpf(1.0f, 127 - int(sb));
     uint8_t *dst = static_cast<uint8_t *>(codes) + row * (d / 2) + lane * (CPL / 2);
@@ -388,8 +387,7 @@ __device__ void store_key_row(const AppendArgs &a, const uint16_t *x, int64_t ro
     for (int k = 0; k < 8; ++k) {
       if (64 * k >= np) break;                                  // uniform
       float amax = fmaxf(fabsf(bf16lo(w[k])), fabsf(bf16hi(w[k])));
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));   // the block's 16 lanes
+      amax = group_max_dpp<16>(amax);                           // the block's 16 lanes
       const uint32_t sb = mx_scale_byte(amax);
       const float inv = ldexpf(1.0f, 127 - int(sb));
       const int q = lane + 64 * k;
