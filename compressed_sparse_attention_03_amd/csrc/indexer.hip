@@ -479,6 +479,7 @@ constexpr int kSmallBucket = 64;
 struct alignas(16) BucketLds {
   uint32_t hist[kBins];
   uint64_t list[kSmallBucket];      // keys of the crossing bin
+  int part[8][kSmallBucket];        // partial ranks of the listed keys, one row per wave
   uint64_t kmin[16];
   uint32_t omin[16], omax[16];
   int wsum[16];
@@ -613,11 +614,36 @@ __device__ __forceinline__ uint64_t block_cut_bucket(const uint64_t (&keys)[KPT]
         }
       }
       lds_barrier();
-      if (wave == 0) {
+      if (cnt <= 16) {                                         // a short list: one wave ranks it
+        if (wave == 0) {
+          const uint64_t v = lane < cnt ? bl.list[lane] : 0;
+          int rank = 0;
+          for (int j = 0; j < cnt; ++j) rank += readlane64(v, j) > v;
+          if (lane < cnt && rank == rneed - above - 1) bl.kmin[0] = v;
+        }
+        lds_barrier();
+        return bl.kmin[0];
+      }
+      // lane l of every wave ranks listed key l against the wave's share of the list (the key of
+      // rank r has exactly r listed keys above it); wave 0 adds the waves' partial ranks
+      {
+        constexpr int SH = kSmallBucket / NW;                  // listed keys per wave
+        static_assert(NW <= 8 && SH * NW == kSmallBucket, "the list splits over the waves");
         const uint64_t v = lane < cnt ? bl.list[lane] : 0;
+        int part = 0;
+#pragma unroll
+        for (int j = 0; j < SH; ++j) {
+          const int o = wave * SH + j;
+          part += (o < cnt && bl.list[o] > v) ? 1 : 0;
+        }
+        bl.part[wave][lane] = part;
+      }
+      lds_barrier();
+      if (wave == 0 && lane < cnt) {
         int rank = 0;
-        for (int j = 0; j < cnt; ++j) rank += readlane64(v, j) > v;
-        if (lane < cnt && rank == rneed - above - 1) bl.kmin[0] = v;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) rank += bl.part[w][lane];
+        if (rank == rneed - above - 1) bl.kmin[0] = bl.list[lane];
       }
       lds_barrier();
       return bl.kmin[0];
