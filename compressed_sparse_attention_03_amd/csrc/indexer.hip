@@ -600,17 +600,24 @@ __device__ __forceinline__ uint64_t block_cut_bucket(const uint64_t (&keys)[KPT]
       return uint64_t(base + (uint32_t(bstar + 1) << shift)) << 32;
     if (above + cnt == rneed) return uint64_t(base + (uint32_t(bstar) << shift)) << 32;
     if (cnt <= kSmallBucket) {                                 // rank the crossing bin's keys (distinct)
+      // the wave's crossing keys (ballots, counted in scalar registers) get one range of the list:
+      // one LDS atomic per wave
+      uint64_t bal[KPT];
+      int tot = 0;
 #pragma unroll
       for (int k = 0; k < KPT; ++k) {
-        const bool m = bin[k] == bstar;
-        const uint64_t bal = __ballot(m);
-        if (bal) {
-          const int first = __ffsll((unsigned long long)bal) - 1;
-          int wb = 0;
-          if (lane == first) wb = atomicAdd(&bl.res[3], __popcll(bal));
-          wb = __builtin_amdgcn_readlane(wb, first);
-          const int r = __builtin_amdgcn_mbcnt_hi(uint32_t(bal >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(bal), 0));
-          if (m) bl.list[wb + r] = keys[k];
+        bal[k] = __ballot(bin[k] == bstar);
+        tot += __popcll(bal[k]);
+      }
+      if (tot) {
+        int wb = 0;
+        if (lane == 0) wb = atomicAdd(&bl.res[3], tot);
+        wb = __builtin_amdgcn_readlane(wb, 0);
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+          const int r = __builtin_amdgcn_mbcnt_hi(uint32_t(bal[k] >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(bal[k]), 0));
+          if (bin[k] == bstar) bl.list[wb + r] = keys[k];
+          wb += __popcll(bal[k]);
         }
       }
       lds_barrier();
