@@ -18,8 +18,8 @@
 //                                                   log2(e) are folded into q)
 //   O_w^T [128 ch x 16 heads] += V_w^T P^T          v_mfma_f32_16x16x16_bf16, V^T fragments from a
 //                                                   transposing LDS read of the staged rows
-// Each wave writes its channels of the slice's normalised fp32 partial; wave 0 writes the slice's
-// log2-sum-exp, and a combine kernel merges the slices in a fixed order.
+// Each wave writes its channels of the slice's normalised partial (O / l rounded to bf16); wave 0
+// writes the slice's log2-sum-exp, and a combine kernel merges the slices in a fixed order.
 #include <mutex>
 
 #include "common.h"

@@ -486,12 +486,6 @@ struct alignas(16) BucketLds {
   int res[4];                       // crossing bin, keys above it, keys in it, keys listed
 };
 
-// The score a key was made from (inverse of score_order).
-__device__ __forceinline__ float order_score(uint32_t o) {
-  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
-}
-__device__ __forceinline__ float key_score(uint64_t k) { return order_score(uint32_t(k >> 32)); }
-
 // Reductions over the wave whose result every lane holds: DPP inside rows of 16 lanes, then the
 // gfx950 half-wave and row swaps across the four rows (no readlane round trips).
 template <bool MIN>
@@ -505,20 +499,6 @@ __device__ __forceinline__ uint32_t wave_all_u32(uint32_t v) {
   v = pick(a[0], a[1]);
   const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
   return pick(b[0], b[1]);
-}
-__device__ __forceinline__ uint64_t wave_all_min_u64(uint64_t v) {
-  v = umin64(v, dpp64<kDppQuadXor1>(v));
-  v = umin64(v, dpp64<kDppQuadXor2>(v));
-  v = umin64(v, dpp64<kDppRowHalfMirror>(v));
-  v = umin64(v, dpp64<kDppRowMirror>(v));
-  const uint32_t lo = uint32_t(v), hi = uint32_t(v >> 32);
-  const auto a0 = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-  const auto a1 = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-  v = umin64((uint64_t(a1[0]) << 32) | a0[0], (uint64_t(a1[1]) << 32) | a0[1]);
-  const uint32_t lo2 = uint32_t(v), hi2 = uint32_t(v >> 32);
-  const auto b0 = __builtin_amdgcn_permlane16_swap(lo2, lo2, false, false);
-  const auto b1 = __builtin_amdgcn_permlane16_swap(hi2, hi2, false, false);
-  return umin64((uint64_t(b1[0]) << 32) | b0[0], (uint64_t(b1[1]) << 32) | b0[1]);
 }
 // Inclusive prefix sum over the wave: DPP shifts inside rows, then the GFX9 row broadcasts of
 // lanes 15 and 31 to the rows above them.
@@ -1087,13 +1067,13 @@ __global__ void __launch_bounds__(NT) index_score_kernel(IndexArgs a) {
 // ---- kernel 1s: streaming scores of quantised keys, one query per workgroup ------------------
 // One 512-thread workgroup per CU owns a contiguous segment of one query's keys (up to 4,096
 // entries) and streams it through a ring of three 32 KB LDS chunks filled by direct-to-LDS
-// buffer loads (range-checked: rows past the cache read as zeros), so the HBM stream does not wait
-// for the query: the first two chunks and the query itself are requested at once, and every chunk
-// scored frees its slot for the chunk two ahead.  The loads are laid out so that lane (r, g) of a
-// scoring wave reads its MFMA key operand (entry r of a 16-entry group, K-chunk g) as one linear
-// 16-byte LDS read.  Scores (same MFMA operands and epilogue order as the tile kernel's, hence the
-// same bits) stay in LDS; the segment then keeps its best keys like a tile, and the query's last
-// segment workgroup to finish merges (FUSE).
+// buffer loads (range-checked: rows past the cache read as zeros): the query and the first chunk
+// are requested at once, the next two chunks once the query is in, and every chunk scored frees
+// its slot for the chunk two ahead.  The loads are laid out so that lane (r, g) of a scoring wave
+// reads its MFMA key operand (entry r of a 16-entry group, K-chunk g) as one linear 16-byte LDS
+// read.  Scores (the same MFMA operands and epilogue order as the shared-tile kernel and the
+// merge's exact re-scoring, hence the same bits) stay in LDS; the segment then keeps its best
+// keys like a tile, and the query's last segment workgroup to finish merges (FUSE).
 //
 // The LDS loads are issued from inline assembly with their LDS address in m0: the compiler then
 // knows of no vector-memory load in flight and adds no waits of its own, and every wait is an
@@ -1319,8 +1299,9 @@ __global__ void __launch_bounds__(kStreamThreads, 1) index_stream_kernel(IndexAr
 // tile's quantised keys are loaded into LDS once and every wave scores them against its own query
 // (encoded once per call by index_query_prep_kernel; each wave copies the image into its LDS slot
 // before the tile arrives and reads its MFMA operands from there), then selects its candidates
-// with a wave-local radix select -- no workgroup barrier after the tile is loaded.  Scores are bit-identical to
-// index_score_kernel's (the same MFMA operands and epilogue order), so the selection is too.
+// with a wave-local radix select -- no workgroup barrier after the tile is loaded.  Scores are
+// bit-identical to the streaming kernel's (the same MFMA operands and epilogue order), so the
+// selection is too.
 constexpr int kMultiQ = 8;              // queries per workgroup, one per wave
 constexpr int kMultiTile = 512;         // entries per tile
 
