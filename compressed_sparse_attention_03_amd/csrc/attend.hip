@@ -438,10 +438,19 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
     const v4f sp[2] = {spp[par][0], spp[par][1]};
     const uint64_t vm0 = vmp[par][0], vm1 = vmp[par][1];
     float sv[8], cmax = -INFINITY;
+    if ((vm0 & vm1) == ~uint64_t(0)) {            // every row of the pair present (wave-uniform)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      sv[v] = ((vm0 >> (4 * g + v)) & 1) ? sp[0][v] : -INFINITY;
-      sv[4 + v] = ((vm1 >> (4 * g + v)) & 1) ? sp[1][v] : -INFINITY;
+      for (int v = 0; v < 4; ++v) {
+        sv[v] = sp[0][v];
+        sv[4 + v] = sp[1][v];
+      }
+    } else {                                      // rows 4g .. 4g+3 of each chunk: this lane's bits
+      const uint32_t bits = (uint32_t(vm0 >> (4 * g)) & 0xfu) | ((uint32_t(vm1 >> (4 * g)) & 0xfu) << 4);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        sv[v] = (bits & (1u << v)) ? sp[0][v] : -INFINITY;
+        sv[4 + v] = (bits & (16u << v)) ? sp[1][v] : -INFINITY;
+      }
     }
 #pragma unroll
     for (int v = 0; v < 8; ++v) cmax = fmaxf(cmax, sv[v]);
