@@ -20,6 +20,8 @@
 //                                                   transposing LDS read of the staged rows
 // Each wave writes its channels of the slice's normalised partial (O / l rounded to bf16); wave 0
 // writes the slice's log2-sum-exp, and a combine kernel merges the slices in a fixed order.
+// Long row lists at D = 512 take a head-shared kernel instead (attend_rows_kernel below: one
+// workgroup of 64 heads per slice, rows streamed once through LDS), which gives the same bits.
 #include <mutex>
 
 #include "common.h"
@@ -58,6 +60,7 @@ __device__ __forceinline__ float elem8(const uint4 &w, int e) {
 }
 
 constexpr int kMaxRowsPerSplit = 2048;
+constexpr int kLongList = 2048;     // row lists longer than this are sliced finer (see plan_attend)
 
 // Row code of slot `ri` of the query's row list: an entry index (< N_cap), N_cap + window row, or
 // -1 when the slot is empty.  Slots below n_sel: selected entry e (SEL; e read from topk_idx) or
@@ -147,6 +150,126 @@ __device__ __forceinline__ float group4_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// One pair's online-softmax step for head r, shared by every attention kernel so that all give
+// the same bits.  Lane (r, g) holds the pair's logits of rows 4g .. 4g+3 of each chunk (exp2
+// domain); vm0 / vm1 are the chunks' row-validity ballots (bit i: row i mod 16 present).  The
+// reference maximum of a head moves only when a logit exceeds it by more than 2^kLazy (or on its
+// first valid row): weights stay below 2^kLazy (no overflow, and bf16 keeps its relative
+// precision), and the running output needs rescaling only on such a move -- rarely after the first
+// rows -- so the caller skips the multiply when no lane of the wave moved.  O / l and m + log2 l
+// are unchanged by the choice of reference.
+constexpr float kLazy = 8.f;
+struct PairSoftmax {
+  float alpha;      // factor of the running output and sum (1 when the maximum stayed)
+  bool rescale;     // some lane of the wave has alpha != 1
+};
+__device__ __forceinline__ PairSoftmax pair_softmax(const v4f &s0, const v4f &s1, uint64_t vm0, uint64_t vm1, int g,
+                                                    float &m_run, float &l_run, Frag8 &pf) {
+  float sv[8], cmax = -INFINITY;
+  if ((vm0 & vm1) == ~uint64_t(0)) {              // every row of the pair present (wave-uniform)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      sv[v] = s0[v];
+      sv[4 + v] = s1[v];
+    }
+  } else {                                        // rows 4g .. 4g+3 of each chunk: this lane's bits
+    const uint32_t bits = (uint32_t(vm0 >> (4 * g)) & 0xfu) | ((uint32_t(vm1 >> (4 * g)) & 0xfu) << 4);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      sv[v] = (bits & (1u << v)) ? s0[v] : -INFINITY;
+      sv[4 + v] = (bits & (16u << v)) ? s1[v] : -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 8; ++v) cmax = fmaxf(cmax, sv[v]);
+  cmax = group4_max(cmax);
+  // (m_run = -inf: any valid row moves it; cmax = -inf: no valid row, nothing moves)
+  const bool move = cmax > m_run + kLazy;
+  const float m_new = move ? cmax : m_run;
+  PairSoftmax r;
+  r.alpha = !move ? 1.f : (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new));
+  r.rescale = __ballot(move) != 0;
+  // v_exp_f32 directly: every argument is <= kLazy, tiny results may flush to zero (below 2^-126
+  // of the reference), and exp2(-inf) = 0 masks the empty rows
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;   // no valid row yet: every sv is -inf
+  float p[8], psum = 0.f;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    p[v] = __builtin_amdgcn_exp2f(sv[v] - m_use);
+    psum += p[v];
+  }
+  l_run = __fmaf_rn(l_run, r.alpha, group4_sum(psum));
+  m_run = m_new;
+  pf.h[0] = pack4(p[0], p[1], p[2], p[3]);
+  pf.h[1] = pack4(p[4], p[5], p[6], p[7]);
+  return r;
+}
+
+// The query operands of S^T = K Q^T: q^ = RoPE(RMSNorm(q)) * softmax scale * log2(e).  Every
+// kernel forms them with the same arithmetic, so all give the same bits, whichever lanes hold
+// which channels: a head's D channels are 32-channel groups k (k = 0 .. D/32 - 1) of four 8-channel
+// runs j (channels 32k + 8j .. +7); the sum of squares is, per run j, a sequential sum over its 8
+// channels within each group k, then a butterfly over k (k ^ 1, k ^ 2, the mirror within eight, the
+// mirror within sixteen -- the lane-row DPP exchanges, for QCH = D / 32 groups), then over the runs
+// as (U0 + U1) + (U2 + U3).  The channel-split kernel's prologue has a thread per (head, group k)
+// and does the butterfly across lanes; the head-shared kernel's lane (head, run j) holds run j of
+// every group and does it in registers.
+__device__ __forceinline__ float run_sumsq(const uint4 &x) {     // sequential over the 8 channels
+  float p = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float v = elem8(x, e);
+    p = __fmaf_rn(v, v, p);
+  }
+  return p;
+}
+// The butterfly over 16 groups held in one lane (P[k] of run j; every P[k] ends with the same total).
+__device__ __forceinline__ float groups16_sum(float (&P)[16]) {
+  float t[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) t[k] = P[k] + P[k ^ 1];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) P[k] = t[k] + t[k ^ 2];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) t[k] = P[k] + P[(k & 8) | (7 - (k & 7))];
+  return t[0] + t[15];
+}
+// (U0 + U1) + (U2 + U3) over the lanes (head, run j) = l, l ^ 16, l ^ 32, l ^ 48, in every lane.
+__device__ __forceinline__ float runs4_sum(float u) {
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(u), false, false);
+  const float y = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+__device__ __forceinline__ float q_inv(const AttendArgs &a, float ss, int D, int head) {
+  return head < a.H ? rsqrtf(ss / float(D) + a.eps) * a.scale_log2 : 0.f;
+}
+// Operand of the channels ch0 .. ch0 + 7 (ch0 = 32k + 8g): x = q's channels, w = the norm weight's
+// (unused without one); the last rope_dim channels (from rope0) are rotated by pairs with the cos /
+// sin table.  rot (wave-uniform): some lane's channels of this k reach rope0.
+__device__ __forceinline__ Frag8 q_frag(const uint4 &x, const uint4 &w, bool has_w, int ch0, bool rot, float inv,
+                                        int rope0, const float *s_cs, const float *s_sn) {
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = __fmul_rn(__fmul_rn(elem8(x, e), inv), has_w ? elem8(w, e) : 1.0f);
+  if (rot) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int ch = ch0 + e;
+      const int u = max(ch - rope0, 0) >> 1;        // rope0 is even: exact; below rope0 unused
+      const float cs = s_cs[u], sn = s_sn[u], x0 = v[e], x1 = v[e + 1];
+      const float y0 = __fmaf_rn(x0, cs, -__fmul_rn(x1, sn));
+      const float y1 = __fmaf_rn(x0, sn, __fmul_rn(x1, cs));
+      v[e] = ch >= rope0 ? y0 : x0;
+      v[e + 1] = ch >= rope0 ? y1 : x1;
+    }
+  }
+  Frag8 f;
+  f.h[0] = pack4(v[0], v[1], v[2], v[3]);
+  f.h[1] = pack4(v[4], v[5], v[6], v[7]);
+  return f;
+}
+
 // Channel split: a workgroup has NW = D / C waves and wave w owns the channels [C w, C w + C) of
 // q, of every row and of O.  All waves take every chunk of the workgroup's slice together.
 template <int D>
@@ -177,8 +300,8 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
   static_assert(QCH >= 2 && QCH <= 16, "a head's prologue threads share one row of 16 lanes");
   static_assert(D / 2 <= NT, "one rotary pair per thread");
   // LDS: q^ during the prologue, then (same bytes) every wave's staging of its current pair of
-  // chunks (their row slices) for the transposing V reads; the waves' S partials (two pairs of chunks, double-buffered); row
-  // codes; rotary angles.
+  // chunks (their row slices) for the transposing V reads; the waves' S partials (three pairs in
+  // rotation); row codes; rotary angles.
   __shared__ __align__(16) unsigned char s_buf[BUF];
   __shared__ __align__(16) float4 s_part[3][2][NW][64];
   __shared__ int s_row[kMaxRowsPerSplit];
@@ -216,6 +339,7 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
 #pragma unroll
     for (int k = 0; k < KP; ++k) pre_e[k] = sel[min(r0_first + min(tid + k * NT, nr_first - 1), last)];
   }
+  // prologue thread (head qh, group qc): q's channels 32 qc .. +31 and the norm weight's
   const bool qthread = tid < 16 * QCH;
   const int qh = tid / QCH, qc = tid % QCH;
   const int qhead = hb * 16 + qh;
@@ -288,64 +412,27 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
   };
   begin_segment(0);                              // its loads go out before q^ is built
 
-  // q^ = RoPE(RMSNorm(q)) * scale * log2(e) for the 16 heads, into LDS, 8 channels at a time
-  // (few registers: the row loads above are in flight meanwhile)
+  // q^ of the 16 heads into LDS (the rotary table is published by the row-code barrier above): run
+  // sums, the butterfly over the head's QCH threads (one lane row), then over the runs
   if (qthread) {
-    float ss = 0.f;
+    float P[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int j = 0; j < 4; ++j) P[j] = run_sumsq(qraw[j]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = elem8(qraw[k], e);
-        ss += x * x;
-      }
+    for (int j = 0; j < 4; ++j) {
+      P[j] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(P[j]), 0xb1, 0xf, 0xf, false));
+      if constexpr (QCH >= 4) P[j] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(P[j]), 0x4e, 0xf, 0xf, false));
+      if constexpr (QCH >= 8) P[j] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(P[j]), 0x141, 0xf, 0xf, false));
+      if constexpr (QCH >= 16) P[j] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(P[j]), 0x140, 0xf, 0xf, false));
     }
-    // over the head's QCH (2 to 16) consecutive threads, inside one row of 16 lanes: DPP
-    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0xb1, 0xf, 0xf, false));
-    if constexpr (QCH >= 4) ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x4e, 0xf, 0xf, false));
-    if constexpr (QCH >= 8) ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x141, 0xf, 0xf, false));
-    if constexpr (QCH >= 16) ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x140, 0xf, 0xf, false));
-    const float inv = qhead < a.H ? rsqrtf(ss / float(D) + a.eps) * a.scale_log2 : 0.f;
+    const float inv = q_inv(a, (P[0] + P[1]) + (P[2] + P[3]), D, qhead);
     const bool has_w = a.q_norm_w != nullptr;
     const int rope0 = D - a.rope_dim;
-    // the rotary pairs of this thread's 32 channels (pair u = (ch - rope0) / 2 = u0 + p), read from
-    // LDS together so that one wait covers them all; reads below the rotated part are clamped
-    // to pair 0 and not used
-    float rcs[16], rsn[16];
-    {
-      const int u0 = (32 * qc - rope0) >> 1;       // rope0 is even: exact
-#pragma unroll
-      for (int p = 0; p < 16; ++p) {
-        const int u = max(u0 + p, 0);
-        rcs[p] = s_cs[u];
-        rsn[p] = s_sn[u];
-      }
-    }
     uint4 *dst = reinterpret_cast<uint4 *>(s_q + qh * QS + 32 * qc);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = elem8(qraw[k], e) * inv * (has_w ? elem8(wraw[k], e) : 1.0f);
       const int ch0 = 32 * qc + 8 * k;
-      if (ch0 + 8 > rope0) {
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const int ch = ch0 + e;
-          if (ch >= rope0) {
-            const float cs = rcs[(8 * k + e) >> 1], sn = rsn[(8 * k + e) >> 1], x0 = v[e], x1 = v[e + 1];
-            v[e] = x0 * cs - x1 * sn;
-            v[e + 1] = x0 * sn + x1 * cs;
-          }
-        }
-      }
-      Pack4 lo, hi;
-      lo.s = pack4(v[0], v[1], v[2], v[3]);
-      hi.s = pack4(v[4], v[5], v[6], v[7]);
-      dst[k] = make_uint4(uint32_t(uint16_t(lo.s[0])) | (uint32_t(uint16_t(lo.s[1])) << 16),
-                          uint32_t(uint16_t(lo.s[2])) | (uint32_t(uint16_t(lo.s[3])) << 16),
-                          uint32_t(uint16_t(hi.s[0])) | (uint32_t(uint16_t(hi.s[1])) << 16),
-                          uint32_t(uint16_t(hi.s[2])) | (uint32_t(uint16_t(hi.s[3])) << 16));
+      dst[k] = q_frag(qraw[k], wraw[k], has_w, ch0, ch0 + 8 > rope0, inv, rope0, s_cs, s_sn).u;
     }
   }
   lds_barrier();
@@ -435,47 +522,15 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
   };
   // then the softmax and O^T += V^T P^T
   auto pair_b = [&](int par) __attribute__((always_inline)) {
-    const v4f sp[2] = {spp[par][0], spp[par][1]};
-    const uint64_t vm0 = vmp[par][0], vm1 = vmp[par][1];
-    float sv[8], cmax = -INFINITY;
-    if ((vm0 & vm1) == ~uint64_t(0)) {            // every row of the pair present (wave-uniform)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        sv[v] = sp[0][v];
-        sv[4 + v] = sp[1][v];
-      }
-    } else {                                      // rows 4g .. 4g+3 of each chunk: this lane's bits
-      const uint32_t bits = (uint32_t(vm0 >> (4 * g)) & 0xfu) | ((uint32_t(vm1 >> (4 * g)) & 0xfu) << 4);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        sv[v] = (bits & (1u << v)) ? sp[0][v] : -INFINITY;
-        sv[4 + v] = (bits & (16u << v)) ? sp[1][v] : -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < 8; ++v) cmax = fmaxf(cmax, sv[v]);
-    cmax = group4_max(cmax);
-    // v_exp_f32 directly: every argument is <= 0, tiny results may flush to zero (they are below
-    // 2^-126 of the head's largest weight), and exp2(-inf) = 0 masks the empty rows
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;      // no valid row yet: every sv is -inf
-    float p[8], psum = 0.f;
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      p[v] = __builtin_amdgcn_exp2f(sv[v] - m_use);
-      psum += p[v];
-    }
-    l_run = l_run * alpha + group4_sum(psum);
-    m_run = m_new;
-#pragma unroll
-    for (int k = 0; k < NB; ++k) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) o[k][v] *= alpha;
-    }
     Frag8 pf;
-    pf.h[0] = pack4(p[0], p[1], p[2], p[3]);
-    pf.h[1] = pack4(p[4], p[5], p[6], p[7]);
+    const PairSoftmax sm = pair_softmax(spp[par][0], spp[par][1], vmp[par][0], vmp[par][1], g, m_run, l_run, pf);
+    if (sm.rescale) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[k][v] *= sm.alpha;
+      }
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vtp[par][nb].b, pf.b, o[nb], 0, 0, 0);
   };
@@ -580,6 +635,288 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
   }
 }
 
+// ---- head-shared decode attention (D = 512) ------------------------------------------------------
+// One workgroup per (query, slice of the row list, group of 64 heads): wave w owns head block w of
+// the group (16 heads) over all 512 channels, so no S partial crosses waves and every row is read
+// from memory once for the 64 heads.  A slice's rows stream through a ring of three 32-row LDS
+// buffers filled by direct-to-LDS buffer loads (one 1 KiB row per wave instruction); every wave
+// reads its MFMA operands from the shared buffers:
+//   S^T [16 rows x 16 heads] per 128-channel quarter = K_q Q_q^T   (16-byte LDS reads, A operand)
+//   S^T = ((S_0 + S_1) + S_2) + S_3                                  in fp32, in quarter order
+//   online softmax in the exp2 domain (pair_softmax), per 32 rows
+//   O^T [512 ch x 16 heads] += V^T P^T                               (transposing LDS reads)
+// It takes the split-K path of long row lists (HCA's every entry), where one read of each row for
+// all 64 heads and a whole CU per workgroup beat four head-block workgroups re-reading it.
+// These are the channel-split kernel's operations on the same operands in the same order (its
+// waves' S partials summed in wave order are the quarters' sums here), so both kernels -- and the
+// fused path, which runs the channel-split kernel -- give the same bits.
+//
+// Rows sit kRowsStride bytes apart (1 KiB + 32: rows 8 apart fall on the same banks) and a row's
+// 16-byte column c is stored at slot c ^ row_swz(row) (row_swz = bit 3 of the row): the 16 rows of
+// one operand read (16 lanes x 16 bytes) cover every bank once, and so do the 32 lanes of a
+// transposing read (8 rows x 32 bytes).
+constexpr int kRowsBytes = 1024;                  // one 512-channel bf16 row
+constexpr int kRowsStride = 1056;                 // its LDS footprint
+constexpr int kRowsPair = 32 * kRowsStride;       // one ring buffer: 32 rows
+constexpr int kRowsRing = 3;
+
+__device__ __forceinline__ int row_swz(int row) { return (row >> 3) & 1; }
+
+__device__ __forceinline__ uint32_t rows_lds_address(const void *p) {      // p points into LDS
+  const __attribute__((address_space(3))) void *l = (const __attribute__((address_space(3))) void *)(p);
+  return __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(l)));
+}
+// Lane l's 16 bytes at byte offset voff of the buffer go to LDS address m0 + 16 l.  The compiler
+// knows of no load in flight; every wait for these is an explicit vmcnt count.
+__device__ __forceinline__ void rows_load16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rs), "{m0}"(lds) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void rows_wait() {                 // at most N vector loads in flight
+  static_assert(N >= 0 && N < 16, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+template <bool SEL>
+__global__ void __launch_bounds__(256, 1) attend_rows_kernel(AttendArgs a, int64_t n_queries) {
+  constexpr int D = 512, NT = 256;
+  __shared__ __align__(16) unsigned char s_rows[kRowsRing][kRowsPair];
+  __shared__ int s_row[kMaxRowsPerSplit];
+  __shared__ float s_cs[256], s_sn[256];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r = lane & 15;
+  const int ns = a.plan.n_splits;
+  const int n_hg = (a.plan.n_hb + 3) >> 2;
+  const uint32_t L = blockIdx.x;
+  const int hg = int(L % uint32_t(n_hg));
+  const uint32_t rest = L / uint32_t(n_hg);
+  const int64_t qi = int64_t(rest / uint32_t(ns));
+  const int split = int(rest % uint32_t(ns));
+  if (qi >= n_queries) return;
+  const int hb = hg * 4 + wave;                   // this wave's head block
+  const int b = int(uint32_t(qi) / uint32_t(a.Sq)), s_idx = int(qi) - b * a.Sq;   // B * Sq < 2^16
+  const int64_t r0 = int64_t(split) * a.plan.rows_per_split;
+  const int nr = int(min(int64_t(a.plan.n_rows), r0 + a.plan.rows_per_split) - r0);
+  const int n_chunks = (nr + 15) >> 4;
+  const int np = (n_chunks + 1) >> 1;             // 32-row pairs
+
+  // ---- prologue: every global load of the workgroup except the rows, in one round trip --------
+  constexpr int KP = 4;
+  int pre_e[KP];
+  if constexpr (SEL) {
+    const int32_t *sel = a.topk_idx + qi * a.n_sel;
+    const int64_t last = a.n_sel - 1;
+#pragma unroll
+    for (int k = 0; k < KP; ++k) pre_e[k] = sel[min(r0 + min(tid + k * NT, nr - 1), last)];
+  }
+  // head r's channels 32k + 8g .. +7 of q and of the norm weight, k = 0 .. 15
+  const int qhead = hb * 16 + r;
+  uint4 qraw[16], wraw[16];
+  {
+    const uint16_t *src = a.q + (qi * a.H + (qhead < a.H ? qhead : 0)) * D + 8 * g;
+    const uint16_t *wsrc = (a.q_norm_w ? a.q_norm_w : a.q) + 8 * g;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) qraw[k] = *reinterpret_cast<const uint4 *>(src + 32 * k);
+    if (a.q_norm_w) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) wraw[k] = *reinterpret_cast<const uint4 *>(wsrc + 32 * k);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) wraw[k] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int npairs = a.rope_dim / 2;
+  const double rf = tid < npairs ? rope_turns_per_pos(tid, rope_rate(a.rope_dim, a.log2_base)) : 0.0;
+  const int64_t t = a.q_pos0[b] + s_idx;
+  const int64_t wp0 = a.win_pos0 ? a.win_pos0[b] : 0;
+  const int64_t n_vis = SEL ? 0 : min(a.n_entries[b], div_count(t + 1, a.m));
+  if (tid < npairs) rope_cos_sin_f(t, rf, &s_cs[tid], &s_sn[tid]);
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    const int i = tid + k * NT;
+    if (i < nr) {
+      const int64_t ri = r0 + i;
+      s_row[i] = (SEL && ri < a.n_sel) ? selected_code(a, pre_e[k]) : row_code<SEL>(a, qi, wp0, t, n_vis, ri);
+    }
+  }
+  for (int i = tid + KP * NT; i < nr; i += NT) s_row[i] = row_code<SEL>(a, qi, wp0, t, n_vis, r0 + i);
+  for (int i = nr + tid; i < 32 * np; i += NT) s_row[i] = -1;     // the last pair's missing rows
+  // every load the compiler issued is complete from here on (it counts none of the row loads)
+  __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
+  lds_barrier();
+
+  // rows of pair P (this wave: rows 8w .. 8w+7 of the pair), one wave instruction per row; an
+  // empty row reads entry row 0 (finite, weight exactly 0)
+  const __amdgpu_buffer_rsrc_t ent_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(a.entries + int64_t(b) * a.N_cap * D), short(0), int(uint32_t(a.N_cap) * kRowsBytes),
+      kRawBufferDesc3);
+  const __amdgpu_buffer_rsrc_t win_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(a.win_rows + int64_t(b) * a.W_cap * D), short(0), int(uint32_t(a.W_cap) * kRowsBytes),
+      kRawBufferDesc3);
+  const int n_cap = int(a.N_cap);
+  auto issue_pair = [&](int P) __attribute__((always_inline)) {
+    unsigned char *buf = s_rows[P % kRowsRing];
+    const int4 ca = *reinterpret_cast<const int4 *>(s_row + P * 32 + wave * 8);
+    const int4 cb = *reinterpret_cast<const int4 *>(s_row + P * 32 + wave * 8 + 4);
+    const int cs[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = wave * 8 + j;
+      const int code = __builtin_amdgcn_readfirstlane(cs[j]);
+      const bool win = code >= n_cap;
+      const uint32_t roff = code < 0 ? 0u : uint32_t(win ? code - n_cap : code) * uint32_t(kRowsBytes);
+      const uint32_t voff = roff + 16u * uint32_t(lane ^ row_swz(row));
+      rows_load16(win ? win_rs : ent_rs, voff, rows_lds_address(buf + row * kRowsStride));
+    }
+  };
+  if (np > 0) issue_pair(0);
+  if (np > 1) issue_pair(1);
+
+  // ---- q^ as this wave's B operands (the rotary table is published by the barrier above) ---------
+  Frag8 qf[16];                                   // [quarter q * 4 + step s]: head r, channels 128q + 32s + 8g
+  {
+    float P[16];                                  // run g of every group k
+#pragma unroll
+    for (int k = 0; k < 16; ++k) P[k] = run_sumsq(qraw[k]);
+    const float inv = q_inv(a, runs4_sum(groups16_sum(P)), D, qhead);
+    const bool has_w = a.q_norm_w != nullptr;
+    const int rope0 = D - a.rope_dim;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      qf[k] = q_frag(qraw[k], wraw[k], has_w, 32 * k + 8 * g, 32 * k + 32 > rope0, inv, rope0, s_cs, s_sn);
+  }
+
+  // ---- the slice's pairs ------------------------------------------------------------------------
+  v4f o[32];                                      // [q * 8 + nb]: head r, channels 128q + 16nb + 4g + v
+#pragma unroll
+  for (int k = 0; k < 32; ++k) o[k] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;           // of head r
+  const int kx = row_swz(r);                      // operand rows r and 16 + r
+  const int vrow = 4 * g + (r >> 2), vx = row_swz(vrow), vcol = (r & 3) >> 1, vhalf = 8 * (r & 1);
+  // O^T += V^T P^T over the pair in `buf`, software-pipelined one channel quarter apart: quarter
+  // q + 1's transposing reads are issued before quarter q's products (scheduling fences keep them
+  // there)
+  auto pv = [&](const unsigned char *buf, const Frag8 &pf) __attribute__((always_inline)) {
+    const unsigned char *v0 = buf + vrow * kRowsStride + vhalf;
+    Frag8 vt[2][8];
+    auto read_v = [&](int q, Frag8 (&dst)[8]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const int off = 16 * (16 * q + ((2 * nb + vcol) ^ vx));
+        dst[nb].h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(v0 + off));
+        dst[nb].h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(v0 + 16 * kRowsStride + off));
+      }
+    };
+    read_v(0, vt[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q < 3) read_v(q + 1, vt[(q + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+        o[8 * q + nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[q & 1][nb].b, pf.b, o[8 * q + nb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // The pairs.  A pair whose softmax moves some head's reference maximum leaves the inner loop, and
+  // the outer one rescales the running output before its products: the running output then stays
+  // in the accumulation registers through the inner loop (no copies for the rare multiply).
+  int p = 0;
+  const unsigned char *buf = s_rows[0];
+  Frag8 pf;
+  float alpha = 1.f;
+  for (;;) {
+    bool moved = false;
+    for (; p < np; ++p) {
+      if (p + 1 < np) rows_wait<8>(); else rows_wait<0>();   // this wave's rows of pair p are in LDS
+      lds_sync();                                 // ... every wave's; and pair p - 1's buffer is free
+      if (p + 2 < np) issue_pair(p + 2);
+      buf = s_rows[p % kRowsRing];
+      // validity of rows r and 16 + r (row order as in the channel-split kernel's masks)
+      const uint64_t vm0 = __ballot(s_row[32 * p + r] >= 0);
+      const uint64_t vm1 = __ballot(s_row[32 * p + 16 + r] >= 0);
+      // S^T of both chunks, quarter by quarter, software-pipelined like the products above: quarter
+      // q + 1's eight operand reads go out before quarter q's eight products; then the running
+      // sum ((S_0 + S_1) + S_2) + S_3
+      v4f sp[2];
+      {
+        Frag8 kf[2][2][4];
+        auto read_k = [&](int q, Frag8 (&dst)[2][4]) __attribute__((always_inline)) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              dst[c][s].u = *reinterpret_cast<const uint4 *>(buf + (16 * c + r) * kRowsStride +
+                                                             16 * (16 * q + ((4 * s + g) ^ kx)));
+        };
+        read_k(0, kf[0]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (q < 3) read_k(q + 1, kf[(q + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          v4f part[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+              part[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[q & 1][c][s].b, qf[4 * q + s].b, part[c], 0, 0, 0);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            if (q == 0) {
+              sp[c] = part[c];
+            } else {
+              sp[c][0] += part[c][0]; sp[c][1] += part[c][1]; sp[c][2] += part[c][2]; sp[c][3] += part[c][3];
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      const PairSoftmax sm = pair_softmax(sp[0], sp[1], vm0, vm1, g, m_run, l_run, pf);
+      if (sm.rescale) {
+        alpha = sm.alpha;
+        moved = true;
+        break;
+      }
+      pv(buf, pf);
+    }
+    if (!moved) break;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[k][v] *= alpha;
+    }
+    pv(buf, pf);
+    ++p;
+  }
+  rows_wait<0>();
+
+  // ---- this wave's heads of the slice: O / l (bf16) and the log2-sum-exp -----------------------
+  const int gh = hb * 16 + r;
+  if (gh < a.H) {
+    const float inv = slice_scale(l_run);
+    const float ls = slice_lse2(m_run, l_run);
+    uint16_t *dst;
+    if (ns == 1) {
+      dst = a.out + (qi * a.H + gh) * D + 4 * g;
+      if (a.lse && g == 0) a.lse[qi * a.H + gh] = ls * 0.6931471805599453f;
+    } else {
+      uint16_t *po = static_cast<uint16_t *>(a.workspace);
+      float *plse = reinterpret_cast<float *>(po + n_queries * a.H * ns * D);
+      dst = po + ((qi * a.H + gh) * ns + split) * int64_t(D) + 4 * g;
+      if (g == 0) plse[(qi * a.H + gh) * ns + split] = ls;
+    }
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      *reinterpret_cast<v4s *>(dst + 128 * (k >> 3) + 16 * (k & 7)) =
+          pack4(slice_value(o[k][0], inv), slice_value(o[k][1], inv), slice_value(o[k][2], inv),
+                slice_value(o[k][3], inv));
+  }
+}
+
 // One workgroup per (query, head): merge the slices in order.
 template <int D>
 __global__ void __launch_bounds__(D / 4) attend_combine_kernel(AttendArgs a, int64_t n_queries) {
@@ -626,11 +963,15 @@ AttendPlan plan_attend(int64_t n_queries, int H, int64_t n_sel, int window, int 
   p.n_hb = (H + 15) / 16;
   p.n_rows = int(n_sel + window);
   // The slices depend on the row count alone -- never on how many queries share the call -- so a
-  // query's output has the same bits in any batch (batch invariance): up to 16 slices of about 144
-  // rows or more, each a multiple of 32 rows (a pair of 16-row chunks).  (k + W = 1,152 rows give 8
-  // slices: 512 workgroups, one round, for 16 queries of 64 heads.)
-  int64_t splits = (p.n_rows + 143) / 144;
-  if (splits > 16) splits = 16;
+  // query's output has the same bits in any batch (batch invariance), each a multiple of 32 rows (a
+  // pair of 16-row chunks).  Lists of up to kLongList rows (CSA selections: k + W = 1,152 rows give
+  // 8 slices, 512 channel-split workgroups in one round for 16 queries of 64 heads): up to 16 slices
+  // of 144 rows or more.  Longer lists (HCA's every entry; at D = 512 taken by the head-shared
+  // kernel, one workgroup of 64 heads per CU): up to 32 slices of 96 rows or more (8,320 rows give
+  // 29 slices of 288: 232 workgroups for 8 queries).
+  const bool long_list = p.n_rows > kLongList;
+  int64_t splits = long_list ? (p.n_rows + 95) / 96 : (p.n_rows + 143) / 144;
+  if (splits > (long_list ? 32 : 16)) splits = long_list ? 32 : 16;
   if (splits < 1) splits = 1;
   int64_t rps = (p.n_rows + splits - 1) / splits;
   rps = (rps + 31) / 32 * 32;
@@ -638,10 +979,12 @@ AttendPlan plan_attend(int64_t n_queries, int H, int64_t n_sel, int window, int 
   p.rows_per_split = int(rps);
   p.n_splits = int((p.n_rows + rps - 1) / rps);
   // Split-K (a workgroup per slice, partials merged by the combine kernel) while the grid stays
-  // within a few rounds of resident workgroups (two per CU); beyond that one workgroup per
-  // (query, head block) takes the slices in order and merges them itself, with no workspace.
-  p.fused = (p.n_splits > 1 && n_queries * p.n_hb * p.n_splits > 4 * 512) ? 1 : 0;
-  (void)D;
+  // within a few rounds of resident workgroups (at D = 512 one head-shared workgroup of 64 heads
+  // per CU, else two of 16 heads); beyond that one workgroup per (query, head block) takes the
+  // slices in order and merges them itself, with no workspace.
+  const bool rows = D == 512 && long_list;
+  const int64_t wgs = rows ? n_queries * ((p.n_hb + 3) / 4) * p.n_splits : n_queries * p.n_hb * p.n_splits;
+  p.fused = (p.n_splits > 1 && wgs > (rows ? 4 * 256 : 4 * 512)) ? 1 : 0;
   return p;
 }
 
@@ -684,6 +1027,14 @@ hipError_t attend_scratch(void **ptr) {
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream) {
   hipError_t e = hipSuccess;
   const int64_t nq = int64_t(a.B) * a.Sq;
+  // split-K over a long row list at D = 512 (row offsets within 32 bits): the head-shared kernel,
+  // which gives the same bits as the channel-split one
+  if (a.D == 512 && !a.plan.fused && a.plan.n_rows > kLongList && a.N_cap <= (int64_t(1) << 22) - 1 &&
+      a.W_cap <= (int64_t(1) << 22) - 1) {
+    dim3 rgrid(unsigned(nq * a.plan.n_splits * ((a.plan.n_hb + 3) / 4)));
+    return a.topk_idx ? launch("attend_split", attend_rows_kernel<true>, rgrid, dim3(256), stream, a, nq)
+                      : launch("attend_split", attend_rows_kernel<false>, rgrid, dim3(256), stream, a, nq);
+  }
   const int64_t pairs = nq * (a.plan.fused ? 1 : a.plan.n_splits);
   dim3 grid(unsigned(((pairs + 7) / 8) * 8 * a.plan.n_hb));
 #define CSA_ATTEND_LAUNCH(DD)                                                                          \
