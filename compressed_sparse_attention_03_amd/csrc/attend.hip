@@ -895,25 +895,37 @@ __global__ void __launch_bounds__(256, 1) attend_rows_kernel(AttendArgs a, int64
   rows_wait<0>();
 
   // ---- this wave's heads of the slice: O / l (bf16) and the log2-sum-exp -----------------------
+  // The values go through LDS (the ring is idle once every wave is past its last pair) so that each
+  // store instruction writes one head's whole 1 KiB row: every workgroup stores its 64 KiB at
+  // once at the end, and rows written in 32-byte pieces made that burst several times slower.
   const int gh = hb * 16 + r;
-  if (gh < a.H) {
-    const float inv = slice_scale(l_run);
-    const float ls = slice_lse2(m_run, l_run);
-    uint16_t *dst;
-    if (ns == 1) {
-      dst = a.out + (qi * a.H + gh) * D + 4 * g;
-      if (a.lse && g == 0) a.lse[qi * a.H + gh] = ls * 0.6931471805599453f;
-    } else {
-      uint16_t *po = static_cast<uint16_t *>(a.workspace);
-      float *plse = reinterpret_cast<float *>(po + n_queries * a.H * ns * D);
-      dst = po + ((qi * a.H + gh) * ns + split) * int64_t(D) + 4 * g;
-      if (g == 0) plse[(qi * a.H + gh) * ns + split] = ls;
-    }
+  const float inv = slice_scale(l_run);
+  const float ls = slice_lse2(m_run, l_run);
+  constexpr int kOutStride = kRowsBytes + 16;     // staging row stride: the lanes of a write differ by row
+  static_assert(4 * 16 * kOutStride <= kRowsRing * kRowsPair, "the output staging fits the ring");
+  unsigned char *stage = &s_rows[0][0] + wave * 16 * kOutStride;
+  lds_sync();                                     // every wave is done with the ring
 #pragma unroll
-    for (int k = 0; k < 32; ++k)
-      *reinterpret_cast<v4s *>(dst + 128 * (k >> 3) + 16 * (k & 7)) =
-          pack4(slice_value(o[k][0], inv), slice_value(o[k][1], inv), slice_value(o[k][2], inv),
-                slice_value(o[k][3], inv));
+  for (int k = 0; k < 32; ++k)
+    *reinterpret_cast<v4s *>(stage + r * kOutStride + 2 * (128 * (k >> 3) + 16 * (k & 7) + 4 * g)) =
+        pack4(slice_value(o[k][0], inv), slice_value(o[k][1], inv), slice_value(o[k][2], inv),
+              slice_value(o[k][3], inv));
+  wave_lds_sync();
+  uint16_t *po = static_cast<uint16_t *>(a.workspace);
+  const int64_t head0 = qi * a.H + hb * 16;       // this wave's first head (query-major)
+  if (gh < a.H && g == 0) {
+    if (ns == 1) {
+      if (a.lse) a.lse[qi * a.H + gh] = ls * 0.6931471805599453f;
+    } else {
+      reinterpret_cast<float *>(po + n_queries * a.H * ns * D)[(qi * a.H + gh) * ns + split] = ls;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    if (hb * 16 + h >= a.H) break;                // (wave-uniform)
+    const uint4 v = *reinterpret_cast<const uint4 *>(stage + h * kOutStride + 16 * lane);
+    uint16_t *dst = ns == 1 ? a.out + (head0 + h) * D : po + ((head0 + h) * ns + split) * int64_t(D);
+    *reinterpret_cast<uint4 *>(dst + 8 * lane) = v;
   }
 }
 
