@@ -548,24 +548,36 @@ __global__ void __launch_bounds__(64 * waves_of<D>(), 2) attend_split_kernel(Att
 #pragma unroll
         for (int v = 0; v < 4; ++v) facc[nb][v] = merge_value(facc[nb][v], k, slice_value(o[nb][v], inv));
     }
-  } else if (gh < a.H) {
-    if (a.plan.n_splits == 1) {
-      uint16_t *dst = a.out + (qi * a.H + gh) * D + c0;
+  } else {
+    // through the wave's staging area (only this wave reads it, and its last pair's V^T fragments
+    // are in registers): each store writes whole 2C-byte rows of four heads instead of 32-byte
+    // pieces of sixteen
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        *reinterpret_cast<v4s *>(dst + 16 * nb) = pack4(slice_value(o[nb][0], inv), slice_value(o[nb][1], inv),
-                                                       slice_value(o[nb][2], inv), slice_value(o[nb][3], inv));
-      if (a.lse && wave == 0 && g == 0) a.lse[qi * a.H + gh] = ls * 0.6931471805599453f;
-    } else {
-      // workspace: bf16 partials [query, head, slice, D], then fp32 log2-sum-exps [query, head, slice]
-      uint16_t *po = static_cast<uint16_t *>(a.workspace);
-      float *plse = reinterpret_cast<float *>(po + n_queries * a.H * a.plan.n_splits * D);
-      uint16_t *dst = po + ((qi * a.H + gh) * a.plan.n_splits + split) * int64_t(D) + c0;
+    for (int nb = 0; nb < NB; ++nb)
+      *reinterpret_cast<v4s *>(stage + r * RS + 2 * (16 * nb + 4 * g)) =
+          pack4(slice_value(o[nb][0], inv), slice_value(o[nb][1], inv), slice_value(o[nb][2], inv),
+                slice_value(o[nb][3], inv));
+    wave_lds_sync();
+    // workspace: bf16 partials [query, head, slice, D], then fp32 log2-sum-exps [query, head, slice]
+    uint16_t *po = static_cast<uint16_t *>(a.workspace);
+    const int ns = a.plan.n_splits;
+    if (gh < a.H && wave == 0 && g == 0) {
+      if (ns == 1) {
+        if (a.lse) a.lse[qi * a.H + gh] = ls * 0.6931471805599453f;
+      } else {
+        reinterpret_cast<float *>(po + n_queries * a.H * ns * D)[(qi * a.H + gh) * ns + split] = ls;
+      }
+    }
+    constexpr int LPH = C / 8;                    // lanes per head row (16 bytes each)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        *reinterpret_cast<v4s *>(dst + 16 * nb) = pack4(slice_value(o[nb][0], inv), slice_value(o[nb][1], inv),
-                                                       slice_value(o[nb][2], inv), slice_value(o[nb][3], inv));
-      if (wave == 0 && g == 0) plse[(qi * a.H + gh) * a.plan.n_splits + split] = ls;
+    for (int j = 0; j < 16 * LPH / 64; ++j) {
+      const int h = j * (64 / LPH) + lane / LPH, part = lane % LPH;
+      const int64_t head = qi * a.H + hb * 16 + h;
+      if (hb * 16 + h < a.H) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(stage + h * RS + 16 * part);
+        uint16_t *dst = ns == 1 ? a.out + head * D : po + (head * ns + split) * int64_t(D);
+        *reinterpret_cast<uint4 *>(dst + C * wave + 8 * part) = v;
+      }
     }
   }
   };
