@@ -106,11 +106,11 @@ def test_index_selection_does_not_depend_on_the_batch():
         assert np.array_equal(s1.cpu().numpy()[0], sel_all[b]), f"sequence {b}"
 
 
-@pytest.mark.parametrize("heads,norm_w", [(48, False), (80, True)])
+@pytest.mark.parametrize("heads,norm_w", [(48, False), (80, True), (128, False)])
 def test_long_list_kernel_bits_equal_the_fused_path(heads, norm_w):
     """A long row list (2,048 selected entries + a 128-row window) at D = 512 is taken by the
     head-shared split kernel for a few queries and by the channel-split fused kernel for many: the
-    outputs are bitwise equal, with head counts that leave part of a 64-head group empty, ragged
+    outputs are bitwise equal, with head counts that leave part of a 64-head group empty or fill two, ragged
     selections and a norm weight; a sample of queries also against the oracle."""
     k_long, sq = 2048, 300
     say(f"case: long-list kernel vs fused path H={heads} D={D} k={k_long} W={W} norm_w={norm_w}")
