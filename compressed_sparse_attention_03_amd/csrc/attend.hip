@@ -950,27 +950,36 @@ __global__ void __launch_bounds__(D / 4) attend_combine_kernel(AttendArgs a, int
   const uint16_t *po = static_cast<const uint16_t *>(a.workspace) + qh * ns * int64_t(D);
   const float *plse = reinterpret_cast<const float *>(static_cast<const uint16_t *>(a.workspace) +
                                                       n_queries * a.H * ns * int64_t(D)) + qh * ns;
-  const int ch = threadIdx.x * 4;
+  const int ch = threadIdx.x * 4, lane = threadIdx.x & 63;
   // every slice's log2-sum-exp and partial are loaded before any is used (one round trip per
-  // batch of slices), then merged in slice order with a running maximum
+  // batch of slices), then merged in slice order with a running maximum.  The log2-sum-exps of a
+  // window of slices come in one vector load (lane s: slice w0 + s) and are taken by readlane: as
+  // uniform scalar loads, which complete out of order, each use waited for all of them and the
+  // compiler issued them one round trip apart.
   float M = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < ns; s0 += kBatch) {
-    float ls[kBatch];
-    float4 x[kBatch];
+  constexpr int WIN = D / 4 < 64 ? D / 4 : 64;   // slices per window: one per active lane
+  static_assert(WIN % kBatch == 0, "a batch stays inside one window");
+  for (int w0 = 0; w0 < ns; w0 += WIN) {
+    const float lsv = plse[min(w0 + lane, ns - 1)];
+    const int wend = min(ns, w0 + WIN);
+    for (int s0 = w0; s0 < wend; s0 += kBatch) {
+      float ls[kBatch];
+      float4 x[kBatch];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int s = s0 + j < ns ? s0 + j : ns - 1;
-      ls[j] = plse[s];
-      const uint2 w = *reinterpret_cast<const uint2 *>(po + s * int64_t(D) + ch);
-      x[j] = make_float4(bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y));
-    }
+      for (int j = 0; j < kBatch; ++j) {
+        const int s = s0 + j < ns ? s0 + j : ns - 1;
+        ls[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsv), s - w0));
+        const uint2 w = *reinterpret_cast<const uint2 *>(po + s * int64_t(D) + ch);
+        x[j] = make_float4(bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y));
+      }
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      if (s0 + j >= ns || ls[j] == -INFINITY) continue;
-      const MergeWeights k = merge_slice(M, L, ls[j]);
-      acc.x = merge_value(acc.x, k, x[j].x); acc.y = merge_value(acc.y, k, x[j].y);
-      acc.z = merge_value(acc.z, k, x[j].z); acc.w = merge_value(acc.w, k, x[j].w);
+      for (int j = 0; j < kBatch; ++j) {
+        if (s0 + j >= ns || ls[j] == -INFINITY) continue;
+        const MergeWeights k = merge_slice(M, L, ls[j]);
+        acc.x = merge_value(acc.x, k, x[j].x); acc.y = merge_value(acc.y, k, x[j].y);
+        acc.z = merge_value(acc.z, k, x[j].z); acc.w = merge_value(acc.w, k, x[j].w);
+      }
     }
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;

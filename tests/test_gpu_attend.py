@@ -169,3 +169,24 @@ def test_deterministic_repeat():
     a, la = ops.csa_attend(*args, rope_dim=64, window=128, lse=True)
     b, lb = ops.csa_attend(*args, rope_dim=64, window=128, lse=True)
     assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_hca_long_list_many_slices(D):
+    """A list of 70,032 rows is cut into 35 slices of 2,048: more than one window of slice
+    log2-sum-exps in the combine (16 at D = 64, 32 at D = 128); against the oracle."""
+    B, Sq, H, N, W, m = 1, 1, 8, 70000, 32, 4
+    cfg = 76
+    q = gen.normal_bf16(cfg, 0, (B * Sq * H, D)).reshape(B, Sq, H, D)
+    ent = gen.normal_bf16(cfg, 1, (B * N, D)).reshape(B, N, D)
+    win = gen.normal_bf16(cfg, 2, (B * W, D)).reshape(B, W, D)
+    t = np.array([m * N + 3], dtype=np.int64)                    # every entry visible
+    wp = t - W + 1
+    n_ent = np.array([N], dtype=np.int64)
+    say(f"case: hca long list D={D} N={N} (35 slices)")
+    out, lse = ops.hca_attend(dev_bf16(q), dev_bf16(ent), dev(n_ent), dev_bf16(win), dev(wp), dev(t), m=m,
+                              rope_dim=16, window=W, lse=True)
+    ref_o, ref_l = oa.hca_attend(f64(q[0, 0]), f64(ent[0]), N, f64(win[0]), int(wp[0]), int(t[0]), W, 16,
+                                 1.0 / math.sqrt(D))
+    assert_close(host_f64(out)[0, 0], ref_o, "out")
+    assert_close(host_f64(lse)[0, 0], ref_l, "lse")
